@@ -1,0 +1,125 @@
+"""Seeded synthetic inputs for the bidirectional selective scan.
+
+This module only draws random numbers and rounds them to the I/O dtype; it
+holds none of the scan's arithmetic.  Both the HIP tests and the oracle's
+tests take their inputs from here, so the two sides always see the same bits.
+
+Recipe (shapes follow the 1.3B-layer workloads the library is measured on):
+  parameters (seed 0):
+    u_d        = exp(Uniform(ln 1e-3, ln 1e-1))     per channel
+    dt_bias[d] = log(expm1(u_d))                    so that softplus(dt_bias) = u_d
+    A[d, n]    = -(n + 1)                           (exact in fp32)
+    D[d]       = 1
+  activations (seed 1, one independent stream per tensor):
+    x, z, B, C ~ N(0, 1);  dt ~ 0.5 * N(0, 1)
+    drawn in fp32 and rounded once, round-to-nearest-even, to the I/O dtype.
+Every tensor uses its own PCG64 stream keyed by (seed, tensor id), so a
+tensor does not change when another one changes size.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+_TENSOR_IDS = {"x": 1, "dt": 2, "z": 3, "B": 4, "C": 5, "dt_bias": 11, "A_jitter": 12}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    seqlen: int
+    d_inner: int
+    d_state: int
+    io_dtype: str  # "f32" or "bf16"
+    calls: int = 1
+    block_len: int = 0  # > 0: block-cache sweep with blocks of this many tokens
+
+
+WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("tiny_fp32", 1, 256, 64, 16, "f32"),
+        Workload("layer_2k_bf16", 1, 2048, 4096, 16, "bf16"),
+        Workload("long_64k_bf16", 1, 65536, 4096, 16, "bf16"),
+        Workload("batched_8k_bf16", 8, 8192, 2048, 16, "bf16", calls=128),
+        Workload("block_32k_bf16", 1, 32768, 4096, 16, "bf16", block_len=32),
+    )
+}
+
+
+def _rng(seed: int, tensor: str) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _TENSOR_IDS[tensor]])))
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + r) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> the fp32 values they denote (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def round_to(a: np.ndarray, io_dtype: str) -> np.ndarray:
+    """Round fp32 values to the I/O dtype and return them as exact fp32 values."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if io_dtype == "f32":
+        return a
+    if io_dtype == "bf16":
+        return bf16_bits_to_f32(bf16_bits(a))
+    raise ValueError(io_dtype)
+
+
+def make_params(d_inner: int, d_state: int, seed: int = 0, a_jitter: float = 0.0):
+    """A [D, N], D [D], dt_bias [D] as fp32 arrays.
+
+    a_jitter > 0 multiplies A by (1 + a_jitter * U(-1, 1)) per entry, giving a
+    matrix without the per-channel geometric structure of the default init.
+    """
+    u = np.exp(_rng(seed, "dt_bias").uniform(np.log(1e-3), np.log(1e-1), size=d_inner))
+    dt_bias = np.log(np.expm1(u)).astype(np.float32)
+    A = -np.tile(np.arange(1, d_state + 1, dtype=np.float32), (d_inner, 1))
+    if a_jitter > 0.0:
+        j = _rng(seed, "A_jitter").uniform(-1.0, 1.0, size=A.shape).astype(np.float32)
+        A = (A * (np.float32(1.0) + np.float32(a_jitter) * j)).astype(np.float32)
+    D = np.ones(d_inner, dtype=np.float32)
+    return np.ascontiguousarray(A), D, dt_bias
+
+
+def normal(seed: int, tensor: str, shape, scale: float = 1.0, io_dtype: str = "f32") -> np.ndarray:
+    """One seeded N(0, scale^2) tensor, rounded to io_dtype, returned as fp32."""
+    a = _rng(seed, tensor).standard_normal(size=shape, dtype=np.float32)
+    if scale != 1.0:
+        a *= np.float32(scale)
+    return round_to(a, io_dtype)
+
+
+def make_activations(batch: int, seqlen: int, d_inner: int, d_state: int, io_dtype: str, seed: int = 1,
+                     xz_seed: int | None = None):
+    """x, dt, z [B, L, D] and B, C [B, L, N] as fp32 arrays exact in io_dtype.
+
+    xz_seed, when given, draws x and z from that seed instead (fresh
+    activations per denoising call with dt, B, C held fixed).
+    """
+    s_xz = seed if xz_seed is None else xz_seed
+    act = {
+        "x": normal(s_xz, "x", (batch, seqlen, d_inner), 1.0, io_dtype),
+        "dt": normal(seed, "dt", (batch, seqlen, d_inner), 0.5, io_dtype),
+        "z": normal(s_xz, "z", (batch, seqlen, d_inner), 1.0, io_dtype),
+        "B": normal(seed, "B", (batch, seqlen, d_state), 1.0, io_dtype),
+        "C": normal(seed, "C", (batch, seqlen, d_state), 1.0, io_dtype),
+    }
+    return act
+
+
+def make_workload_inputs(w: Workload, seed: int = 1, xz_seed: int | None = None, a_jitter: float = 0.0):
+    """Parameters and activations for one workload (fp32 arrays)."""
+    A, D, dt_bias = make_params(w.d_inner, w.d_state, a_jitter=a_jitter)
+    act = make_activations(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype, seed=seed, xz_seed=xz_seed)
+    act.update(A=A, D=D, dt_bias=dt_bias)
+    return act

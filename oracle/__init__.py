@@ -1,0 +1,14 @@
+"""fp64 CPU oracle for the bidirectional selective scan.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the graft entry point's
+smoke check and by the benchmark's CPU-baseline leg, never by the library.
+"""
+from .scan import (  # noqa: F401
+    discretise,
+    forward_scan,
+    reverse_scan,
+    scan_block,
+    scan_fwd,
+    silu,
+    softplus,
+)
