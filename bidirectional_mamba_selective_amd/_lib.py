@@ -1,0 +1,190 @@
+"""ctypes binding of libbimamba.so.
+
+Argument marshalling only: torch tensors are checked (device, dtype,
+contiguity, shape), their data pointers and the current HIP stream are passed
+to the C entry points of include/bimamba.h, and a non-zero status raises.
+Every step of the scan runs in the library's HIP kernels; there is no other
+path.  If the library is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libbimamba.so")
+
+BIMAMBA_OK = 0
+BIMAMBA_ERR_INVALID_ARGUMENT = 1
+BIMAMBA_ERR_UNSUPPORTED = 2
+BIMAMBA_ERR_WORKSPACE_TOO_SMALL = 3
+BIMAMBA_ERR_HIP = 4
+
+BIMAMBA_F32 = 0
+BIMAMBA_BF16 = 1
+
+FLAG_NO_GATE = 1
+FLAG_FWD_ONLY = 2
+FLAG_REV_ONLY = 4
+
+# every symbol include/bimamba.h declares
+EXPORTED = (
+    "bimamba_version",
+    "bimamba_status_string",
+    "bimamba_scan_fwd_workspace_bytes",
+    "bimamba_scan_fwd",
+    "bimamba_scan_block_workspace_bytes",
+    "bimamba_scan_block",
+)
+
+_lib = None
+
+
+class BimambaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libbimamba.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bidirectional_mamba_selective_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.bimamba_version.restype = ctypes.c_int
+    lib.bimamba_version.argtypes = []
+    lib.bimamba_status_string.restype = ctypes.c_char_p
+    lib.bimamba_status_string.argtypes = [ctypes.c_int]
+    lib.bimamba_scan_fwd_workspace_bytes.restype = sz
+    lib.bimamba_scan_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.bimamba_scan_block_workspace_bytes.restype = sz
+    lib.bimamba_scan_block_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.bimamba_scan_fwd.restype = ctypes.c_int
+    lib.bimamba_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                     ctypes.c_uint32, vp, sz, vp]
+    lib.bimamba_scan_block.restype = ctypes.c_int
+    lib.bimamba_scan_block.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                       ctypes.c_uint32, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def bimamba_version() -> int:
+    return load().bimamba_version()
+
+
+def status_string(status: int) -> str:
+    return load().bimamba_status_string(int(status)).decode()
+
+
+bimamba_status_string = status_string
+
+
+def bimamba_scan_fwd_workspace_bytes(batch: int, seqlen: int, d_inner: int, d_state: int) -> int:
+    return int(load().bimamba_scan_fwd_workspace_bytes(batch, seqlen, d_inner, d_state))
+
+
+def bimamba_scan_block_workspace_bytes(batch: int, block_len: int, d_inner: int, d_state: int) -> int:
+    return int(load().bimamba_scan_block_workspace_bytes(batch, block_len, d_inner, d_state))
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _io_dtype(x):
+    torch = _torch()
+    if x.dtype == torch.bfloat16:
+        return BIMAMBA_BF16
+    if x.dtype == torch.float32:
+        return BIMAMBA_F32
+    raise TypeError(f"unsupported I/O dtype {x.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _common(x, dt, A, B, C, D, z, dt_bias, out):
+    torch = _torch()
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, seqlen, d_inner]")
+    nb, L, nd = x.shape
+    ns = A.shape[1] if A.dim() == 2 else -1
+    io = x.dtype
+    dev = x.device
+    _check(x, "x", (nb, L, nd), io, dev)
+    _check(dt, "dt", (nb, L, nd), io, dev)
+    _check(z, "z", (nb, L, nd), io, dev)
+    _check(B, "B", (nb, L, ns), io, dev)
+    _check(C, "C", (nb, L, ns), io, dev)
+    _check(A, "A", (nd, ns), torch.float32, dev)
+    _check(D, "D", (nd,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (nd,), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (nb, L, nd), io, dev)
+    return nb, L, nd, ns, out
+
+
+def _stream(stream, device):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def bimamba_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, flags: int = 0, workspace=None,
+                     stream=None):
+    """Full-sequence bidirectional scan; returns out ([batch, seqlen, d_inner], x's dtype)."""
+    torch = _torch()
+    nb, L, nd, ns, out = _common(x, dt, A, B, C, D, z, dt_bias, out)
+    lib = load()
+    need = int(lib.bimamba_scan_fwd_workspace_bytes(nb, L, nd, ns))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib.bimamba_scan_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                              _ptr(out), nb, L, nd, ns, _io_dtype(x), flags, _ptr(workspace), workspace.numel(),
+                              _stream(stream, x.device))
+    if st != BIMAMBA_OK:
+        raise BimambaError(st, "bimamba_scan_fwd")
+    return out
+
+
+def bimamba_scan_block(x, dt, A, B, C, D=None, z=None, dt_bias=None, h_in=None, h_out=None, out=None,
+                       flags: int = 0, workspace=None, stream=None):
+    """One block of block-cache decoding; returns out.  h_out (fp32 [batch, d_inner, d_state]) receives the
+    forward state after the block when given (it may be the same tensor as h_in)."""
+    torch = _torch()
+    nb, L, nd, ns, out = _common(x, dt, A, B, C, D, z, dt_bias, out)
+    _check(h_in, "h_in", (nb, nd, ns), torch.float32, x.device)
+    _check(h_out, "h_out", (nb, nd, ns), torch.float32, x.device)
+    lib = load()
+    need = int(lib.bimamba_scan_block_workspace_bytes(nb, L, nd, ns))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wbytes = 0 if workspace is None else workspace.numel()
+    st = lib.bimamba_scan_block(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                                _ptr(h_in), _ptr(h_out), _ptr(out), nb, L, nd, ns, _io_dtype(x), flags,
+                                _ptr(workspace), wbytes, _stream(stream, x.device))
+    if st != BIMAMBA_OK:
+        raise BimambaError(st, "bimamba_scan_block")
+    return out

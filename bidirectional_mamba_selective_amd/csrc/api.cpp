@@ -1,0 +1,141 @@
+// C ABI of the bidirectional selective-scan library (declared in include/bimamba.h).
+// Every argument is validated here, before any HIP call.
+#include "../../include/bimamba.h"
+
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "launch.h"
+#include "plan.h"
+
+namespace {
+
+using bimamba::Plan;
+
+constexpr uint32_t kKnownFlags = BIMAMBA_FLAG_NO_GATE | BIMAMBA_FLAG_FWD_ONLY | BIMAMBA_FLAG_REV_ONLY;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Shape check shared by both entry points.
+int check_shape(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int io_dtype) {
+  if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_state <= 0) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (io_dtype != BIMAMBA_F32 && io_dtype != BIMAMBA_BF16) return BIMAMBA_ERR_UNSUPPORTED;
+  if (d_inner % bimamba::kLanes != 0 || d_state > 16) return BIMAMBA_ERR_UNSUPPORTED;
+  // grid and index limits of the kernels: int token/channel indices, 16-bit grid y/z
+  if (seqlen > INT32_MAX / 2 || d_inner > INT32_MAX / 2 || batch > 65535) return BIMAMBA_ERR_UNSUPPORTED;
+  if (static_cast<double>(batch) * seqlen * d_inner > 9.0e15) return BIMAMBA_ERR_UNSUPPORTED;
+  return BIMAMBA_OK;
+}
+
+// Pointer checks shared by both entry points; sizes in elements.
+int check_tensors(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                  const void* z, const float* dt_bias, void* out, int64_t batch, int64_t seqlen, int64_t d_inner,
+                  int64_t d_state, int io_dtype, uint32_t flags) {
+  if (flags & ~kKnownFlags) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if ((flags & BIMAMBA_FLAG_FWD_ONLY) && (flags & BIMAMBA_FLAG_REV_ONLY)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (!x || !dt || !A || !B || !C || !out) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (!z && !(flags & BIMAMBA_FLAG_NO_GATE)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const size_t es = io_dtype == BIMAMBA_BF16 ? 2 : 4;
+  if (!aligned(x, 16) || !aligned(dt, 16) || !aligned(out, 16) || (z && !aligned(z, 16))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (!aligned(B, es) || !aligned(C, es)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (!aligned(A, 16) || (D && !aligned(D, 16)) || (dt_bias && !aligned(dt_bias, 16))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const size_t act = static_cast<size_t>(batch) * seqlen * d_inner * es;
+  const size_t bc = static_cast<size_t>(batch) * seqlen * d_state * es;
+  const Range o = range_of(out, act);
+  if (overlap(o, range_of(x, act)) || overlap(o, range_of(dt, act)) || overlap(o, range_of(B, bc)) ||
+      overlap(o, range_of(C, bc)) || (z && overlap(o, range_of(z, act))) ||
+      overlap(o, range_of(A, static_cast<size_t>(d_inner) * d_state * 4)) ||
+      (D && overlap(o, range_of(D, static_cast<size_t>(d_inner) * 4))) ||
+      (dt_bias && overlap(o, range_of(dt_bias, static_cast<size_t>(d_inner) * 4))))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  return BIMAMBA_OK;
+}
+
+int check_workspace(const Plan& p, void* workspace, size_t workspace_bytes, void* out, size_t out_bytes) {
+  if (workspace_bytes < p.total) return BIMAMBA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 256)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (overlap(range_of(workspace, p.total), range_of(out, out_bytes))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  return BIMAMBA_OK;
+}
+
+int map_hip(hipError_t e) { return e == hipSuccess ? BIMAMBA_OK : BIMAMBA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int bimamba_version(void) { return (0 << 16) | (1 << 8) | 0; }
+
+const char* bimamba_status_string(int status) {
+  switch (status) {
+    case BIMAMBA_OK: return "ok";
+    case BIMAMBA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case BIMAMBA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case BIMAMBA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case BIMAMBA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t bimamba_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+  if (check_shape(batch, seqlen, d_inner, d_state, BIMAMBA_F32) != BIMAMBA_OK) return 0;
+  return bimamba::make_plan(batch, seqlen, d_inner, d_state).total;
+}
+
+int bimamba_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                     const void* z, const float* dt_bias, void* out, int64_t batch, int64_t seqlen, int64_t d_inner,
+                     int64_t d_state, int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  int s = check_shape(batch, seqlen, d_inner, d_state, io_dtype);
+  if (s != BIMAMBA_OK) return s;
+  s = check_tensors(x, dt, A, B, C, D, z, dt_bias, out, batch, seqlen, d_inner, d_state, io_dtype, flags);
+  if (s != BIMAMBA_OK) return s;
+  const Plan p = bimamba::make_plan(batch, seqlen, d_inner, d_state);
+  const size_t es = io_dtype == BIMAMBA_BF16 ? 2 : 4;
+  s = check_workspace(p, workspace, workspace_bytes, out, static_cast<size_t>(batch) * seqlen * d_inner * es);
+  if (s != BIMAMBA_OK) return s;
+  bimamba::ScanArgs a{x, dt, A, B, C, D, z, dt_bias, out, nullptr, nullptr, io_dtype, flags};
+  return map_hip(bimamba::launch_chunked(a, p, workspace, stream));
+}
+
+size_t bimamba_scan_block_workspace_bytes(int64_t batch, int64_t block_len, int64_t d_inner, int64_t d_state) {
+  if (check_shape(batch, block_len, d_inner, d_state, BIMAMBA_F32) != BIMAMBA_OK) return 0;
+  return bimamba::make_plan(batch, block_len, d_inner, d_state).total;
+}
+
+int bimamba_scan_block(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                       const void* z, const float* dt_bias, const float* h_in, float* h_out, void* out,
+                       int64_t batch, int64_t block_len, int64_t d_inner, int64_t d_state, int io_dtype,
+                       uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int s = check_shape(batch, block_len, d_inner, d_state, io_dtype);
+  if (s != BIMAMBA_OK) return s;
+  s = check_tensors(x, dt, A, B, C, D, z, dt_bias, out, batch, block_len, d_inner, d_state, io_dtype, flags);
+  if (s != BIMAMBA_OK) return s;
+  const size_t st_bytes = static_cast<size_t>(batch) * d_inner * d_state * sizeof(float);
+  if ((h_in && !aligned(h_in, 16)) || (h_out && !aligned(h_out, 16))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (h_in && h_out && h_in != h_out && overlap(range_of(h_in, st_bytes), range_of(h_out, st_bytes)))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const size_t es = io_dtype == BIMAMBA_BF16 ? 2 : 4;
+  const size_t out_bytes = static_cast<size_t>(batch) * block_len * d_inner * es;
+  if (h_out && overlap(range_of(h_out, st_bytes), range_of(out, out_bytes))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const Plan p = bimamba::make_plan(batch, block_len, d_inner, d_state);
+  s = check_workspace(p, workspace, workspace_bytes, out, out_bytes);
+  if (s != BIMAMBA_OK) return s;
+  if (h_out && overlap(range_of(h_out, st_bytes), range_of(workspace, p.total))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  bimamba::ScanArgs a{x, dt, A, B, C, D, z, dt_bias, out, h_in, h_out, io_dtype, flags};
+  return map_hip(bimamba::launch_chunked(a, p, workspace, stream));
+}
+
+}  // extern "C"

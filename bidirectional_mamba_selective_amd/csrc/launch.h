@@ -1,0 +1,32 @@
+// Internal interface between the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace bimamba {
+
+enum : uint32_t { kNoGate = 1u, kFwdOnly = 2u, kRevOnly = 4u };
+
+struct ScanArgs {
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* dt_bias;
+  void* out;
+  const float* h_in;  // forward state entering the sequence (NULL = zeros)
+  float* h_out;       // forward state after the last token (NULL = not written)
+  int io_dtype;       // 0 = fp32, 1 = bf16
+  uint32_t flags;
+};
+
+// Three-kernel chunked scan (summary -> carry -> output) for any length.
+hipError_t launch_chunked(const ScanArgs& a, const Plan& p, void* workspace, hipStream_t stream);
+
+}  // namespace bimamba

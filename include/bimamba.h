@@ -1,0 +1,120 @@
+/*
+ * bimamba.h - C ABI of the MI355X (gfx950) bidirectional selective-scan library.
+ *
+ * The operation is the bidirectional Mamba (S6) mixer scan of "DiffuMamba:
+ * High-Throughput Diffusion LMs with Mamba Backbone" (arXiv v4):
+ *   - Section 3.2, eq. (4): forward recurrence  h_i = A_f * h_{i-1} + B_f * x_i, i = 1..L
+ *   - Section 3.2, eq. (5): reverse recurrence  h_i = A_b * h_{i+1} + B_b * x_i, i = L..1
+ *   - Section 3.2, eq. (6): the two directions are summed.
+ *   - Section 2 (state-space models): the SSM is selective, i.e. input-conditioned.
+ *   - Appendix C, Table 12 caption: the input projection supplies the gate z,
+ *     the step dt, B, C and a per-channel bias on dt.
+ * with the selective discretisation written out per channel d, state n, token t:
+ *   delta[t,d] = softplus(dt[t,d] + dt_bias[d])
+ *   abar       = exp(delta[t,d] * A[d,n])
+ *   h_fwd[t]   = abar * h_fwd[t-1] + delta[t,d] * x[t,d] * B[t,n]     (h_fwd[-1] = 0)
+ *   h_rev[t]   = abar * h_rev[t+1] + delta[t,d] * x[t,d] * B[t,n]     (h_rev[L]  = 0)
+ *   y_dir[t,d] = sum_n C[t,n] * h_dir[t,d,n] + D[d] * x[t,d]
+ *   out[t,d]   = (y_fwd + y_rev) * z * sigmoid(z)
+ * Both directions use one set of (A, D, dt_bias) and one (x, dt, B, C).
+ *
+ * Conventions common to every entry point:
+ *   - Every pointer is a DEVICE pointer owned by the caller.  The library never
+ *     allocates, frees or synchronises; work is enqueued on `stream` (0 = the
+ *     null stream) and the call returns after enqueue.  A fault inside a kernel
+ *     surfaces at the caller's next synchronisation.
+ *   - Layouts are dense and row-major: x, dt, z, out are [batch, seqlen, d_inner]
+ *     (channels contiguous); B and C are [batch, seqlen, d_state] (one B_t and
+ *     one C_t per token, shared by all channels); A is [d_inner, d_state] fp32;
+ *     D and dt_bias are [d_inner] fp32.  Base pointers must be 16-byte aligned.
+ *   - io_dtype (a bimamba_dtype) applies to x, dt, z, B, C and out.  A, D,
+ *     dt_bias, block states and every internal state are fp32; out is rounded
+ *     to nearest even when io_dtype is BF16.
+ *   - D == NULL means D = 0; dt_bias == NULL means dt_bias = 0; z may be NULL
+ *     only together with BIMAMBA_FLAG_NO_GATE.  Inputs are read-only and out
+ *     must not overlap any input or the workspace.
+ *   - Supported shapes: batch >= 1, seqlen/block_len >= 1, d_inner a positive
+ *     multiple of 64, 1 <= d_state <= 16; anything else returns
+ *     BIMAMBA_ERR_UNSUPPORTED (bad values) or BIMAMBA_ERR_INVALID_ARGUMENT.
+ *   - All arguments are validated before any HIP call, so a rejected call has
+ *     no side effect.  Launch failures return BIMAMBA_ERR_HIP.
+ *   - Calls are re-entrant; the library keeps no mutable global state.
+ */
+#ifndef BIMAMBA_H
+#define BIMAMBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BIMAMBA_OK = 0,
+  BIMAMBA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad flag combination, misaligned pointer */
+  BIMAMBA_ERR_UNSUPPORTED = 2,        /* shape or dtype outside the supported set */
+  BIMAMBA_ERR_WORKSPACE_TOO_SMALL = 3,
+  BIMAMBA_ERR_HIP = 4                 /* a HIP launch returned an error */
+} bimamba_status;
+
+typedef enum { BIMAMBA_F32 = 0, BIMAMBA_BF16 = 1 } bimamba_dtype;
+
+enum {
+  BIMAMBA_FLAG_NO_GATE = 1u,  /* out = y_fwd + y_rev, no SiLU(z) factor (z may be NULL) */
+  BIMAMBA_FLAG_FWD_ONLY = 2u, /* keep only the forward direction, eq. (4)            */
+  BIMAMBA_FLAG_REV_ONLY = 4u  /* keep only the reverse direction, eq. (5)            */
+};
+
+/* Library version, (major << 16) | (minor << 8) | patch. */
+int bimamba_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* bimamba_status_string(int status);
+
+/* Bytes of device workspace bimamba_scan_fwd needs for this shape (a pure host
+ * computation, no HIP call).  Returns 0 for an unsupported shape. */
+size_t bimamba_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state);
+
+/* Full-sequence bidirectional scan, Section 3.2 eq. (4)-(6): every token sees
+ * the whole sequence in both directions.  out[b,t,d] as defined above.
+ * workspace: caller-owned device memory of at least
+ * bimamba_scan_fwd_workspace_bytes(...) bytes, 256-byte aligned; its contents
+ * on entry are ignored and on exit are unspecified.  Two calls that overlap in
+ * time must not share a workspace. */
+int bimamba_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                     const float* D, const void* z, const float* dt_bias, void* out,
+                     int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                     int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Bytes of device workspace bimamba_scan_block needs for this shape; 0 when the
+ * block is short enough for the single-kernel path (no workspace needed). */
+size_t bimamba_scan_block_workspace_bytes(int64_t batch, int64_t block_len, int64_t d_inner, int64_t d_state);
+
+/* One block of block-cache decoding (Section 4.3, block-cache paragraph; also
+ * the abstract of arXiv 2607.02805, which restricts the reverse scan to the
+ * active block): the forward direction resumes from the cached state h_in,
+ * the reverse direction starts from zero at the block's last token and never
+ * looks past the block.  x, dt, z, B, C, out hold the block's block_len tokens.
+ *   h_in : [batch, d_inner, d_state] fp32, the forward state before the block;
+ *          NULL means zeros.
+ *   h_out: [batch, d_inner, d_state] fp32, receives the forward state after the
+ *          block's last token (the cache for the next block); NULL means do not
+ *          write.  h_out may equal h_in (in-place commit) but must not
+ *          otherwise overlap it.  The flags select the directions summed into
+ *          out; h_out is the forward state in every case.
+ * workspace may be NULL when bimamba_scan_block_workspace_bytes returns 0. */
+int bimamba_scan_block(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* dt_bias,
+                       const float* h_in, float* h_out, void* out,
+                       int64_t batch, int64_t block_len, int64_t d_inner, int64_t d_state,
+                       int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BIMAMBA_H */

@@ -1,0 +1,142 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call.
+
+The pointer values below are never dereferenced: every call here fails
+validation, which happens on the host before anything reaches HIP.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bidirectional_mamba_selective_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bimamba.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libbimamba.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bimamba_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib.load()
+    decl = declared_functions()
+    assert decl, "no functions found in the header"
+    assert sorted(_lib.EXPORTED) == decl
+    for name in decl:
+        assert hasattr(lib, name), f"{name} is declared but not exported"
+
+
+def test_version_and_status_strings():
+    assert _lib.bimamba_version() == (0 << 16) | (1 << 8) | 0
+    assert _lib.status_string(0) == "ok"
+    assert "workspace" in _lib.status_string(3)
+    assert _lib.status_string(12345) == "unknown status"
+
+
+def test_workspace_size_is_monotone_and_zero_when_unsupported():
+    f = _lib.bimamba_scan_fwd_workspace_bytes
+    sizes = [f(1, L, 4096, 16) for L in (1, 16, 17, 1000, 2048, 65536)]
+    assert all(s > 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    assert f(1, 1024, 100, 16) == 0  # d_inner not a multiple of 64
+    assert f(1, 1024, 64, 17) == 0  # d_state above 16
+    assert f(0, 1024, 64, 16) == 0
+    assert all(s % 256 == 0 for s in sizes)
+
+
+BASE = 1 << 30
+SPAN = 1 << 26  # far apart, 256-byte aligned fake device addresses
+
+
+def fake(i, off=0):
+    return ctypes.c_void_p(BASE + i * SPAN + off)
+
+
+def call_fwd(**kw):
+    lib = _lib.load()
+    a = dict(x=fake(0), dt=fake(1), A=fake(2), B=fake(3), C=fake(4), D=fake(5), z=fake(6), dt_bias=fake(7),
+             out=fake(8), batch=1, L=64, d=64, n=16, io=_lib.BIMAMBA_BF16, flags=0, ws=fake(9), wsb=0, stream=None)
+    a.update(kw)
+    return lib.bimamba_scan_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["dt_bias"], a["out"],
+                                a["batch"], a["L"], a["d"], a["n"], a["io"], a["flags"], a["ws"], a["wsb"],
+                                a["stream"])
+
+
+def call_block(**kw):
+    lib = _lib.load()
+    a = dict(x=fake(0), dt=fake(1), A=fake(2), B=fake(3), C=fake(4), D=fake(5), z=fake(6), dt_bias=fake(7),
+             h_in=fake(10), h_out=fake(11), out=fake(8), batch=1, L=32, d=64, n=16, io=_lib.BIMAMBA_BF16, flags=0,
+             ws=fake(9), wsb=0, stream=None)
+    a.update(kw)
+    return lib.bimamba_scan_block(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["dt_bias"], a["h_in"],
+                                  a["h_out"], a["out"], a["batch"], a["L"], a["d"], a["n"], a["io"], a["flags"],
+                                  a["ws"], a["wsb"], a["stream"])
+
+
+INV, UNS, WS = _lib.BIMAMBA_ERR_INVALID_ARGUMENT, _lib.BIMAMBA_ERR_UNSUPPORTED, _lib.BIMAMBA_ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), INV),
+    (dict(dt=None), INV),
+    (dict(A=None), INV),
+    (dict(B=None), INV),
+    (dict(C=None), INV),
+    (dict(out=None), INV),
+    (dict(z=None), INV),  # z is required unless the gate is off
+    (dict(flags=_lib.FLAG_FWD_ONLY | _lib.FLAG_REV_ONLY), INV),
+    (dict(flags=64), INV),
+    (dict(batch=0), INV),
+    (dict(L=0), INV),
+    (dict(L=-5), INV),
+    (dict(d=0), INV),
+    (dict(n=0), INV),
+    (dict(d=100), UNS),
+    (dict(n=17), UNS),
+    (dict(io=2), UNS),
+    (dict(batch=70000), UNS),
+    (dict(x=fake(0, 8)), INV),  # misaligned activation
+    (dict(A=fake(2, 4)), INV),
+    (dict(B=fake(3, 1)), INV),  # not even element-aligned
+    (dict(out=fake(0, 64)), INV),  # out overlaps x
+    (dict(wsb=0), WS),
+    (dict(ws=None, wsb=1 << 40), INV),
+    (dict(ws=fake(9, 16), wsb=1 << 40), INV),  # workspace not 256-byte aligned
+])
+def test_scan_fwd_rejects(kw, want):
+    assert call_fwd(**kw) == want
+
+
+def test_scan_fwd_checks_run_in_order():
+    # z may be NULL with NO_GATE: the call then gets as far as the workspace check
+    assert call_fwd(z=None, flags=_lib.FLAG_NO_GATE, wsb=0) == WS
+    # D and dt_bias are optional
+    assert call_fwd(D=None, dt_bias=None, wsb=0) == WS
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(h_in=fake(10, 8)), INV),  # misaligned state
+    (dict(h_out=fake(10, 256)), INV),  # partial overlap with h_in
+    (dict(h_out=fake(8, 0)), INV),  # h_out overlaps out
+    (dict(x=None), INV),
+    (dict(L=0), INV),
+    (dict(n=20), UNS),
+])
+def test_scan_block_rejects(kw, want):
+    assert call_block(**kw) == want
+
+
+def test_scan_block_allows_in_place_state():
+    need = _lib.bimamba_scan_block_workspace_bytes(1, 32, 64, 16)
+    if need == 0:
+        pytest.skip("single-kernel block path needs no workspace; a valid call would launch")
+    # h_out == h_in is accepted; the call then stops at the workspace size check
+    assert call_block(h_out=fake(10), wsb=0) == WS
+    assert call_block(h_in=None, h_out=None, wsb=0) == WS
