@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of the bidirectional selective scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_64k_bf16]
+
+One step = one bimamba_scan_fwd call over the whole workload (summary, carry
+and output kernels), inputs already resident in HBM.  W untimed steps, then K
+timed steps bracketed by device synchronisations; one JSON line is printed.
+
+Besides the headline tokens/s the line carries:
+  roofline      the output kernel (the dominant one) against the VALU roofline,
+                its duration measured live with HIP events on the stream the
+                library launches on (staged entry point, same arguments);
+  hbm           algorithmic bytes of the whole call / step time vs 8 TB/s;
+  cpu_baseline  the fp64 oracle timed on this host on a bounded channel sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "bidir selective-scan tokens/s + achieved HBM GB/s (% peak) at L=65536"
+HBM_PEAK_GBS = 8000.0
+# MI355X published fp32 vector peak; one fp32 FMA = 2 FLOP, one transcendental
+# (v_exp_f32 / v_log_f32 / v_rcp_f32) issues at a quarter of the FMA rate and
+# is counted as the 8 FLOP of the four FMA slots it occupies.
+VALU_PEAK_TFLOPS = 157.3
+FLOP_PER_ELEMENT_OUTPUT = 18  # per (token, channel, state): mul + exp(8) + mul + 2 fma(4) + 2 fma(4)
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "k_output_long_64k_bf16_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "bidirectional_mamba_selective_amd", "csrc", "scan_kernels.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(batch, L, D, N, es):
+    """Each input read once, out written once, A/D/dt_bias once per call."""
+    per_token = 4 * D * es + 2 * N * es  # x, dt, z, out + B, C
+    return batch * L * per_token + D * N * 4 + 2 * D * 4
+
+
+def kernel_source_hash():
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def profiled_traffic(launch_elems):
+    """HBM bytes per output-kernel launch from the committed rocprofv3 counter summary,
+    or None when it is missing or was taken on a different kernel source."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    txt = open(PROFILE_TRAFFIC).read()
+    m_src = re.search(r"source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_dispatch:\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(inp, L, D, nch):
+    """The oracle as it stands on all L tokens of nch channels (exact for those channels:
+    a channel's output depends on that channel and the shared B, C only), scaled to tokens/s of
+    the full channel count.  numpy elementwise work runs on one thread."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    chan = np.linspace(0, D - 1, nch).astype(np.int64)
+    sub = dict(x=inp["x"][:, :, chan], dt=inp["dt"][:, :, chan], z=inp["z"][:, :, chan], B=inp["B"], C=inp["C"],
+               A=inp["A"][chan], D=inp["D"][chan], dt_bias=inp["dt_bias"][chan])
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    t0 = time.perf_counter()
+    if ctx:
+        with ctx:
+            oracle.scan_fwd(sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], sub["dt_bias"])
+    else:
+        oracle.scan_fwd(sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], sub["dt_bias"])
+    sec = time.perf_counter() - t0
+    batch = inp["x"].shape[0]
+    tok_s = batch * L / (sec * D / nch)
+    return {"value": tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {batch}x{L} tokens of {nch} of {D} channels in {sec:.1f} s on 1 host thread, "
+                      f"scaled by {D}/{nch} to the full channel count"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_64k_bf16")
+    ap.add_argument("--cpu-channels", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain device copy of known size (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the scan runs on a single MI355X and this build has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bidirectional_mamba_selective_amd as bm
+    from bidirectional_mamba_selective_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    if w.block_len:
+        raise SystemExit("block workloads are measured by the block sweep test, not by this benchmark")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bm.load()
+
+    log(f"workload {w.name}: batch {w.batch} L {w.seqlen} d_inner {w.d_inner} d_state {w.d_state} {w.io_dtype}")
+    t0 = time.perf_counter()
+    inp = I.make_workload_inputs(w)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def up(k, io=True):
+        a = inp[k]
+        if io and w.io_dtype == "bf16":
+            return torch.from_numpy(I.bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    x, dt, z, B, C = (up(k) for k in ("x", "dt", "z", "B", "C"))
+    A, Dv, bias = (up(k, False) for k in ("A", "D", "dt_bias"))
+    out = torch.empty_like(x)
+    need = bm.bimamba_scan_fwd_workspace_bytes(w.batch, w.seqlen, w.d_inner, w.d_state)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        bm.bimamba_scan_fwd(x, dt, A, B, C, Dv, z, bias, out=out, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms_step_ev = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step wall, {ms_step_ev:.4f} ms/step events")
+
+    # per-kernel attribution on the same stream: staged entry point, events between stages
+    names = ("k_summary", "k_carry", "k_output")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        e = evs[s]
+        e[0].record(stream)
+        for st in range(3):
+            bm.bimamba_scan_fwd_stage(st, x, dt, A, B, C, Dv, z, bias, out=out, workspace=ws, stream=stream)
+            e[st + 1].record(stream)
+    torch.cuda.synchronize()
+    per = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+           for i, n in enumerate(names)}
+    log("per-kernel ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per.items()))
+
+    if args.calibrate_copy:
+        buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(buf)
+        for _ in range(3):
+            dst.copy_(buf)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of 1 GiB done")
+
+    es = 2 if w.io_dtype == "bf16" else 4
+    elems = w.batch * w.seqlen * w.d_inner * w.d_state
+    tokens = w.batch * w.seqlen
+    abytes = algorithmic_bytes(w.batch, w.seqlen, w.d_inner, w.d_state, es)
+    t_out = per["k_output"] * 1e-3
+    achieved = FLOP_PER_ELEMENT_OUTPUT * elems / t_out / 1e12
+    traffic = profiled_traffic(elems) if w.name == "long_64k_bf16" else None
+    roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / VALU_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": "k_output",
+                "kernel_ms": round(per["k_output"], 4)}
+    hbm_gbs = abytes / (ms_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.io_dtype if w.io_dtype != "f32" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, A[d,n]=-(n+1), D=1, log-uniform softplus(dt_bias))",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "d_inner": w.d_inner,
+                   "d_state": w.d_state, "io_dtype": w.io_dtype, "state_dtype": "f32"},
+        "roofline": roofline,
+        "hbm": {"algorithmic_bytes": abytes, "achieved_gbs": round(hbm_gbs, 1),
+                "frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4), "peak_gbs": HBM_PEAK_GBS},
+        "kernels_ms": {k: round(v, 4) for k, v in per.items()},
+        "ms_per_step_events": round(ms_step_ev, 4),
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_channels} channels")
+        line["cpu_baseline"] = cpu_baseline(inp, w.seqlen, w.d_inner, min(args.cpu_channels, w.d_inner))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,6 +33,7 @@ EXPORTED = (
     "bimamba_status_string",
     "bimamba_scan_fwd_workspace_bytes",
     "bimamba_scan_fwd",
+    "bimamba_scan_fwd_stage",
     "bimamba_scan_block_workspace_bytes",
     "bimamba_scan_block",
 )
@@ -66,6 +67,9 @@ def load() -> ctypes.CDLL:
     lib.bimamba_scan_fwd.restype = ctypes.c_int
     lib.bimamba_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                      ctypes.c_uint32, vp, sz, vp]
+    lib.bimamba_scan_fwd_stage.restype = ctypes.c_int
+    lib.bimamba_scan_fwd_stage.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                           ctypes.c_int, ctypes.c_uint32, vp, sz, vp]
     lib.bimamba_scan_block.restype = ctypes.c_int
     lib.bimamba_scan_block.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                        ctypes.c_uint32, vp, sz, vp]
@@ -166,6 +170,21 @@ def bimamba_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, fla
                               _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_scan_fwd")
+    return out
+
+
+def bimamba_scan_fwd_stage(stage: int, x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, flags: int = 0,
+                           workspace=None, stream=None):
+    """One stage (0 summary, 1 carry, 2 output) of bimamba_scan_fwd; the caller keeps workspace and out across
+    the three calls.  Returns out."""
+    nb, L, nd, ns, out = _common(x, dt, A, B, C, D, z, dt_bias, out)
+    if workspace is None:
+        raise ValueError("the staged entry point needs a caller-kept workspace")
+    st = load().bimamba_scan_fwd_stage(int(stage), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                       _ptr(dt_bias), _ptr(out), nb, L, nd, ns, _io_dtype(x), flags, _ptr(workspace),
+                                       workspace.numel(), _stream(stream, x.device))
+    if st != BIMAMBA_OK:
+        raise BimambaError(st, f"bimamba_scan_fwd_stage({stage})")
     return out
 
 

@@ -94,10 +94,11 @@ size_t bimamba_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d
   return bimamba::make_plan(batch, seqlen, d_inner, d_state).total;
 }
 
-int bimamba_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
-                     const void* z, const float* dt_bias, void* out, int64_t batch, int64_t seqlen, int64_t d_inner,
-                     int64_t d_state, int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream) {
+static int scan_fwd_impl(int stage, const void* x, const void* dt, const float* A, const void* B, const void* C,
+                         const float* D, const void* z, const float* dt_bias, void* out, int64_t batch,
+                         int64_t seqlen, int64_t d_inner, int64_t d_state, int io_dtype, uint32_t flags,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (stage < -1 || stage > 2) return BIMAMBA_ERR_INVALID_ARGUMENT;
   int s = check_shape(batch, seqlen, d_inner, d_state, io_dtype);
   if (s != BIMAMBA_OK) return s;
   s = check_tensors(x, dt, A, B, C, D, z, dt_bias, out, batch, seqlen, d_inner, d_state, io_dtype, flags);
@@ -107,7 +108,23 @@ int bimamba_scan_fwd(const void* x, const void* dt, const float* A, const void* 
   s = check_workspace(p, workspace, workspace_bytes, out, static_cast<size_t>(batch) * seqlen * d_inner * es);
   if (s != BIMAMBA_OK) return s;
   bimamba::ScanArgs a{x, dt, A, B, C, D, z, dt_bias, out, nullptr, nullptr, io_dtype, flags};
-  return map_hip(bimamba::launch_chunked(a, p, workspace, stream));
+  return map_hip(bimamba::launch_chunked(a, p, workspace, stream, stage));
+}
+
+int bimamba_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                     const void* z, const float* dt_bias, void* out, int64_t batch, int64_t seqlen, int64_t d_inner,
+                     int64_t d_state, int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  return scan_fwd_impl(-1, x, dt, A, B, C, D, z, dt_bias, out, batch, seqlen, d_inner, d_state, io_dtype, flags,
+                       workspace, workspace_bytes, stream);
+}
+
+int bimamba_scan_fwd_stage(int stage, const void* x, const void* dt, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* dt_bias, void* out, int64_t batch,
+                           int64_t seqlen, int64_t d_inner, int64_t d_state, int io_dtype, uint32_t flags,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return scan_fwd_impl(stage, x, dt, A, B, C, D, z, dt_bias, out, batch, seqlen, d_inner, d_state, io_dtype, flags,
+                       workspace, workspace_bytes, stream);
 }
 
 size_t bimamba_scan_block_workspace_bytes(int64_t batch, int64_t block_len, int64_t d_inner, int64_t d_state) {

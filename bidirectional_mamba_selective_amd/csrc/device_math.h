@@ -21,15 +21,10 @@ __device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(stati
 __device__ __forceinline__ void from_f32(float v, float* dst) { *dst = v; }
 // Round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ void from_f32(float v, bf16_t* dst) {
-  uint32_t u = __float_as_uint(v);
-  uint16_t r;
-  if ((u & 0x7fffffffu) > 0x7f800000u) {
-    r = static_cast<uint16_t>((u >> 16) | 0x40u);
-  } else {
-    u += 0x7fffu + ((u >> 16) & 1u);
-    r = static_cast<uint16_t>(u >> 16);
-  }
-  dst->bits = r;
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t qnan = (u >> 16) | 0x40u;
+  dst->bits = static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? qnan : rounded);
 }
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }

@@ -27,6 +27,7 @@ struct ScanArgs {
 };
 
 // Three-kernel chunked scan (summary -> carry -> output) for any length.
-hipError_t launch_chunked(const ScanArgs& a, const Plan& p, void* workspace, hipStream_t stream);
+// stage < 0 launches all three; 0, 1, 2 launch one of them.
+hipError_t launch_chunked(const ScanArgs& a, const Plan& p, void* workspace, hipStream_t stream, int stage = -1);
 
 }  // namespace bimamba

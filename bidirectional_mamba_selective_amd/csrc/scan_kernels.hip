@@ -38,7 +38,51 @@ __device__ __forceinline__ float ld(const T* __restrict__ p, size_t i) {
 }
 
 // ---------------------------------------------------------------------------
+// Tile loading: SUB consecutive tokens of one channel per lane (coalesced across
+// the 64 lanes of a wavefront), all loads issued together.
+// ---------------------------------------------------------------------------
+template <typename T, int SUB>
+__device__ __forceinline__ void load_tile(const T* __restrict__ p, size_t base, int D, int nvalid, float (&v)[SUB]) {
+  // Addresses are clamped into the valid range and the surplus values zeroed
+  // afterwards, so the loads carry no branches and are all in flight at once.
+#pragma unroll
+  for (int k = 0; k < SUB; ++k) v[k] = ld(p, base + static_cast<size_t>(min(k, nvalid - 1)) * D);
+#pragma unroll
+  for (int k = 0; k < SUB; ++k) v[k] = k < nvalid ? v[k] : 0.0f;
+}
+
+// Stage a [SUB x N] tile of a token-major [*, N] matrix into LDS as fp32 [NM][SUB]
+// (state-major, so a state's SUB values are contiguous); missing tokens and
+// states >= N become 0.
+template <typename T, int NM, int SUB>
+__device__ __forceinline__ void stage_bc(const T* __restrict__ M, size_t row0, int N, int nvalid, float (*dst)[SUB],
+                                         int lane) {
+  constexpr int PER = (NM * SUB + 63) / 64;
+  float v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = i * 64 + lane;
+    const int k = e / NM;
+    const int n = e - k * NM;
+    v[i] = ld(M, (row0 + min(k, nvalid - 1)) * N + min(n, N - 1));
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = i * 64 + lane;
+    const int k = e / NM;
+    const int n = e - k * NM;
+    if (e < NM * SUB) dst[n][k] = (k < nvalid && n < N) ? v[i] : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_summary: grid (d_inner / 64, nchunk, batch), block 64.
+// Walks the chunk's tiles from right to left.  Per state n and tile it forms
+// abar and delta*x*B once per token, runs the tile-local forward recurrence
+// from zero (composed into the chunk's forward end state with the decay of
+// everything to the right of the tile) and continues the reverse recurrence
+// from the running state; the running reverse state is stored at every tile
+// boundary.
 // ---------------------------------------------------------------------------
 template <typename T, int NM>
 __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T* __restrict__ dt,
@@ -47,57 +91,73 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
                                                 int nchunk, int nsub, float* __restrict__ Sf,
                                                 float* __restrict__ Sr, float* __restrict__ P,
                                                 float* __restrict__ R, float* __restrict__ SIG) {
-  const int d = blockIdx.x * 64 + threadIdx.x;
+  constexpr int SUB = static_cast<int>(kSub);
+  __shared__ float sB[NM][SUB];
+  __shared__ float sA2[NM][64];
+  __shared__ float sR[NM][64];
+  __shared__ float sS[NM][64];
+  const int lane = threadIdx.x;
+  const int d = blockIdx.x * 64 + lane;
   const int c = blockIdx.y;
   const int b = blockIdx.z;
   const int t0 = c * chunk;
   const int te = min(L, t0 + chunk);
-
-  float A2[NM], r[NM], S[NM], q[NM];
-#pragma unroll
-  for (int n = 0; n < NM; ++n) {
-    A2[n] = n < N ? A[static_cast<size_t>(d) * N + n] * kLog2e : 0.0f;
-    r[n] = 0.0f;
-    S[n] = 0.0f;
-    q[n] = 1.0f;
-  }
-  const float bias = dt_bias ? dt_bias[d] : 0.0f;
-  float sigma = 0.0f;
   const size_t row = static_cast<size_t>(b) * L;
   const size_t cbase = static_cast<size_t>(b) * nchunk + c;
 
-  for (int t = te - 1; t >= t0; --t) {
-    const size_t i = (row + t) * D + d;
-    const float dl = softplus_f32(ld(dt, i) + bias);
-    const float u = dl * ld(x, i);
-    sigma += dl;
-    const T* __restrict__ brow = Bm + (row + t) * N;
-#pragma unroll
-    for (int n = 0; n < NM; ++n) {
-      const float bn = n < N ? ld(brow, n) : 0.0f;
-      const float a = fast_exp2(dl * A2[n]);
-      const float bb = u * bn;
-      S[n] = fmaf(q[n], bb, S[n]);
-      q[n] *= a;
-      r[n] = fmaf(a, r[n], bb);
-    }
-    const int k = t - t0;
-    if (k > 0 && (k % static_cast<int>(kSub)) == 0) {
-      const size_t jb = cbase * nsub + (k / kSub - 1);
-#pragma unroll
-      for (int n = 0; n < NM; ++n)
-        if (n < N) R[(jb * N + n) * D + d] = r[n];
-      SIG[jb * D + d] = sigma;
-    }
+  for (int n = 0; n < N; ++n) {
+    sA2[n][lane] = A[static_cast<size_t>(d) * N + n] * kLog2e;
+    sR[n][lane] = 0.0f;
+    sS[n][lane] = 0.0f;
   }
+  const float bias = dt_bias ? dt_bias[d] : 0.0f;
+  float sigma = 0.0f;  // sum of delta from the current tile's right edge to the chunk end
+
+  const int nsub_c = (te - t0 + SUB - 1) / SUB;
+  for (int j = nsub_c - 1; j >= 0; --j) {
+    const int ts = t0 + j * SUB;
+    const int nvalid = min(SUB, te - ts);
+    float xr[SUB], dr[SUB];
+    load_tile<T, SUB>(x, (row + ts) * D + d, D, nvalid, xr);
+    load_tile<T, SUB>(dt, (row + ts) * D + d, D, nvalid, dr);
+    __syncthreads();  // previous tile's reads of sB are done
+    stage_bc<T, NM, SUB>(Bm, row + ts, N, nvalid, sB, lane);
+    float dl[SUB], u[SUB];
+    float tile_sum = 0.0f;
 #pragma unroll
-  for (int n = 0; n < NM; ++n) {
-    if (n < N) {
-      const size_t o = (cbase * N + n) * D + d;
-      Sf[o] = S[n];
-      Sr[o] = r[n];
-      P[o] = q[n];
+    for (int k = 0; k < SUB; ++k) {
+      dl[k] = k < nvalid ? softplus_f32(dr[k] + bias) : 0.0f;
+      u[k] = dl[k] * xr[k];
+      tile_sum += dl[k];
     }
+    __syncthreads();
+    const size_t jb = cbase * nsub + (j - 1);
+#pragma unroll 1
+    for (int n = 0; n < N; ++n) {
+      const float a2 = sA2[n][lane];
+      float r = sR[n][lane];
+      float a[SUB], bb[SUB];
+      float f = 0.0f;
+#pragma unroll
+      for (int k = 0; k < SUB; ++k) {
+        a[k] = fast_exp2(dl[k] * a2);
+        bb[k] = u[k] * sB[n][k];
+        f = fmaf(a[k], f, bb[k]);
+      }
+#pragma unroll
+      for (int k = SUB - 1; k >= 0; --k) r = fmaf(a[k], r, bb[k]);
+      sS[n][lane] = fmaf(fast_exp2(a2 * sigma), f, sS[n][lane]);
+      sR[n][lane] = r;
+      if (j > 0) R[(jb * N + n) * D + d] = r;
+    }
+    sigma += tile_sum;
+    if (j > 0) SIG[jb * D + d] = sigma;
+  }
+  for (int n = 0; n < N; ++n) {
+    const size_t o = (cbase * N + n) * D + d;
+    Sf[o] = sS[n][lane];
+    Sr[o] = sR[n][lane];
+    P[o] = fast_exp2(sA2[n][lane] * sigma);
   }
 }
 
@@ -144,9 +204,11 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
   constexpr int SUB = static_cast<int>(kSub);
   __shared__ float sB[NM][SUB];
   __shared__ float sC[NM][SUB];
-  // per-lane forward state and scaled A, indexed by a runtime state index
-  __shared__ float sHf[NM][64];
+  // per-lane state, indexed by a runtime state index
   __shared__ float sA2[NM][64];
+  __shared__ float sHf[NM][64];
+  __shared__ float sHr[NM][64];
+  __shared__ float sCr[NM][64];
   const int lane = threadIdx.x;
   const int d = blockIdx.x * 64 + lane;
   const int c = blockIdx.y;
@@ -159,6 +221,7 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
   for (int n = 0; n < N; ++n) {
     sA2[n][lane] = A[static_cast<size_t>(d) * N + n] * kLog2e;
     sHf[n][lane] = Cf[(cbase * N + n) * D + d];
+    sCr[n][lane] = Cr[(cbase * N + n) * D + d];
   }
   const float bias = dt_bias ? dt_bias[d] : 0.0f;
   constexpr float ndir = (DIRS == 3) ? 2.0f : 1.0f;
@@ -167,36 +230,38 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
   const int nsub_c = (te - t0 + SUB - 1) / SUB;
   for (int j = 0; j < nsub_c; ++j) {
     const int ts = t0 + j * SUB;
+    const int nvalid = min(SUB, te - ts);
+    const bool last = (j == nsub_c - 1);
+    const size_t jb = cbase * nsub + j;
+    // every load of the tile is issued before any of it is used
+    float xr[SUB], dr[SUB], zr[SUB], rj[NM];
+    load_tile<T, SUB>(x, (row + ts) * D + d, D, nvalid, xr);
+    load_tile<T, SUB>(dt, (row + ts) * D + d, D, nvalid, dr);
+    if (gate) load_tile<T, SUB>(z, (row + ts) * D + d, D, nvalid, zr);
+    // the slot of the last tile is inside the allocation but never written: load and discard
+#pragma unroll
+    for (int n = 0; n < NM; ++n) rj[n] = R[(jb * N + min(n, N - 1)) * D + d];
+#pragma unroll
+    for (int n = 0; n < NM; ++n) rj[n] = (!last && n < N) ? rj[n] : 0.0f;
+    const float sj0 = SIG[jb * D + d];
+    const float sj = last ? 0.0f : sj0;
+    __syncthreads();  // previous tile's reads of sB / sC / sHr are done
+    stage_bc<T, NM, SUB>(Bm, row + ts, N, nvalid, sB, lane);
+    stage_bc<T, NM, SUB>(Cm, row + ts, N, nvalid, sC, lane);
     float dl[SUB], u[SUB], y[SUB];
 #pragma unroll
     for (int k = 0; k < SUB; ++k) {
-      const int t = ts + k;
-      float dk = 0.0f, uk = 0.0f;
-      if (t < te) {
-        const size_t i = (row + t) * D + d;
-        dk = softplus_f32(ld(dt, i) + bias);
-        uk = dk * ld(x, i);
-      }
-      dl[k] = dk;
-      u[k] = uk;
-      y[k] = 0.0f;
+      dl[k] = k < nvalid ? softplus_f32(dr[k] + bias) : 0.0f;
+      u[k] = dl[k] * xr[k];
+      y[k] = skip * xr[k];
     }
-    for (int e = lane; e < N * SUB; e += 64) {
-      const int k = e / N;
-      const int n = e - k * N;
-      const int t = ts + k;
-      float bv = 0.0f, cv = 0.0f;
-      if (t < te) {
-        bv = ld(Bm, (row + t) * N + n);
-        cv = ld(Cm, (row + t) * N + n);
-      }
-      sB[n][k] = bv;
-      sC[n][k] = cv;
+    if (DIRS & 2) {
+      // exact reverse state entering this tile from the right
+#pragma unroll
+      for (int n = 0; n < NM; ++n)
+        if (n < N) sHr[n][lane] = fmaf(fast_exp2(sA2[n][lane] * sj), sCr[n][lane], rj[n]);
     }
     __syncthreads();
-    const bool last = (j == nsub_c - 1);
-    const size_t jb = cbase * nsub + j;
-    const float sj = last ? 0.0f : SIG[jb * D + d];
 #pragma unroll 1
     for (int n = 0; n < N; ++n) {
       const float a2 = sA2[n][lane];
@@ -211,9 +276,7 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
       }
       sHf[n][lane] = hf;
       if (DIRS & 2) {
-        const float crn = Cr[(cbase * N + n) * D + d];
-        const float rj = last ? 0.0f : R[(jb * N + n) * D + d];
-        float hr = fmaf(fast_exp2(a2 * sj), crn, rj);
+        float hr = sHr[n][lane];
 #pragma unroll
         for (int k = SUB - 1; k >= 0; --k) {
           hr = fmaf(a[k], hr, bb[k]);
@@ -221,15 +284,11 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
         }
       }
     }
-    __syncthreads();
 #pragma unroll
     for (int k = 0; k < SUB; ++k) {
-      const int t = ts + k;
-      if (t < te) {
-        const size_t i = (row + t) * D + d;
-        float o = fmaf(skip, ld(x, i), y[k]);
-        if (gate) o *= silu_f32(ld(z, i));
-        from_f32(o, out + i);
+      if (k < nvalid) {
+        const float o = gate ? y[k] * silu_f32(zr[k]) : y[k];
+        from_f32(o, out + (row + ts + k) * D + d);
       }
     }
   }
@@ -242,7 +301,7 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
 // Host launchers.
 // ---------------------------------------------------------------------------
 template <typename T, int NM>
-static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipStream_t stream) {
+static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipStream_t stream, int stage) {
   char* w = static_cast<char*>(ws);
   float* Sf = reinterpret_cast<float*>(w + p.off_sf);
   float* Sr = reinterpret_cast<float*>(w + p.off_sr);
@@ -261,16 +320,21 @@ static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipSt
   const T* Cm = static_cast<const T*>(a.C);
   T* out = static_cast<T*>(a.out);
 
-  hipLaunchKernelGGL((k_summary<T, NM>), grid, dim3(64), 0, stream, x, dt, a.A, Bm, a.dt_bias, L, D, N, chunk,
-                     nchunk, nsub, Sf, Sr, P, R, SIG);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (stage < 0 || stage == 0) {
+    hipLaunchKernelGGL((k_summary<T, NM>), grid, dim3(64), 0, stream, x, dt, a.A, Bm, a.dt_bias, L, D, N, chunk,
+                       nchunk, nsub, Sf, Sr, P, R, SIG);
+    e = hipGetLastError();
+    if (e != hipSuccess || stage == 0) return e;
+  }
 
-  const size_t nthreads = static_cast<size_t>(p.batch) * N * D;
-  hipLaunchKernelGGL(k_carry, dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256), 0, stream, Sf, Sr, P,
-                     Cf, Cr, a.h_in, static_cast<int>(p.batch), nchunk, N, D);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (stage < 0 || stage == 1) {
+    const size_t nthreads = static_cast<size_t>(p.batch) * N * D;
+    hipLaunchKernelGGL(k_carry, dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256), 0, stream, Sf, Sr,
+                       P, Cf, Cr, a.h_in, static_cast<int>(p.batch), nchunk, N, D);
+    e = hipGetLastError();
+    if (e != hipSuccess || stage == 1) return e;
+  }
 
   const int gate = (a.flags & kNoGate) ? 0 : 1;
   if (a.flags & kFwdOnly) {
@@ -287,15 +351,15 @@ static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipSt
 }
 
 template <typename T>
-static hipError_t launch_dtype(const ScanArgs& a, const Plan& p, void* ws, hipStream_t stream) {
-  if (p.d_state <= 4) return launch_typed<T, 4>(a, p, ws, stream);
-  if (p.d_state <= 8) return launch_typed<T, 8>(a, p, ws, stream);
-  return launch_typed<T, 16>(a, p, ws, stream);
+static hipError_t launch_dtype(const ScanArgs& a, const Plan& p, void* ws, hipStream_t stream, int stage) {
+  if (p.d_state <= 4) return launch_typed<T, 4>(a, p, ws, stream, stage);
+  if (p.d_state <= 8) return launch_typed<T, 8>(a, p, ws, stream, stage);
+  return launch_typed<T, 16>(a, p, ws, stream, stage);
 }
 
-hipError_t launch_chunked(const ScanArgs& a, const Plan& p, void* workspace, hipStream_t stream) {
-  if (a.io_dtype == 1) return launch_dtype<bf16_t>(a, p, workspace, stream);
-  return launch_dtype<float>(a, p, workspace, stream);
+hipError_t launch_chunked(const ScanArgs& a, const Plan& p, void* workspace, hipStream_t stream, int stage) {
+  if (a.io_dtype == 1) return launch_dtype<bf16_t>(a, p, workspace, stream, stage);
+  return launch_dtype<float>(a, p, workspace, stream, stage);
 }
 
 }  // namespace bimamba

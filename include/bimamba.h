@@ -89,6 +89,20 @@ int bimamba_scan_fwd(const void* x, const void* dt, const float* A, const void* 
                      int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/* One stage of bimamba_scan_fwd, for callers that schedule other work between
+ * the stages or attribute time per stage.  stage 0 = chunk summaries (reads
+ * x, dt, B; writes the workspace), 1 = carries across chunks (workspace only),
+ * 2 = output (reads x, dt, z, B, C and the workspace; writes out).  Calling
+ * stages 0, 1, 2 in this order on one stream with the same arguments and
+ * workspace produces exactly what one bimamba_scan_fwd call produces.  Any
+ * other stage value returns BIMAMBA_ERR_INVALID_ARGUMENT.  Arguments and
+ * their checks are those of bimamba_scan_fwd. */
+int bimamba_scan_fwd_stage(int stage, const void* x, const void* dt, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* dt_bias, void* out,
+                           int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                           int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* Bytes of device workspace bimamba_scan_block needs for this shape; 0 when the
  * block is short enough for the single-kernel path (no workspace needed). */
 size_t bimamba_scan_block_workspace_bytes(int64_t batch, int64_t block_len, int64_t d_inner, int64_t d_state);

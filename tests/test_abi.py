@@ -114,6 +114,23 @@ def test_scan_fwd_rejects(kw, want):
     assert call_fwd(**kw) == want
 
 
+def test_stage_entry_point_validates():
+    lib = _lib.load()
+
+    def stage(st, **kw):
+        a = dict(x=fake(0), dt=fake(1), A=fake(2), B=fake(3), C=fake(4), D=fake(5), z=fake(6), dt_bias=fake(7),
+                 out=fake(8), ws=fake(9), wsb=0)
+        a.update(kw)
+        return lib.bimamba_scan_fwd_stage(st, a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["dt_bias"],
+                                          a["out"], 1, 64, 64, 16, _lib.BIMAMBA_BF16, 0, a["ws"], a["wsb"], None)
+
+    for bad in (-2, 3, 100):
+        assert stage(bad) == INV
+    for st in (-1, 0, 1, 2):
+        assert stage(st) == WS
+        assert stage(st, x=None) == INV
+
+
 def test_scan_fwd_checks_run_in_order():
     # z may be NULL with NO_GATE: the call then gets as far as the workspace check
     assert call_fwd(z=None, flags=_lib.FLAG_NO_GATE, wsb=0) == WS
