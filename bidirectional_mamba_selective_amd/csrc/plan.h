@@ -24,7 +24,7 @@ struct Plan {
   int64_t nchunk;  // chunks per sequence
   int64_t nsub;    // sub-chunks per full chunk (chunk / kSub)
   // workspace offsets in bytes (each 256-byte aligned)
-  size_t off_sf, off_sr, off_p, off_cf, off_cr, off_r, off_sig, total;
+  size_t off_sf, off_sr, off_p, off_cf, off_cr, off_r, off_sig, off_a2t, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -55,6 +55,7 @@ inline Plan make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_
   p.off_cr = off; off = align256(off + state);
   p.off_r = off;  off = align256(off + bound);
   p.off_sig = off; off = align256(off + sig);
+  p.off_a2t = off; off = align256(off + static_cast<size_t>(d_state) * d_inner * sizeof(float));
   p.total = off;
   return p;
 }

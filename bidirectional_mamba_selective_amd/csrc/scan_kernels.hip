@@ -5,25 +5,34 @@
 // delta = softplus(dt + dt_bias), abar = exp(delta * A), input delta * x * B,
 // readout C . h + D * x per direction, and the SiLU(z) gate on the sum.
 //
-// Work decomposition (one lane = one channel d, all d_state states in
-// registers; one wavefront = 64 channels of one chunk of one sequence):
-//   k_summary  walks each chunk backwards and produces, per (chunk, d, n):
-//              Sf = forward state at the chunk end starting from zero,
-//              Sr = reverse state at the chunk start starting from zero,
-//              P  = product of abar over the chunk,
-//              and the zero-started reverse state at every sub-chunk boundary
-//              together with the suffix sum of delta to the chunk end.
+// Work decomposition (one lane = one channel d; one wavefront = 64 channels
+// of one chunk of one sequence; a chunk is walked in tiles of kSub tokens that
+// sit in registers):
+//   k_summary  walks each chunk's tiles right to left.  Per state n and tile it
+//              forms abar and delta*x*B once per token, runs the tile-local
+//              forward recurrence from zero (composed into the chunk's forward
+//              end state with the decay of everything to the tile's right) and
+//              continues the reverse recurrence from the running state, which
+//              it stores at every tile boundary together with the suffix sum
+//              of delta to the chunk end.  Outputs per (chunk, d, n):
+//              Sf = forward end state from zero, Sr = reverse start state from
+//              zero, P = product of abar over the chunk.
 //   k_carry    composes the affine chunk maps h -> P h + S in both directions:
 //              Cf[c] = forward state entering chunk c, Cr[c] = reverse state
 //              entering chunk c from the right.
-//   k_output   walks each chunk forwards one sub-chunk of 16 tokens at a time.
-//              For every state n it forms abar and delta*x*B once per token,
-//              runs the forward recurrence from the carried state and the
-//              reverse recurrence from the exact boundary state, and
-//              accumulates C . (h_fwd + h_rev) per token; then adds the skip
-//              term, applies the gate and stores.
+//   k_output   walks each chunk's tiles left to right.  Per state n it forms
+//              abar and delta*x*B once per token and shares them between the
+//              forward recurrence (from the carried state) and the reverse
+//              recurrence (from the exact boundary state), accumulating
+//              C . (h_fwd + h_rev) per token; then skip term, gate, store.
 // The transition is diagonal per (d, n), so nothing here is a dense
-// contraction; the kernels are bound by VALU/transcendental issue.
+// contraction; the kernels are bound by VALU and transcendental issue.
+//
+// Per-channel geometric A.  When a channel's row satisfies A[d,n] = (n+1) A[d,0]
+// exactly (the S4D-real initialisation has this form), exp(delta A[d,n]) is
+// the (n+1)-th power of r = exp(delta A[d,0]); the kernels then form abar by
+// one multiplication per state instead of one exponential.  The test is exact
+// and per wavefront; any other A takes the general path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,39 +41,80 @@
 
 namespace bimamba {
 
-template <typename T>
-__device__ __forceinline__ float ld(const T* __restrict__ p, size_t i) {
-  return to_f32(p[i]);
+// ---------------------------------------------------------------------------
+// Buffer-resource I/O.  A tile's base address goes into the resource, the
+// lane's channel into the VGPR offset and the token row into the SGPR offset,
+// so loads and stores need no per-lane address arithmetic.
+// ---------------------------------------------------------------------------
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor, untyped 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const int n = bytes > 0x7fffffffull ? 0x7fffffff : static_cast<int>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, kRsrcWord3);
 }
 
-// ---------------------------------------------------------------------------
-// Tile loading: SUB consecutive tokens of one channel per lane (coalesced across
-// the 64 lanes of a wavefront), all loads issued together.
-// ---------------------------------------------------------------------------
+template <typename T>
+struct IO;
+
+template <>
+struct IO<float> {
+  static constexpr uint32_t kBytes = 4;
+  static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+  }
+  static __device__ __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+  }
+};
+
+template <>
+struct IO<bf16_t> {
+  static constexpr uint32_t kBytes = 2;
+  static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+  }
+  // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN
+  static __device__ __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const __bf16 h = static_cast<__bf16>(v);
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), r, voff, soff, 0);
+  }
+};
+
+// v[k] = tile row k (k < nvalid) of this lane's channel; rows past nvalid are
+// zero.  Row offsets are clamped so that every load is in bounds and none is
+// guarded by a branch: all of them are in flight together.
 template <typename T, int SUB>
-__device__ __forceinline__ void load_tile(const T* __restrict__ p, size_t base, int D, int nvalid, float (&v)[SUB]) {
-  // Addresses are clamped into the valid range and the surplus values zeroed
-  // afterwards, so the loads carry no branches and are all in flight at once.
+__device__ __forceinline__ void load_col(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t row_bytes, int nvalid,
+                                         float (&v)[SUB]) {
 #pragma unroll
-  for (int k = 0; k < SUB; ++k) v[k] = ld(p, base + static_cast<size_t>(min(k, nvalid - 1)) * D);
+  for (int k = 0; k < SUB; ++k) v[k] = IO<T>::load(r, voff, static_cast<uint32_t>(min(k, nvalid - 1)) * row_bytes);
 #pragma unroll
   for (int k = 0; k < SUB; ++k) v[k] = k < nvalid ? v[k] : 0.0f;
 }
 
-// Stage a [SUB x N] tile of a token-major [*, N] matrix into LDS as fp32 [NM][SUB]
-// (state-major, so a state's SUB values are contiguous); missing tokens and
-// states >= N become 0.
+// As load_col, but rows past nvalid repeat the last valid row (for values whose
+// surplus rows are never used).
+template <typename T, int SUB>
+__device__ __forceinline__ void load_col_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t row_bytes, int nvalid,
+                                             float (&v)[SUB]) {
+#pragma unroll
+  for (int k = 0; k < SUB; ++k) v[k] = IO<T>::load(r, voff, static_cast<uint32_t>(min(k, nvalid - 1)) * row_bytes);
+}
+
+// Stage a [SUB x N] tile of a token-major [*, N] matrix (base = first row) into
+// LDS as fp32 [NM][SUB], state-major; missing tokens and states >= N become 0.
 template <typename T, int NM, int SUB>
-__device__ __forceinline__ void stage_bc(const T* __restrict__ M, size_t row0, int N, int nvalid, float (*dst)[SUB],
-                                         int lane) {
+__device__ __forceinline__ void stage_bc(const T* __restrict__ base, int N, int nvalid, float (*dst)[SUB], int lane) {
   constexpr int PER = (NM * SUB + 63) / 64;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, static_cast<size_t>(nvalid) * N * IO<T>::kBytes);
   float v[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = i * 64 + lane;
     const int k = e / NM;
     const int n = e - k * NM;
-    v[i] = ld(M, (row0 + min(k, nvalid - 1)) * N + min(n, N - 1));
+    v[i] = IO<T>::load(r, static_cast<uint32_t>(min(k, nvalid - 1) * N + min(n, N - 1)) * IO<T>::kBytes, 0);
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -75,16 +125,65 @@ __device__ __forceinline__ void stage_bc(const T* __restrict__ M, size_t row0, i
   }
 }
 
+// Whether every lane's A row is geometric: A[d,n] == (n+1) * A[d,0] exactly.
+__device__ __forceinline__ bool wave_geometric(bool lane_geo) { return __all(lane_geo ? 1 : 0) != 0; }
+
+// ---------------------------------------------------------------------------
+// k_summary tile body: all states of one tile, right to left across tiles.
+// f is the tile-local forward state from zero; S accumulates it decayed to the
+// chunk end; r is the running reverse state.  GEO: w[k] = exp(delta_k A[d,0])
+// and abar is its power; otherwise w[k] = delta_k.
+// ---------------------------------------------------------------------------
+template <int SUB, bool GEO>
+__device__ __forceinline__ void summary_tile_states(int N, int lane, const float (&w)[SUB], const float (&u)[SUB],
+                                                    float sigma, float a20, float (*sB)[SUB],
+                                                    const float* __restrict__ Arow, float (*sR)[64],
+                                                    float (*sS)[64], float* __restrict__ Rdst, uint32_t r_stride,
+                                                    bool store_r) {
+  float a[SUB];
+  float q = 1.0f, qstep = 1.0f;
+  float a2n = 0.0f;
+  if (GEO) {
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) a[k] = 1.0f;
+    qstep = fast_exp2(a20 * sigma);
+  } else {
+    a2n = Arow[0] * kLog2e;
+  }
+#pragma unroll 1
+  for (int n = 0; n < N; ++n) {
+    const float a2 = a2n;
+    if (!GEO) a2n = Arow[min(n + 1, N - 1)] * kLog2e;  // one state ahead
+    float bb[SUB];
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) {
+      a[k] = GEO ? a[k] * w[k] : fast_exp2(w[k] * a2);
+      bb[k] = u[k] * sB[n][k];
+    }
+    // the forward (ascending) and reverse (descending) chains are independent:
+    // interleaving them doubles the instruction-level parallelism
+    float f = 0.0f;
+    float r = sR[n][lane];
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      f = fmaf(a[s], f, bb[s]);
+      r = fmaf(a[SUB - 1 - s], r, bb[SUB - 1 - s]);
+    }
+    if (GEO) {
+      q *= qstep;
+    } else {
+      q = fast_exp2(a2 * sigma);
+    }
+    sS[n][lane] = fmaf(q, f, sS[n][lane]);
+    sR[n][lane] = r;
+    if (store_r) Rdst[static_cast<size_t>(n) * r_stride] = r;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // k_summary: grid (d_inner / 64, nchunk, batch), block 64.
-// Walks the chunk's tiles from right to left.  Per state n and tile it forms
-// abar and delta*x*B once per token, runs the tile-local forward recurrence
-// from zero (composed into the chunk's forward end state with the decay of
-// everything to the right of the tile) and continues the reverse recurrence
-// from the running state; the running reverse state is stored at every tile
-// boundary.
 // ---------------------------------------------------------------------------
-template <typename T, int NM>
+template <typename T, int NM, bool GEO>
 __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T* __restrict__ dt,
                                                 const float* __restrict__ A, const T* __restrict__ Bm,
                                                 const float* __restrict__ dt_bias, int L, int D, int N, int chunk,
@@ -93,7 +192,6 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
                                                 float* __restrict__ R, float* __restrict__ SIG) {
   constexpr int SUB = static_cast<int>(kSub);
   __shared__ float sB[NM][SUB];
-  __shared__ float sA2[NM][64];
   __shared__ float sR[NM][64];
   __shared__ float sS[NM][64];
   const int lane = threadIdx.x;
@@ -105,23 +203,34 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
   const size_t row = static_cast<size_t>(b) * L;
   const size_t cbase = static_cast<size_t>(b) * nchunk + c;
 
+  const float* __restrict__ Arow = A + static_cast<size_t>(d) * N;
+  const float a0 = Arow[0];
+  bool geo_lane = true;
   for (int n = 0; n < N; ++n) {
-    sA2[n][lane] = A[static_cast<size_t>(d) * N + n] * kLog2e;
+    const float an = Arow[n];
+    geo_lane = geo_lane && (an == static_cast<float>(n + 1) * a0);
     sR[n][lane] = 0.0f;
     sS[n][lane] = 0.0f;
   }
+  // Each wavefront runs in exactly one of the two instantiations (general / geometric A).
+  if (wave_geometric(geo_lane) != GEO) return;
+  const float a20 = a0 * kLog2e;
   const float bias = dt_bias ? dt_bias[d] : 0.0f;
+  const uint32_t voff = static_cast<uint32_t>(lane) * IO<T>::kBytes;
+  const uint32_t row_bytes = static_cast<uint32_t>(D) * IO<T>::kBytes;
   float sigma = 0.0f;  // sum of delta from the current tile's right edge to the chunk end
 
   const int nsub_c = (te - t0 + SUB - 1) / SUB;
   for (int j = nsub_c - 1; j >= 0; --j) {
     const int ts = t0 + j * SUB;
     const int nvalid = min(SUB, te - ts);
+    const size_t tile = (row + ts) * D + static_cast<size_t>(blockIdx.x) * 64;
+    const size_t tile_bytes = static_cast<size_t>(nvalid) * row_bytes;
     float xr[SUB], dr[SUB];
-    load_tile<T, SUB>(x, (row + ts) * D + d, D, nvalid, xr);
-    load_tile<T, SUB>(dt, (row + ts) * D + d, D, nvalid, dr);
-    __syncthreads();  // previous tile's reads of sB are done
-    stage_bc<T, NM, SUB>(Bm, row + ts, N, nvalid, sB, lane);
+    load_col_raw<T, SUB>(make_rsrc(x + tile, tile_bytes), voff, row_bytes, nvalid, xr);
+    load_col_raw<T, SUB>(make_rsrc(dt + tile, tile_bytes), voff, row_bytes, nvalid, dr);
+    __syncthreads();  // the previous tile's reads of sB are done
+    stage_bc<T, NM, SUB>(Bm + (row + ts) * N, N, nvalid, sB, lane);
     float dl[SUB], u[SUB];
     float tile_sum = 0.0f;
 #pragma unroll
@@ -132,23 +241,14 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
     }
     __syncthreads();
     const size_t jb = cbase * nsub + (j - 1);
-#pragma unroll 1
-    for (int n = 0; n < N; ++n) {
-      const float a2 = sA2[n][lane];
-      float r = sR[n][lane];
-      float a[SUB], bb[SUB];
-      float f = 0.0f;
+    float* Rdst = R + jb * N * D + d;
+    if (GEO) {
+      float w[SUB];
 #pragma unroll
-      for (int k = 0; k < SUB; ++k) {
-        a[k] = fast_exp2(dl[k] * a2);
-        bb[k] = u[k] * sB[n][k];
-        f = fmaf(a[k], f, bb[k]);
-      }
-#pragma unroll
-      for (int k = SUB - 1; k >= 0; --k) r = fmaf(a[k], r, bb[k]);
-      sS[n][lane] = fmaf(fast_exp2(a2 * sigma), f, sS[n][lane]);
-      sR[n][lane] = r;
-      if (j > 0) R[(jb * N + n) * D + d] = r;
+      for (int k = 0; k < SUB; ++k) w[k] = fast_exp2(dl[k] * a20);
+      summary_tile_states<SUB, true>(N, lane, w, u, sigma, a20, sB, Arow, sR, sS, Rdst, D, j > 0);
+    } else {
+      summary_tile_states<SUB, false>(N, lane, dl, u, sigma, a20, sB, Arow, sR, sS, Rdst, D, j > 0);
     }
     sigma += tile_sum;
     if (j > 0) SIG[jb * D + d] = sigma;
@@ -157,16 +257,19 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
     const size_t o = (cbase * N + n) * D + d;
     Sf[o] = sS[n][lane];
     Sr[o] = sR[n][lane];
-    P[o] = fast_exp2(sA2[n][lane] * sigma);
+    P[o] = fast_exp2(Arow[n] * kLog2e * sigma);
   }
 }
 
 // ---------------------------------------------------------------------------
 // k_carry: one thread per (b, n, d); sequential over chunks in both directions.
 // ---------------------------------------------------------------------------
+// The batch-0 threads also write the transposed table A2T[n][d] = A[d,n] * log2(e)
+// that the output pass reads with coalesced loads.
 __global__ __launch_bounds__(256) void k_carry(const float* __restrict__ Sf, const float* __restrict__ Sr,
                                                const float* __restrict__ P, float* __restrict__ Cf,
-                                               float* __restrict__ Cr, const float* __restrict__ h_in, int batch,
+                                               float* __restrict__ Cr, const float* __restrict__ h_in,
+                                               const float* __restrict__ A, float* __restrict__ A2T, int batch,
                                                int nchunk, int N, int D) {
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const size_t total = static_cast<size_t>(batch) * N * D;
@@ -174,6 +277,7 @@ __global__ __launch_bounds__(256) void k_carry(const float* __restrict__ Sf, con
   const int d = static_cast<int>(idx % D);
   const int n = static_cast<int>((idx / D) % N);
   const int b = static_cast<int>(idx / (static_cast<size_t>(D) * N));
+  if (b == 0) A2T[static_cast<size_t>(n) * D + d] = A[static_cast<size_t>(d) * N + n] * kLog2e;
   float cf = h_in ? h_in[(static_cast<size_t>(b) * D + d) * N + n] : 0.0f;
   for (int c = 0; c < nchunk; ++c) {
     const size_t o = ((static_cast<size_t>(b) * nchunk + c) * N + n) * D + d;
@@ -189,10 +293,58 @@ __global__ __launch_bounds__(256) void k_carry(const float* __restrict__ Sf, con
 }
 
 // ---------------------------------------------------------------------------
-// k_output: grid (d_inner / 64, nchunk, batch), block 64.
+// k_output tile body: all states of one tile.  GEO: w[k] = exp(delta_k A[d,0])
+// and abar is its power; otherwise w[k] = delta_k.
 // DIRS: bit 0 = forward readout, bit 1 = reverse readout.
 // ---------------------------------------------------------------------------
-template <typename T, int NM, int DIRS>
+// A2T points at this lane's column of the transposed table A[d,n] * log2(e), [N][D].
+template <int SUB, int DIRS, bool GEO>
+__device__ __forceinline__ void output_tile_states(int N, int D, int lane, const float (&w)[SUB],
+                                                   const float (&u)[SUB], float (&y)[SUB], float (*sB)[SUB],
+                                                   float (*sC)[SUB], const float* __restrict__ A2T,
+                                                   float (*sHf)[64], float (*sHr)[64]) {
+  float a[SUB];
+  float a2n = 0.0f;
+  if (GEO) {
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) a[k] = 1.0f;
+  } else {
+    a2n = A2T[0];
+  }
+#pragma unroll 1
+  for (int n = 0; n < N; ++n) {
+    const float a2 = a2n;
+    if (!GEO) a2n = A2T[static_cast<size_t>(min(n + 1, N - 1)) * D];  // one state ahead
+    float bb[SUB];
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) {
+      a[k] = GEO ? a[k] * w[k] : fast_exp2(w[k] * a2);
+      bb[k] = u[k] * sB[n][k];
+    }
+    // keep the C reads below this point: B and C values are then never live together
+    __builtin_amdgcn_sched_barrier(0);
+    float hf = sHf[n][lane];
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) {
+      hf = fmaf(a[k], hf, bb[k]);
+      if (DIRS & 1) y[k] = fmaf(sC[n][k], hf, y[k]);
+    }
+    if (DIRS & 2) {
+      float hr = sHr[n][lane];
+#pragma unroll
+      for (int k = SUB - 1; k >= 0; --k) {
+        hr = fmaf(a[k], hr, bb[k]);
+        y[k] = fmaf(sC[n][k], hr, y[k]);
+      }
+    }
+    sHf[n][lane] = hf;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_output: grid (d_inner / 64, nchunk, batch), block 64.
+// ---------------------------------------------------------------------------
+template <typename T, int NM, int DIRS, bool GEO>
 __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T* __restrict__ dt,
                                                const T* __restrict__ z, const float* __restrict__ A,
                                                const T* __restrict__ Bm, const T* __restrict__ Cm,
@@ -200,15 +352,14 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
                                                T* __restrict__ out, int L, int D, int N, int chunk, int nchunk,
                                                int nsub, int gate, const float* __restrict__ Cf,
                                                const float* __restrict__ Cr, const float* __restrict__ R,
-                                               const float* __restrict__ SIG, float* __restrict__ h_out) {
+                                               const float* __restrict__ SIG, const float* __restrict__ A2T,
+                                               float* __restrict__ h_out) {
   constexpr int SUB = static_cast<int>(kSub);
   __shared__ float sB[NM][SUB];
   __shared__ float sC[NM][SUB];
   // per-lane state, indexed by a runtime state index
-  __shared__ float sA2[NM][64];
   __shared__ float sHf[NM][64];
   __shared__ float sHr[NM][64];
-  __shared__ float sCr[NM][64];
   const int lane = threadIdx.x;
   const int d = blockIdx.x * 64 + lane;
   const int c = blockIdx.y;
@@ -218,14 +369,25 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
   const size_t row = static_cast<size_t>(b) * L;
   const size_t cbase = static_cast<size_t>(b) * nchunk + c;
 
+  const float* __restrict__ Arow = A + static_cast<size_t>(d) * N;
+  const float a0 = Arow[0];
+  bool geo_lane = true;
   for (int n = 0; n < N; ++n) {
-    sA2[n][lane] = A[static_cast<size_t>(d) * N + n] * kLog2e;
+    const float an = Arow[n];
+    geo_lane = geo_lane && (an == static_cast<float>(n + 1) * a0);
     sHf[n][lane] = Cf[(cbase * N + n) * D + d];
-    sCr[n][lane] = Cr[(cbase * N + n) * D + d];
   }
+  // Each wavefront runs in exactly one of the two instantiations (general / geometric A).
+  if (wave_geometric(geo_lane) != GEO) return;
+  constexpr bool geo = GEO;
+  const float a20 = a0 * kLog2e;
   const float bias = dt_bias ? dt_bias[d] : 0.0f;
   constexpr float ndir = (DIRS == 3) ? 2.0f : 1.0f;
   const float skip = Dv ? ndir * Dv[d] : 0.0f;
+  const uint32_t voff = static_cast<uint32_t>(lane) * IO<T>::kBytes;
+  const uint32_t row_bytes = static_cast<uint32_t>(D) * IO<T>::kBytes;
+  const uint32_t voff4 = static_cast<uint32_t>(lane) * 4u;
+  const uint32_t nstride4 = static_cast<uint32_t>(D) * 4u;
 
   const int nsub_c = (te - t0 + SUB - 1) / SUB;
   for (int j = 0; j < nsub_c; ++j) {
@@ -233,21 +395,32 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
     const int nvalid = min(SUB, te - ts);
     const bool last = (j == nsub_c - 1);
     const size_t jb = cbase * nsub + j;
+    const size_t tile = (row + ts) * D + static_cast<size_t>(blockIdx.x) * 64;
+    const size_t tile_bytes = static_cast<size_t>(nvalid) * row_bytes;
     // every load of the tile is issued before any of it is used
-    float xr[SUB], dr[SUB], zr[SUB], rj[NM];
-    load_tile<T, SUB>(x, (row + ts) * D + d, D, nvalid, xr);
-    load_tile<T, SUB>(dt, (row + ts) * D + d, D, nvalid, dr);
-    if (gate) load_tile<T, SUB>(z, (row + ts) * D + d, D, nvalid, zr);
-    // the slot of the last tile is inside the allocation but never written: load and discard
+    float xr[SUB], dr[SUB], rj[NM], cr[NM], a2t[NM];
+    load_col_raw<T, SUB>(make_rsrc(x + tile, tile_bytes), voff, row_bytes, nvalid, xr);
+    load_col_raw<T, SUB>(make_rsrc(dt + tile, tile_bytes), voff, row_bytes, nvalid, dr);
+    // the boundary slot of a chunk's last tile is allocated but never written: load and discard
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(R + jb * N * D + static_cast<size_t>(blockIdx.x) * 64,
+                                                static_cast<size_t>(N) * D * 4);
 #pragma unroll
-    for (int n = 0; n < NM; ++n) rj[n] = R[(jb * N + min(n, N - 1)) * D + d];
+    for (int n = 0; n < NM; ++n) rj[n] = IO<float>::load(rr, voff4, static_cast<uint32_t>(min(n, N - 1)) * nstride4);
 #pragma unroll
     for (int n = 0; n < NM; ++n) rj[n] = (!last && n < N) ? rj[n] : 0.0f;
+    if (DIRS & 2) {
+#pragma unroll
+      for (int n = 0; n < NM; ++n) cr[n] = Cr[(cbase * N + min(n, N - 1)) * D + d];
+      if (!geo) {
+#pragma unroll
+        for (int n = 0; n < NM; ++n) a2t[n] = A2T[static_cast<size_t>(min(n, N - 1)) * D + d];
+      }
+    }
     const float sj0 = SIG[jb * D + d];
     const float sj = last ? 0.0f : sj0;
-    __syncthreads();  // previous tile's reads of sB / sC / sHr are done
-    stage_bc<T, NM, SUB>(Bm, row + ts, N, nvalid, sB, lane);
-    stage_bc<T, NM, SUB>(Cm, row + ts, N, nvalid, sC, lane);
+    __syncthreads();  // the previous tile's reads of sB / sC / sHr are done
+    stage_bc<T, NM, SUB>(Bm + (row + ts) * N, N, nvalid, sB, lane);
+    stage_bc<T, NM, SUB>(Cm + (row + ts) * N, N, nvalid, sC, lane);
     float dl[SUB], u[SUB], y[SUB];
 #pragma unroll
     for (int k = 0; k < SUB; ++k) {
@@ -257,39 +430,40 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
     }
     if (DIRS & 2) {
       // exact reverse state entering this tile from the right
+      if (geo) {
+        const float qstep = fast_exp2(a20 * sj);
+        float q = 1.0f;
 #pragma unroll
-      for (int n = 0; n < NM; ++n)
-        if (n < N) sHr[n][lane] = fmaf(fast_exp2(sA2[n][lane] * sj), sCr[n][lane], rj[n]);
+        for (int n = 0; n < NM; ++n) {
+          q *= qstep;
+          if (n < N) sHr[n][lane] = fmaf(q, cr[n], rj[n]);
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < NM; ++n)
+          if (n < N) sHr[n][lane] = fmaf(fast_exp2(a2t[n] * sj), cr[n], rj[n]);
+      }
     }
     __syncthreads();
-#pragma unroll 1
-    for (int n = 0; n < N; ++n) {
-      const float a2 = sA2[n][lane];
-      float hf = sHf[n][lane];
-      float a[SUB], bb[SUB];
+    if (geo) {
+      float w[SUB];
 #pragma unroll
-      for (int k = 0; k < SUB; ++k) {
-        a[k] = fast_exp2(dl[k] * a2);
-        bb[k] = u[k] * sB[n][k];
-        hf = fmaf(a[k], hf, bb[k]);
-        if (DIRS & 1) y[k] = fmaf(sC[n][k], hf, y[k]);
-      }
-      sHf[n][lane] = hf;
-      if (DIRS & 2) {
-        float hr = sHr[n][lane];
-#pragma unroll
-        for (int k = SUB - 1; k >= 0; --k) {
-          hr = fmaf(a[k], hr, bb[k]);
-          y[k] = fmaf(sC[n][k], hr, y[k]);
-        }
-      }
+      for (int k = 0; k < SUB; ++k) w[k] = fast_exp2(dl[k] * a20);
+      output_tile_states<SUB, DIRS, true>(N, D, lane, w, u, y, sB, sC, A2T + d, sHf, sHr);
+    } else {
+      output_tile_states<SUB, DIRS, false>(N, D, lane, dl, u, y, sB, sC, A2T + d, sHf, sHr);
     }
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + tile, tile_bytes);
+    if (gate) {
+      float zr[SUB];
+      load_col_raw<T, SUB>(make_rsrc(z + tile, tile_bytes), voff, row_bytes, nvalid, zr);
 #pragma unroll
-    for (int k = 0; k < SUB; ++k) {
-      if (k < nvalid) {
-        const float o = gate ? y[k] * silu_f32(zr[k]) : y[k];
-        from_f32(o, out + (row + ts + k) * D + d);
-      }
+      for (int k = 0; k < SUB; ++k)
+        if (k < nvalid) IO<T>::store(y[k] * silu_f32(zr[k]), ro, voff, static_cast<uint32_t>(k) * row_bytes);
+    } else {
+#pragma unroll
+      for (int k = 0; k < SUB; ++k)
+        if (k < nvalid) IO<T>::store(y[k], ro, voff, static_cast<uint32_t>(k) * row_bytes);
     }
   }
   if (h_out != nullptr && c == nchunk - 1) {
@@ -300,6 +474,17 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
 // ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
+template <typename T, int NM, int DIRS>
+static void launch_output(dim3 grid, hipStream_t stream, const T* x, const T* dt, const T* z, const ScanArgs& a,
+                          const T* Bm, const T* Cm, T* out, int L, int D, int N, int chunk, int nchunk, int nsub,
+                          int gate, const float* Cf, const float* Cr, const float* R, const float* SIG,
+                          const float* A2T) {
+  hipLaunchKernelGGL((k_output<T, NM, DIRS, true>), grid, dim3(64), 0, stream, x, dt, z, a.A, Bm, Cm, a.D,
+                     a.dt_bias, out, L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R, SIG, A2T, a.h_out);
+  hipLaunchKernelGGL((k_output<T, NM, DIRS, false>), grid, dim3(64), 0, stream, x, dt, z, a.A, Bm, Cm, a.D,
+                     a.dt_bias, out, L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R, SIG, A2T, a.h_out);
+}
+
 template <typename T, int NM>
 static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipStream_t stream, int stage) {
   char* w = static_cast<char*>(ws);
@@ -310,6 +495,7 @@ static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipSt
   float* Cr = reinterpret_cast<float*>(w + p.off_cr);
   float* R = reinterpret_cast<float*>(w + p.off_r);
   float* SIG = reinterpret_cast<float*>(w + p.off_sig);
+  float* A2T = reinterpret_cast<float*>(w + p.off_a2t);
   const int L = static_cast<int>(p.seqlen), D = static_cast<int>(p.d_inner), N = static_cast<int>(p.d_state);
   const int chunk = static_cast<int>(p.chunk), nchunk = static_cast<int>(p.nchunk), nsub = static_cast<int>(p.nsub);
   const dim3 grid(static_cast<unsigned>(D / 64), static_cast<unsigned>(nchunk), static_cast<unsigned>(p.batch));
@@ -321,9 +507,13 @@ static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipSt
   T* out = static_cast<T*>(a.out);
 
   hipError_t e = hipSuccess;
+  // Both A-path instantiations are launched; every wavefront exits from the one
+  // that does not match its channels' A rows.
   if (stage < 0 || stage == 0) {
-    hipLaunchKernelGGL((k_summary<T, NM>), grid, dim3(64), 0, stream, x, dt, a.A, Bm, a.dt_bias, L, D, N, chunk,
-                       nchunk, nsub, Sf, Sr, P, R, SIG);
+    hipLaunchKernelGGL((k_summary<T, NM, true>), grid, dim3(64), 0, stream, x, dt, a.A, Bm, a.dt_bias, L, D, N,
+                       chunk, nchunk, nsub, Sf, Sr, P, R, SIG);
+    hipLaunchKernelGGL((k_summary<T, NM, false>), grid, dim3(64), 0, stream, x, dt, a.A, Bm, a.dt_bias, L, D, N,
+                       chunk, nchunk, nsub, Sf, Sr, P, R, SIG);
     e = hipGetLastError();
     if (e != hipSuccess || stage == 0) return e;
   }
@@ -331,21 +521,21 @@ static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipSt
   if (stage < 0 || stage == 1) {
     const size_t nthreads = static_cast<size_t>(p.batch) * N * D;
     hipLaunchKernelGGL(k_carry, dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256), 0, stream, Sf, Sr,
-                       P, Cf, Cr, a.h_in, static_cast<int>(p.batch), nchunk, N, D);
+                       P, Cf, Cr, a.h_in, a.A, A2T, static_cast<int>(p.batch), nchunk, N, D);
     e = hipGetLastError();
     if (e != hipSuccess || stage == 1) return e;
   }
 
   const int gate = (a.flags & kNoGate) ? 0 : 1;
   if (a.flags & kFwdOnly) {
-    hipLaunchKernelGGL((k_output<T, NM, 1>), grid, dim3(64), 0, stream, x, dt, z, a.A, Bm, Cm, a.D, a.dt_bias, out,
-                       L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R, SIG, a.h_out);
+    launch_output<T, NM, 1>(grid, stream, x, dt, z, a, Bm, Cm, out, L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R,
+                            SIG, A2T);
   } else if (a.flags & kRevOnly) {
-    hipLaunchKernelGGL((k_output<T, NM, 2>), grid, dim3(64), 0, stream, x, dt, z, a.A, Bm, Cm, a.D, a.dt_bias, out,
-                       L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R, SIG, a.h_out);
+    launch_output<T, NM, 2>(grid, stream, x, dt, z, a, Bm, Cm, out, L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R,
+                            SIG, A2T);
   } else {
-    hipLaunchKernelGGL((k_output<T, NM, 3>), grid, dim3(64), 0, stream, x, dt, z, a.A, Bm, Cm, a.D, a.dt_bias, out,
-                       L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R, SIG, a.h_out);
+    launch_output<T, NM, 3>(grid, stream, x, dt, z, a, Bm, Cm, out, L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R,
+                            SIG, A2T);
   }
   return hipGetLastError();
 }

@@ -68,14 +68,18 @@ def test_tiny_fp32_workload():
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_ragged_multichunk(io):
-    """Many chunks, a ragged last chunk and a ragged last sub-chunk, batch 2."""
-    check_variants(case(2, 1000, 128, 16, io), io, tag=f"ragged_{io}")
+@pytest.mark.parametrize("a_jitter", [0.0, 0.2])
+def test_ragged_multichunk(io, a_jitter):
+    """Many chunks, a ragged last chunk and a ragged last sub-chunk, batch 2; A with (jitter 0) and without
+    (jitter 0.2) the per-channel geometric structure."""
+    check_variants(case(2, 1000, 128, 16, io, a_jitter=a_jitter), io, tag=f"ragged_{io}_j{a_jitter}")
 
 
 @pytest.mark.parametrize("N", [1, 3, 4, 5, 8, 12, 16])
-def test_state_sizes(N):
-    check_variants(case(1, 333, 64, N, "f32", seed=N), "f32", variants=VARIANTS[:2], tag=f"N{N}")
+@pytest.mark.parametrize("a_jitter", [0.0, 0.2])
+def test_state_sizes(N, a_jitter):
+    check_variants(case(1, 333, 64, N, "f32", seed=N, a_jitter=a_jitter), "f32", variants=VARIANTS[:2],
+                   tag=f"N{N}_j{a_jitter}")
 
 
 @pytest.mark.parametrize("L", [1, 2, 15, 16, 17, 31, 33, 4097])
@@ -88,9 +92,29 @@ def test_general_A_matrix():
     check_variants(case(1, 700, 192, 16, "f32", a_jitter=0.3), "f32", variants=VARIANTS[:2], tag="jitterA")
 
 
-def test_impulse_crosses_chunks():
+def test_mixed_A_rows():
+    """Geometric rows in some wavefronts and general rows in others (and one general row inside an otherwise
+    geometric wavefront): each wavefront picks its own path."""
+    inp = case(1, 900, 256, 16, "f32")
+    A = inp["A"].copy()
+    A[64:128] *= np.float32(1.0) + np.float32(0.05) * np.linspace(-1, 1, 16, dtype=np.float32)[None, :]
+    A[200, 7] *= np.float32(1.001)
+    inp["A"] = A
+    check_variants(inp, "f32", variants=VARIANTS[:2], tag="mixedA")
+
+
+def test_geometric_rows_other_than_default():
+    """A[d, n] = (n + 1) * a_d with a per-channel a_d != -1 (still geometric)."""
+    inp = case(1, 900, 128, 16, "f32")
+    a = -np.exp(np.random.default_rng(3).uniform(-1.0, 1.0, size=128)).astype(np.float32)
+    inp["A"] = (a[:, None] * np.arange(1, 17, dtype=np.float32)[None, :]).astype(np.float32)
+    check_variants(inp, "f32", variants=VARIANTS[:2], tag="geoA")
+
+
+@pytest.mark.parametrize("a_jitter", [0.0, 0.2])
+def test_impulse_crosses_chunks(a_jitter):
     """An impulse in one channel set: every other output is carry-only (both directions)."""
-    inp = case(1, 4000, 64, 16, "f32")
+    inp = case(1, 4000, 64, 16, "f32", a_jitter=a_jitter)
     inp["x"] = np.zeros_like(inp["x"])
     inp["x"][0, 1234, :] = 1.0
     inp["dt_bias"] = np.full_like(inp["dt_bias"], -6.0)  # delta ~ 2.5e-3: memory of thousands of tokens
@@ -121,9 +145,10 @@ def test_layer_2k_workload():
     check_variants(inp, w.io_dtype, variants=VARIANTS[:4], chan=chan, tag="layer_2k")
 
 
-def test_layer_2k_fp32_ssm_only():
+@pytest.mark.parametrize("a_jitter", [0.0, 0.2])
+def test_layer_2k_fp32_ssm_only(a_jitter):
     """Same shape with fp32 I/O: the SSM-only part at the tight fp32 bar."""
-    inp = case(1, 2048, 4096, 16, "f32")
+    inp = case(1, 2048, 4096, 16, "f32", a_jitter=a_jitter)
     chan = np.arange(3, 4096, 16)
     check_variants(inp, "f32", variants=VARIANTS[1:2], chan=chan, tag="layer_2k_f32")
 
@@ -135,3 +160,11 @@ def test_long_64k_workload():
     inp = case(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype)
     chan = np.concatenate([np.arange(0, 64, 7), np.arange(2000, 2064, 9), np.arange(4032, 4096, 5)])
     check_variants(inp, w.io_dtype, variants=VARIANTS[:2], chan=chan, tag="long_64k")
+
+
+def test_long_64k_general_A():
+    """The L = 65536 launch with A off the geometric structure (general exponential path)."""
+    w = I.WORKLOADS["long_64k_bf16"]
+    inp = case(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype, a_jitter=0.2)
+    chan = np.arange(17, w.d_inner, 211)
+    check_variants(inp, w.io_dtype, variants=VARIANTS[1:2], chan=chan, tag="long_64k_jitterA")
