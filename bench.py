@@ -138,13 +138,15 @@ def main():
 
     x, dt, z, B, C = (up(k) for k in ("x", "dt", "z", "B", "C"))
     A, Dv, bias = (up(k, False) for k in ("A", "D", "dt_bias"))
+    # the same workload with A moved off its per-channel geometric structure (general exponential path)
+    A_gen = torch.from_numpy(I.make_params(w.d_inner, w.d_state, a_jitter=0.2)[0]).to(dev)
     out = torch.empty_like(x)
     need = bm.bimamba_scan_fwd_workspace_bytes(w.batch, w.seqlen, w.d_inner, w.d_state)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        bm.bimamba_scan_fwd(x, dt, A, B, C, Dv, z, bias, out=out, workspace=ws, stream=stream)
+    def step(a_mat=A):
+        bm.bimamba_scan_fwd(x, dt, a_mat, B, C, Dv, z, bias, out=out, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -164,6 +166,17 @@ def main():
     ms_step = wall * 1e3 / args.steps
     ms_step_ev = ev0.elapsed_time(ev1) / args.steps
     log(f"timed {args.steps} steps: {ms_step:.4f} ms/step wall, {ms_step_ev:.4f} ms/step events")
+
+    # the general-A path on the same inputs (reported beside the headline)
+    for _ in range(2):
+        step(A_gen)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(A_gen)
+    torch.cuda.synchronize()
+    ms_step_gen = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"general A: {ms_step_gen:.4f} ms/step")
 
     # per-kernel attribution on the same stream: staged entry point, events between stages
     names = ("k_summary", "k_carry", "k_output")
@@ -196,7 +209,8 @@ def main():
     achieved = FLOP_PER_ELEMENT_OUTPUT * elems / t_out / 1e12
     traffic = profiled_traffic(elems) if w.name == "long_64k_bf16" else None
     roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / VALU_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": "k_output",
+                "frac": round(achieved / VALU_PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel": "k_output (output pass, both A instantiations; the geometric one does the work here)",
                 "kernel_ms": round(per["k_output"], 4)}
     hbm_gbs = abytes / (ms_step * 1e-3) / 1e9
     line = {
@@ -218,6 +232,9 @@ def main():
         "hbm": {"algorithmic_bytes": abytes, "achieved_gbs": round(hbm_gbs, 1),
                 "frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4), "peak_gbs": HBM_PEAK_GBS},
         "kernels_ms": {k: round(v, 4) for k, v in per.items()},
+        "general_A": {"ms_per_step": round(ms_step_gen, 4), "tokens_per_s": round(tokens / (ms_step_gen * 1e-3), 1),
+                      "note": "A[d,n] = -(n+1)*(1+0.2*U(-1,1)): no per-channel geometric structure, one exp per "
+                              "(token, channel, state) in each pass"},
         "ms_per_step_events": round(ms_step_ev, 4),
     }
     if not args.no_cpu_baseline:

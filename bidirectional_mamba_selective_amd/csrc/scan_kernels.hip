@@ -206,14 +206,13 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
   const float* __restrict__ Arow = A + static_cast<size_t>(d) * N;
   const float a0 = Arow[0];
   bool geo_lane = true;
+  for (int n = 0; n < N; ++n) geo_lane = geo_lane && (Arow[n] == static_cast<float>(n + 1) * a0);
+  // Each wavefront runs in exactly one of the two instantiations (general / geometric A).
+  if (wave_geometric(geo_lane) != GEO) return;
   for (int n = 0; n < N; ++n) {
-    const float an = Arow[n];
-    geo_lane = geo_lane && (an == static_cast<float>(n + 1) * a0);
     sR[n][lane] = 0.0f;
     sS[n][lane] = 0.0f;
   }
-  // Each wavefront runs in exactly one of the two instantiations (general / geometric A).
-  if (wave_geometric(geo_lane) != GEO) return;
   const float a20 = a0 * kLog2e;
   const float bias = dt_bias ? dt_bias[d] : 0.0f;
   const uint32_t voff = static_cast<uint32_t>(lane) * IO<T>::kBytes;
@@ -372,13 +371,10 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
   const float* __restrict__ Arow = A + static_cast<size_t>(d) * N;
   const float a0 = Arow[0];
   bool geo_lane = true;
-  for (int n = 0; n < N; ++n) {
-    const float an = Arow[n];
-    geo_lane = geo_lane && (an == static_cast<float>(n + 1) * a0);
-    sHf[n][lane] = Cf[(cbase * N + n) * D + d];
-  }
+  for (int n = 0; n < N; ++n) geo_lane = geo_lane && (Arow[n] == static_cast<float>(n + 1) * a0);
   // Each wavefront runs in exactly one of the two instantiations (general / geometric A).
   if (wave_geometric(geo_lane) != GEO) return;
+  for (int n = 0; n < N; ++n) sHf[n][lane] = Cf[(cbase * N + n) * D + d];
   constexpr bool geo = GEO;
   const float a20 = a0 * kLog2e;
   const float bias = dt_bias ? dt_bias[d] : 0.0f;
