@@ -15,16 +15,15 @@ constexpr int64_t kLanes = 64;
 // Wavefronts the chunking aims to give the summary and output kernels (four per
 // SIMD on a 256-CU part).
 constexpr int64_t kTargetWaves = 4096;
-// Longest block the single-kernel block path handles (no workspace).
-constexpr int64_t kBlockSingleMax = 64;
 
 struct Plan {
   int64_t batch, seqlen, d_inner, d_state;
   int64_t chunk;   // tokens per chunk (multiple of kSub)
   int64_t nchunk;  // chunks per sequence
   int64_t nsub;    // sub-chunks per full chunk (chunk / kSub)
+  int64_t ntile;   // kSub-token tiles per sequence (chunks start on tile boundaries)
   // workspace offsets in bytes (each 256-byte aligned)
-  size_t off_sf, off_sr, off_p, off_cf, off_cr, off_r, off_sig, off_a2t, total;
+  size_t off_sf, off_sr, off_p, off_cf, off_cr, off_r, off_sig, off_a2t, off_bct, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -44,6 +43,7 @@ inline Plan make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_
   p.chunk = chunk;
   p.nchunk = (seqlen + chunk - 1) / chunk;
   p.nsub = chunk / kSub;
+  p.ntile = (seqlen + kSub - 1) / kSub;
   const size_t state = static_cast<size_t>(batch) * p.nchunk * d_state * d_inner * sizeof(float);
   const size_t bound = static_cast<size_t>(batch) * p.nchunk * p.nsub * d_state * d_inner * sizeof(float);
   const size_t sig = static_cast<size_t>(batch) * p.nchunk * p.nsub * d_inner * sizeof(float);
@@ -56,6 +56,8 @@ inline Plan make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_
   p.off_r = off;  off = align256(off + bound);
   p.off_sig = off; off = align256(off + sig);
   p.off_a2t = off; off = align256(off + static_cast<size_t>(d_state) * d_inner * sizeof(float));
+  // B and C in fp32, per tile and state: kSub values of B then kSub of C
+  p.off_bct = off; off = align256(off + static_cast<size_t>(batch) * p.ntile * d_state * 2 * kSub * sizeof(float));
   p.total = off;
   return p;
 }

@@ -8,6 +8,14 @@
 // Work decomposition (one lane = one channel d; one wavefront = 64 channels
 // of one chunk of one sequence; a chunk is walked in tiles of kSub tokens that
 // sit in registers):
+//   k_stage_bc copies B and C into an fp32 table laid out per tile and state
+//              (kSub values of B, then kSub of C; zero past the sequence end).
+//              B and C do not depend on the channel: the output pass and the
+//              general-A summary read them with wave-uniform scalar loads into
+//              SGPRs, which VALU instructions take as operands, so they hold
+//              no vector registers (the saving buys a wavefront per SIMD).  The
+//              geometric-A summary, whose state step is too short to hide a
+//              scalar load's wait, copies each tile's B rows into LDS instead.
 //   k_summary  walks each chunk's tiles right to left.  Per state n and tile it
 //              forms abar and delta*x*B once per token, runs the tile-local
 //              forward recurrence from zero (composed into the chunk's forward
@@ -102,78 +110,94 @@ __device__ __forceinline__ void load_col_raw(__amdgpu_buffer_rsrc_t r, uint32_t 
   for (int k = 0; k < SUB; ++k) v[k] = IO<T>::load(r, voff, static_cast<uint32_t>(min(k, nvalid - 1)) * row_bytes);
 }
 
-// Stage a [SUB x N] tile of a token-major [*, N] matrix (base = first row) into
-// LDS as fp32 [NM][SUB], state-major; missing tokens and states >= N become 0.
-template <typename T, int NM, int SUB>
-__device__ __forceinline__ void stage_bc(const T* __restrict__ base, int N, int nvalid, float (*dst)[SUB], int lane) {
-  constexpr int PER = (NM * SUB + 63) / 64;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, static_cast<size_t>(nvalid) * N * IO<T>::kBytes);
-  float v[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = i * 64 + lane;
-    const int k = e / NM;
-    const int n = e - k * NM;
-    v[i] = IO<T>::load(r, static_cast<uint32_t>(min(k, nvalid - 1) * N + min(n, N - 1)) * IO<T>::kBytes, 0);
+// Loads through a constant-address-space pointer with a wave-uniform address
+// become scalar loads into SGPRs.  Only for memory no kernel in flight writes.
+typedef const float __attribute__((address_space(4))) sfloat;
+
+__device__ __forceinline__ const sfloat* scalar_ptr(const float* p) { return (const sfloat*)p; }
+
+template <typename T>
+__device__ __forceinline__ float ld_f32(const T* p);
+template <>
+__device__ __forceinline__ float ld_f32<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float ld_f32<bf16_t>(const bf16_t* p) { return to_f32(*p); }
+
+// ---------------------------------------------------------------------------
+// k_stage_bc: one thread per (batch, tile, state, token of the tile).
+// bct[((b * ntile + g) * N + n) * 2 * kSub + {k, kSub + k}] = {B, C}[b, g * kSub + k, n].
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_stage_bc(const T* __restrict__ Bm, const T* __restrict__ Cm,
+                                                  float* __restrict__ bct, int L, int N, int ntile, size_t total) {
+  constexpr int SUB = static_cast<int>(kSub);
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int k = static_cast<int>(idx % SUB);
+  const size_t rest = idx / SUB;
+  const int n = static_cast<int>(rest % N);
+  const size_t bg = rest / N;  // b * ntile + g
+  const int g = static_cast<int>(bg % ntile);
+  const size_t b = bg / ntile;
+  const int t = g * SUB + k;
+  float bv = 0.0f, cv = 0.0f;
+  if (t < L) {
+    const size_t src = (b * L + t) * N + n;
+    bv = ld_f32(Bm + src);
+    cv = ld_f32(Cm + src);
   }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = i * 64 + lane;
-    const int k = e / NM;
-    const int n = e - k * NM;
-    if (e < NM * SUB) dst[n][k] = (k < nvalid && n < N) ? v[i] : 0.0f;
-  }
+  float* dst = bct + rest * 2 * SUB;
+  dst[k] = bv;
+  dst[SUB + k] = cv;
 }
 
 // Whether every lane's A row is geometric: A[d,n] == (n+1) * A[d,0] exactly.
 __device__ __forceinline__ bool wave_geometric(bool lane_geo) { return __all(lane_geo ? 1 : 0) != 0; }
 
 // ---------------------------------------------------------------------------
-// k_summary tile body: all states of one tile, right to left across tiles.
+// k_summary state loop: all states of one tile, right to left across tiles.
 // f is the tile-local forward state from zero; S accumulates it decayed to the
-// chunk end; r is the running reverse state.  GEO: w[k] = exp(delta_k A[d,0])
-// and abar is its power; otherwise w[k] = delta_k.
+// chunk end; r is the running reverse state.
+//   GEO:  w[k] = exp(delta_k A[d,0]) and abar is its power; B comes from LDS
+//         (sB, one row of kSub tokens per state): the state step is short, and
+//         the wait of a per-state scalar load would not be hidden.
+//   else: w[k] = delta_k and abar = exp2(delta_k A[d,n] log2 e); B comes from
+//         the scalar table (bt), which keeps LDS at the two per-lane state
+//         arrays; A[d,n] is read one state ahead.
 // ---------------------------------------------------------------------------
 template <int SUB, bool GEO>
 __device__ __forceinline__ void summary_tile_states(int N, int lane, const float (&w)[SUB], const float (&u)[SUB],
                                                     float sigma, float a20, float (*sB)[SUB],
-                                                    const float* __restrict__ Arow, float (*sR)[64],
-                                                    float (*sS)[64], float* __restrict__ Rdst, uint32_t r_stride,
-                                                    bool store_r) {
+                                                    const float* __restrict__ bt, const float* __restrict__ Arow,
+                                                    float (*sR)[64], float (*sS)[64], float* __restrict__ Rdst,
+                                                    uint32_t r_stride, bool store_r) {
   float a[SUB];
-  float q = 1.0f, qstep = 1.0f;
-  float a2n = 0.0f;
-  if (GEO) {
 #pragma unroll
-    for (int k = 0; k < SUB; ++k) a[k] = 1.0f;
-    qstep = fast_exp2(a20 * sigma);
-  } else {
-    a2n = Arow[0] * kLog2e;
-  }
+  for (int k = 0; k < SUB; ++k) a[k] = 1.0f;
+  float q = 1.0f;
+  const float qstep = GEO ? fast_exp2(a20 * sigma) : 1.0f;
+  float a2n = GEO ? 0.0f : Arow[0] * kLog2e;
 #pragma unroll 1
   for (int n = 0; n < N; ++n) {
     const float a2 = a2n;
     if (!GEO) a2n = Arow[min(n + 1, N - 1)] * kLog2e;  // one state ahead
+    const sfloat* bn = scalar_ptr(bt + static_cast<size_t>(n) * 2 * SUB);
     float bb[SUB];
 #pragma unroll
     for (int k = 0; k < SUB; ++k) {
       a[k] = GEO ? a[k] * w[k] : fast_exp2(w[k] * a2);
-      bb[k] = u[k] * sB[n][k];
+      bb[k] = u[k] * (GEO ? sB[n][k] : bn[k]);
     }
     // the forward (ascending) and reverse (descending) chains are independent:
     // interleaving them doubles the instruction-level parallelism
     float f = 0.0f;
     float r = sR[n][lane];
 #pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-      f = fmaf(a[s], f, bb[s]);
-      r = fmaf(a[SUB - 1 - s], r, bb[SUB - 1 - s]);
+    for (int t = 0; t < SUB; ++t) {
+      f = fmaf(a[t], f, bb[t]);
+      r = fmaf(a[SUB - 1 - t], r, bb[SUB - 1 - t]);
     }
-    if (GEO) {
-      q *= qstep;
-    } else {
-      q = fast_exp2(a2 * sigma);
-    }
+    q = GEO ? q * qstep : fast_exp2(a2 * sigma);
     sS[n][lane] = fmaf(q, f, sS[n][lane]);
     sR[n][lane] = r;
     if (store_r) Rdst[static_cast<size_t>(n) * r_stride] = r;
@@ -185,15 +209,16 @@ __device__ __forceinline__ void summary_tile_states(int N, int lane, const float
 // ---------------------------------------------------------------------------
 template <typename T, int NM, bool GEO>
 __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T* __restrict__ dt,
-                                                const float* __restrict__ A, const T* __restrict__ Bm,
+                                                const float* __restrict__ A, const float* __restrict__ bct,
                                                 const float* __restrict__ dt_bias, int L, int D, int N, int chunk,
-                                                int nchunk, int nsub, float* __restrict__ Sf,
+                                                int nchunk, int nsub, int ntile, float* __restrict__ Sf,
                                                 float* __restrict__ Sr, float* __restrict__ P,
                                                 float* __restrict__ R, float* __restrict__ SIG) {
   constexpr int SUB = static_cast<int>(kSub);
-  __shared__ float sB[NM][SUB];
+  static_assert(NM * SUB <= 64 * 4, "one float4 of B per lane");
   __shared__ float sR[NM][64];
   __shared__ float sS[NM][64];
+  __shared__ __align__(16) float sB[GEO ? NM : 1][SUB];  // this tile's B, one row per state (GEO)
   const int lane = threadIdx.x;
   const int d = blockIdx.x * 64 + lane;
   const int c = blockIdx.y;
@@ -228,8 +253,15 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
     float xr[SUB], dr[SUB];
     load_col_raw<T, SUB>(make_rsrc(x + tile, tile_bytes), voff, row_bytes, nvalid, xr);
     load_col_raw<T, SUB>(make_rsrc(dt + tile, tile_bytes), voff, row_bytes, nvalid, dr);
-    __syncthreads();  // the previous tile's reads of sB are done
-    stage_bc<T, NM, SUB>(Bm + (row + ts) * N, N, nvalid, sB, lane);
+    const float* bt = bct + (static_cast<size_t>(b) * ntile + static_cast<size_t>(c) * nsub + j) * N * 2 * SUB;
+    if (GEO) {
+      // copy the tile's B rows (fp32, from the staged table) into LDS: lane = (state, quarter row).
+      // One wavefront per workgroup: its LDS accesses are performed in program order.
+      const int n = min(lane / (SUB / 4), N - 1);
+      const int part = lane % (SUB / 4);
+      const float4 v = *reinterpret_cast<const float4*>(bt + static_cast<size_t>(n) * 2 * SUB + part * 4);
+      if (lane < NM * (SUB / 4)) *reinterpret_cast<float4*>(&sB[GEO ? lane / (SUB / 4) : 0][part * 4]) = v;
+    }
     float dl[SUB], u[SUB];
     float tile_sum = 0.0f;
 #pragma unroll
@@ -238,16 +270,15 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
       u[k] = dl[k] * xr[k];
       tile_sum += dl[k];
     }
-    __syncthreads();
     const size_t jb = cbase * nsub + (j - 1);
     float* Rdst = R + jb * N * D + d;
     if (GEO) {
       float w[SUB];
 #pragma unroll
       for (int k = 0; k < SUB; ++k) w[k] = fast_exp2(dl[k] * a20);
-      summary_tile_states<SUB, true>(N, lane, w, u, sigma, a20, sB, Arow, sR, sS, Rdst, D, j > 0);
+      summary_tile_states<SUB, true>(N, lane, w, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, j > 0);
     } else {
-      summary_tile_states<SUB, false>(N, lane, dl, u, sigma, a20, sB, Arow, sR, sS, Rdst, D, j > 0);
+      summary_tile_states<SUB, false>(N, lane, dl, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, j > 0);
     }
     sigma += tile_sum;
     if (j > 0) SIG[jb * D + d] = sigma;
@@ -292,48 +323,68 @@ __global__ __launch_bounds__(256) void k_carry(const float* __restrict__ Sf, con
 }
 
 // ---------------------------------------------------------------------------
-// k_output tile body: all states of one tile.  GEO: w[k] = exp(delta_k A[d,0])
+// k_output state loop: all states of one tile.  GEO: w[k] = exp(delta_k A[d,0])
 // and abar is its power; otherwise w[k] = delta_k.
 // DIRS: bit 0 = forward readout, bit 1 = reverse readout.
+//
+// The reverse state entering the tile from the right is formed per state from
+// the zero-started boundary state Rj[n] (summary pass) and the chunk's carry
+// Cr[n]: hr = Rj[n] + exp(A[d,n] sigma_j) Cr[n], sigma_j being the sum of delta
+// from the tile's right edge to the chunk end (on the chunk's last tile, hr =
+// Cr[n]).  Rj and Cr are read with vector loads one state ahead; vector loads
+// complete in order, so only the older of the two in flight is waited for.
 // ---------------------------------------------------------------------------
-// A2T points at this lane's column of the transposed table A[d,n] * log2(e), [N][D].
 template <int SUB, int DIRS, bool GEO>
 __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const float (&w)[SUB],
-                                                   const float (&u)[SUB], float (&y)[SUB], float (*sB)[SUB],
-                                                   float (*sC)[SUB], const float* __restrict__ A2T,
-                                                   float (*sHf)[64], float (*sHr)[64]) {
+                                                   const float (&u)[SUB], float (&y)[SUB],
+                                                   const float* __restrict__ bt, float (*sA2)[64],
+                                                   float (*sHf)[64], __amdgpu_buffer_rsrc_t rj_rsrc,
+                                                   __amdgpu_buffer_rsrc_t cr_rsrc, float qstep, float sj,
+                                                   bool last) {
+  constexpr bool kRev = (DIRS & 2) != 0;
+  const uint32_t voff4 = static_cast<uint32_t>(lane) * 4u;
+  const uint32_t nstride4 = static_cast<uint32_t>(D) * 4u;
   float a[SUB];
-  float a2n = 0.0f;
-  if (GEO) {
 #pragma unroll
-    for (int k = 0; k < SUB; ++k) a[k] = 1.0f;
-  } else {
-    a2n = A2T[0];
+  for (int k = 0; k < SUB; ++k) a[k] = 1.0f;
+  float q = 1.0f;
+  float rj_next = 0.0f, cr_next = 0.0f;
+  if (kRev) {
+    rj_next = IO<float>::load(rj_rsrc, voff4, 0);
+    cr_next = IO<float>::load(cr_rsrc, voff4, 0);
   }
 #pragma unroll 1
   for (int n = 0; n < N; ++n) {
-    const float a2 = a2n;
-    if (!GEO) a2n = A2T[static_cast<size_t>(min(n + 1, N - 1)) * D];  // one state ahead
+    const sfloat* bn = scalar_ptr(bt + static_cast<size_t>(n) * 2 * SUB);
+    const float a2 = GEO ? 0.0f : sA2[n][lane];
+    float hf = sHf[n][lane];
+    float rj = 0.0f, cr = 0.0f;
+    if (kRev) {
+      rj = rj_next;
+      cr = cr_next;
+      const uint32_t s1 = static_cast<uint32_t>(min(n + 1, N - 1)) * nstride4;
+      rj_next = IO<float>::load(rj_rsrc, voff4, s1);
+      cr_next = IO<float>::load(cr_rsrc, voff4, s1);
+    }
     float bb[SUB];
 #pragma unroll
     for (int k = 0; k < SUB; ++k) {
       a[k] = GEO ? a[k] * w[k] : fast_exp2(w[k] * a2);
-      bb[k] = u[k] * sB[n][k];
+      bb[k] = u[k] * bn[k];
     }
-    // keep the C reads below this point: B and C values are then never live together
-    __builtin_amdgcn_sched_barrier(0);
-    float hf = sHf[n][lane];
 #pragma unroll
     for (int k = 0; k < SUB; ++k) {
       hf = fmaf(a[k], hf, bb[k]);
-      if (DIRS & 1) y[k] = fmaf(sC[n][k], hf, y[k]);
+      if (DIRS & 1) y[k] = fmaf(bn[SUB + k], hf, y[k]);
     }
-    if (DIRS & 2) {
-      float hr = sHr[n][lane];
+    if (kRev) {
+      q = GEO ? q * qstep : fast_exp2(a2 * sj);
+      // the last tile's boundary slot is never written: its value is discarded here
+      float hr = last ? cr : fmaf(q, cr, rj);
 #pragma unroll
       for (int k = SUB - 1; k >= 0; --k) {
         hr = fmaf(a[k], hr, bb[k]);
-        y[k] = fmaf(sC[n][k], hr, y[k]);
+        y[k] = fmaf(bn[SUB + k], hr, y[k]);
       }
     }
     sHf[n][lane] = hf;
@@ -346,21 +397,19 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
 template <typename T, int NM, int DIRS, bool GEO>
 __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T* __restrict__ dt,
                                                const T* __restrict__ z, const float* __restrict__ A,
-                                               const T* __restrict__ Bm, const T* __restrict__ Cm,
-                                               const float* __restrict__ Dv, const float* __restrict__ dt_bias,
-                                               T* __restrict__ out, int L, int D, int N, int chunk, int nchunk,
-                                               int nsub, int gate, const float* __restrict__ Cf,
-                                               const float* __restrict__ Cr, const float* __restrict__ R,
-                                               const float* __restrict__ SIG, const float* __restrict__ A2T,
-                                               float* __restrict__ h_out) {
+                                               const float* __restrict__ bct, const float* __restrict__ Dv,
+                                               const float* __restrict__ dt_bias, T* __restrict__ out, int L, int D,
+                                               int N, int chunk, int nchunk, int nsub, int ntile, int gate,
+                                               const float* __restrict__ Cf, const float* __restrict__ Cr,
+                                               const float* __restrict__ R, const float* __restrict__ SIG,
+                                               const float* __restrict__ A2T, float* __restrict__ h_out) {
   constexpr int SUB = static_cast<int>(kSub);
-  __shared__ float sB[NM][SUB];
-  __shared__ float sC[NM][SUB];
-  // per-lane state, indexed by a runtime state index
+  // per-lane forward state and A[d,n] log2(e) (general A), indexed by a runtime state index
   __shared__ float sHf[NM][64];
-  __shared__ float sHr[NM][64];
+  __shared__ float sA2[GEO ? 1 : NM][64];
   const int lane = threadIdx.x;
   const int d = blockIdx.x * 64 + lane;
+  const size_t col0 = static_cast<size_t>(blockIdx.x) * 64;
   const int c = blockIdx.y;
   const int b = blockIdx.z;
   const int t0 = c * chunk;
@@ -374,16 +423,18 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
   for (int n = 0; n < N; ++n) geo_lane = geo_lane && (Arow[n] == static_cast<float>(n + 1) * a0);
   // Each wavefront runs in exactly one of the two instantiations (general / geometric A).
   if (wave_geometric(geo_lane) != GEO) return;
-  for (int n = 0; n < N; ++n) sHf[n][lane] = Cf[(cbase * N + n) * D + d];
-  constexpr bool geo = GEO;
+  for (int n = 0; n < N; ++n) {
+    sHf[n][lane] = Cf[(cbase * N + n) * D + d];
+    if (!GEO) sA2[GEO ? 0 : n][lane] = A2T[static_cast<size_t>(n) * D + d];
+  }
   const float a20 = a0 * kLog2e;
   const float bias = dt_bias ? dt_bias[d] : 0.0f;
   constexpr float ndir = (DIRS == 3) ? 2.0f : 1.0f;
   const float skip = Dv ? ndir * Dv[d] : 0.0f;
   const uint32_t voff = static_cast<uint32_t>(lane) * IO<T>::kBytes;
   const uint32_t row_bytes = static_cast<uint32_t>(D) * IO<T>::kBytes;
-  const uint32_t voff4 = static_cast<uint32_t>(lane) * 4u;
-  const uint32_t nstride4 = static_cast<uint32_t>(D) * 4u;
+  const size_t state_bytes = static_cast<size_t>(N) * D * 4;
+  const __amdgpu_buffer_rsrc_t cr_rsrc = make_rsrc(Cr + cbase * N * D + col0, state_bytes);
 
   const int nsub_c = (te - t0 + SUB - 1) / SUB;
   for (int j = 0; j < nsub_c; ++j) {
@@ -391,32 +442,14 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
     const int nvalid = min(SUB, te - ts);
     const bool last = (j == nsub_c - 1);
     const size_t jb = cbase * nsub + j;
-    const size_t tile = (row + ts) * D + static_cast<size_t>(blockIdx.x) * 64;
+    const size_t tile = (row + ts) * D + col0;
     const size_t tile_bytes = static_cast<size_t>(nvalid) * row_bytes;
-    // every load of the tile is issued before any of it is used
-    float xr[SUB], dr[SUB], rj[NM], cr[NM], a2t[NM];
+    float xr[SUB], dr[SUB];
     load_col_raw<T, SUB>(make_rsrc(x + tile, tile_bytes), voff, row_bytes, nvalid, xr);
     load_col_raw<T, SUB>(make_rsrc(dt + tile, tile_bytes), voff, row_bytes, nvalid, dr);
-    // the boundary slot of a chunk's last tile is allocated but never written: load and discard
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(R + jb * N * D + static_cast<size_t>(blockIdx.x) * 64,
-                                                static_cast<size_t>(N) * D * 4);
-#pragma unroll
-    for (int n = 0; n < NM; ++n) rj[n] = IO<float>::load(rr, voff4, static_cast<uint32_t>(min(n, N - 1)) * nstride4);
-#pragma unroll
-    for (int n = 0; n < NM; ++n) rj[n] = (!last && n < N) ? rj[n] : 0.0f;
-    if (DIRS & 2) {
-#pragma unroll
-      for (int n = 0; n < NM; ++n) cr[n] = Cr[(cbase * N + min(n, N - 1)) * D + d];
-      if (!geo) {
-#pragma unroll
-        for (int n = 0; n < NM; ++n) a2t[n] = A2T[static_cast<size_t>(min(n, N - 1)) * D + d];
-      }
-    }
-    const float sj0 = SIG[jb * D + d];
-    const float sj = last ? 0.0f : sj0;
-    __syncthreads();  // the previous tile's reads of sB / sC / sHr are done
-    stage_bc<T, NM, SUB>(Bm + (row + ts) * N, N, nvalid, sB, lane);
-    stage_bc<T, NM, SUB>(Cm + (row + ts) * N, N, nvalid, sC, lane);
+    const float sj = last ? 0.0f : SIG[jb * D + d];
+    const float* bt = bct + (static_cast<size_t>(b) * ntile + static_cast<size_t>(c) * nsub + j) * N * 2 * SUB;
+    const __amdgpu_buffer_rsrc_t rj_rsrc = make_rsrc(R + jb * N * D + col0, state_bytes);
     float dl[SUB], u[SUB], y[SUB];
 #pragma unroll
     for (int k = 0; k < SUB; ++k) {
@@ -424,30 +457,15 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
       u[k] = dl[k] * xr[k];
       y[k] = skip * xr[k];
     }
-    if (DIRS & 2) {
-      // exact reverse state entering this tile from the right
-      if (geo) {
-        const float qstep = fast_exp2(a20 * sj);
-        float q = 1.0f;
-#pragma unroll
-        for (int n = 0; n < NM; ++n) {
-          q *= qstep;
-          if (n < N) sHr[n][lane] = fmaf(q, cr[n], rj[n]);
-        }
-      } else {
-#pragma unroll
-        for (int n = 0; n < NM; ++n)
-          if (n < N) sHr[n][lane] = fmaf(fast_exp2(a2t[n] * sj), cr[n], rj[n]);
-      }
-    }
-    __syncthreads();
-    if (geo) {
+    if (GEO) {
       float w[SUB];
 #pragma unroll
       for (int k = 0; k < SUB; ++k) w[k] = fast_exp2(dl[k] * a20);
-      output_tile_states<SUB, DIRS, true>(N, D, lane, w, u, y, sB, sC, A2T + d, sHf, sHr);
+      output_tile_states<SUB, DIRS, true>(N, D, lane, w, u, y, bt, sA2, sHf, rj_rsrc, cr_rsrc,
+                                          fast_exp2(a20 * sj), sj, last);
     } else {
-      output_tile_states<SUB, DIRS, false>(N, D, lane, dl, u, y, sB, sC, A2T + d, sHf, sHr);
+      output_tile_states<SUB, DIRS, false>(N, D, lane, dl, u, y, bt, sA2, sHf, rj_rsrc, cr_rsrc, 1.0f, sj,
+                                           last);
     }
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + tile, tile_bytes);
     if (gate) {
@@ -472,13 +490,13 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
 // ---------------------------------------------------------------------------
 template <typename T, int NM, int DIRS>
 static void launch_output(dim3 grid, hipStream_t stream, const T* x, const T* dt, const T* z, const ScanArgs& a,
-                          const T* Bm, const T* Cm, T* out, int L, int D, int N, int chunk, int nchunk, int nsub,
+                          const float* bct, T* out, int L, int D, int N, int chunk, int nchunk, int nsub, int ntile,
                           int gate, const float* Cf, const float* Cr, const float* R, const float* SIG,
                           const float* A2T) {
-  hipLaunchKernelGGL((k_output<T, NM, DIRS, true>), grid, dim3(64), 0, stream, x, dt, z, a.A, Bm, Cm, a.D,
-                     a.dt_bias, out, L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R, SIG, A2T, a.h_out);
-  hipLaunchKernelGGL((k_output<T, NM, DIRS, false>), grid, dim3(64), 0, stream, x, dt, z, a.A, Bm, Cm, a.D,
-                     a.dt_bias, out, L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R, SIG, A2T, a.h_out);
+  hipLaunchKernelGGL((k_output<T, NM, DIRS, true>), grid, dim3(64), 0, stream, x, dt, z, a.A, bct, a.D, a.dt_bias,
+                     out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf, Cr, R, SIG, A2T, a.h_out);
+  hipLaunchKernelGGL((k_output<T, NM, DIRS, false>), grid, dim3(64), 0, stream, x, dt, z, a.A, bct, a.D, a.dt_bias,
+                     out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf, Cr, R, SIG, A2T, a.h_out);
 }
 
 template <typename T, int NM>
@@ -492,6 +510,8 @@ static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipSt
   float* R = reinterpret_cast<float*>(w + p.off_r);
   float* SIG = reinterpret_cast<float*>(w + p.off_sig);
   float* A2T = reinterpret_cast<float*>(w + p.off_a2t);
+  float* bct = reinterpret_cast<float*>(w + p.off_bct);
+  const int ntile = static_cast<int>(p.ntile);
   const int L = static_cast<int>(p.seqlen), D = static_cast<int>(p.d_inner), N = static_cast<int>(p.d_state);
   const int chunk = static_cast<int>(p.chunk), nchunk = static_cast<int>(p.nchunk), nsub = static_cast<int>(p.nsub);
   const dim3 grid(static_cast<unsigned>(D / 64), static_cast<unsigned>(nchunk), static_cast<unsigned>(p.batch));
@@ -506,10 +526,13 @@ static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipSt
   // Both A-path instantiations are launched; every wavefront exits from the one
   // that does not match its channels' A rows.
   if (stage < 0 || stage == 0) {
-    hipLaunchKernelGGL((k_summary<T, NM, true>), grid, dim3(64), 0, stream, x, dt, a.A, Bm, a.dt_bias, L, D, N,
-                       chunk, nchunk, nsub, Sf, Sr, P, R, SIG);
-    hipLaunchKernelGGL((k_summary<T, NM, false>), grid, dim3(64), 0, stream, x, dt, a.A, Bm, a.dt_bias, L, D, N,
-                       chunk, nchunk, nsub, Sf, Sr, P, R, SIG);
+    const size_t nbc = static_cast<size_t>(p.batch) * ntile * N * kSub;
+    hipLaunchKernelGGL((k_stage_bc<T>), dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0, stream, Bm, Cm,
+                       bct, L, N, ntile, nbc);
+    hipLaunchKernelGGL((k_summary<T, NM, true>), grid, dim3(64), 0, stream, x, dt, a.A, bct, a.dt_bias, L, D, N,
+                       chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG);
+    hipLaunchKernelGGL((k_summary<T, NM, false>), grid, dim3(64), 0, stream, x, dt, a.A, bct, a.dt_bias, L, D, N,
+                       chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG);
     e = hipGetLastError();
     if (e != hipSuccess || stage == 0) return e;
   }
@@ -524,14 +547,14 @@ static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipSt
 
   const int gate = (a.flags & kNoGate) ? 0 : 1;
   if (a.flags & kFwdOnly) {
-    launch_output<T, NM, 1>(grid, stream, x, dt, z, a, Bm, Cm, out, L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R,
-                            SIG, A2T);
+    launch_output<T, NM, 1>(grid, stream, x, dt, z, a, bct, out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf,
+                            Cr, R, SIG, A2T);
   } else if (a.flags & kRevOnly) {
-    launch_output<T, NM, 2>(grid, stream, x, dt, z, a, Bm, Cm, out, L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R,
-                            SIG, A2T);
+    launch_output<T, NM, 2>(grid, stream, x, dt, z, a, bct, out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf,
+                            Cr, R, SIG, A2T);
   } else {
-    launch_output<T, NM, 3>(grid, stream, x, dt, z, a, Bm, Cm, out, L, D, N, chunk, nchunk, nsub, gate, Cf, Cr, R,
-                            SIG, A2T);
+    launch_output<T, NM, 3>(grid, stream, x, dt, z, a, bct, out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf,
+                            Cr, R, SIG, A2T);
   }
   return hipGetLastError();
 }
