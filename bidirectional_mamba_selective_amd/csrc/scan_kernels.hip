@@ -89,25 +89,44 @@ struct IO<bf16_t> {
   }
 };
 
-// v[k] = tile row k (k < nvalid) of this lane's channel; rows past nvalid are
-// zero.  Row offsets are clamped so that every load is in bounds and none is
-// guarded by a branch: all of them are in flight together.
-template <typename T, int SUB>
-__device__ __forceinline__ void load_col(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t row_bytes, int nvalid,
-                                         float (&v)[SUB]) {
-#pragma unroll
-  for (int k = 0; k < SUB; ++k) v[k] = IO<T>::load(r, voff, static_cast<uint32_t>(min(k, nvalid - 1)) * row_bytes);
-#pragma unroll
-  for (int k = 0; k < SUB; ++k) v[k] = k < nvalid ? v[k] : 0.0f;
-}
-
-// As load_col, but rows past nvalid repeat the last valid row (for values whose
-// surplus rows are never used).
+// v[k] = tile row k of this lane's channel; rows past nvalid repeat the last
+// valid row (their values are never used).  Row offsets are clamped so that
+// every load is in bounds and none is guarded by a branch: all of them are in
+// flight together.
 template <typename T, int SUB>
 __device__ __forceinline__ void load_col_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t row_bytes, int nvalid,
                                              float (&v)[SUB]) {
 #pragma unroll
   for (int k = 0; k < SUB; ++k) v[k] = IO<T>::load(r, voff, static_cast<uint32_t>(min(k, nvalid - 1)) * row_bytes);
+}
+
+// delta = softplus(dt + dt_bias) for a tile's tokens; tokens past nvalid get
+// delta = 0 (abar = 1 and no input: they leave the states unchanged).  Full
+// tiles take a path without the per-token test, which the compiler would turn
+// into a branch around each softplus.
+template <int SUB>
+__device__ __forceinline__ void tile_delta(const float (&dr)[SUB], float bias, int nvalid, float (&dl)[SUB]) {
+  if (nvalid == SUB) {
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) dl[k] = softplus_f32(dr[k] + bias);
+  } else {
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) dl[k] = k < nvalid ? softplus_f32(dr[k] + bias) : 0.0f;
+  }
+}
+
+// Store rows k < nvalid of a tile column (full tiles without per-row tests).
+template <typename T, int SUB>
+__device__ __forceinline__ void store_col(const float (&v)[SUB], __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                          uint32_t row_bytes, int nvalid) {
+  if (nvalid == SUB) {
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) IO<T>::store(v[k], r, voff, static_cast<uint32_t>(k) * row_bytes);
+  } else {
+#pragma unroll
+    for (int k = 0; k < SUB; ++k)
+      if (k < nvalid) IO<T>::store(v[k], r, voff, static_cast<uint32_t>(k) * row_bytes);
+  }
 }
 
 // Loads through a constant-address-space pointer with a wave-uniform address
@@ -263,10 +282,10 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
       if (lane < NM * (SUB / 4)) *reinterpret_cast<float4*>(&sB[GEO ? lane / (SUB / 4) : 0][part * 4]) = v;
     }
     float dl[SUB], u[SUB];
+    tile_delta<SUB>(dr, bias, nvalid, dl);
     float tile_sum = 0.0f;
 #pragma unroll
     for (int k = 0; k < SUB; ++k) {
-      dl[k] = k < nvalid ? softplus_f32(dr[k] + bias) : 0.0f;
       u[k] = dl[k] * xr[k];
       tile_sum += dl[k];
     }
@@ -293,6 +312,9 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
 
 // ---------------------------------------------------------------------------
 // k_carry: one thread per (b, n, d); sequential over chunks in both directions.
+// The two directions run in one loop (two independent chains), and the inputs
+// of kBatch chunks are loaded before they are composed, so the loop pays one
+// memory latency per batch rather than one per chunk.
 // ---------------------------------------------------------------------------
 // The batch-0 threads also write the transposed table A2T[n][d] = A[d,n] * log2(e)
 // that the output pass reads with coalesced loads.
@@ -301,6 +323,7 @@ __global__ __launch_bounds__(256) void k_carry(const float* __restrict__ Sf, con
                                                float* __restrict__ Cr, const float* __restrict__ h_in,
                                                const float* __restrict__ A, float* __restrict__ A2T, int batch,
                                                int nchunk, int N, int D) {
+  constexpr int kBatch = 8;
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const size_t total = static_cast<size_t>(batch) * N * D;
   if (idx >= total) return;
@@ -308,18 +331,70 @@ __global__ __launch_bounds__(256) void k_carry(const float* __restrict__ Sf, con
   const int n = static_cast<int>((idx / D) % N);
   const int b = static_cast<int>(idx / (static_cast<size_t>(D) * N));
   if (b == 0) A2T[static_cast<size_t>(n) * D + d] = A[static_cast<size_t>(d) * N + n] * kLog2e;
+  const size_t base = (static_cast<size_t>(b) * nchunk * N + n) * D + d;  // chunk 0
+  const size_t stride = static_cast<size_t>(N) * D;                       // per chunk
   float cf = h_in ? h_in[(static_cast<size_t>(b) * D + d) * N + n] : 0.0f;
-  for (int c = 0; c < nchunk; ++c) {
-    const size_t o = ((static_cast<size_t>(b) * nchunk + c) * N + n) * D + d;
-    Cf[o] = cf;
-    cf = fmaf(P[o], cf, Sf[o]);
-  }
   float cr = 0.0f;
-  for (int c = nchunk - 1; c >= 0; --c) {
-    const size_t o = ((static_cast<size_t>(b) * nchunk + c) * N + n) * D + d;
-    Cr[o] = cr;
-    cr = fmaf(P[o], cr, Sr[o]);
+  for (int c0 = 0; c0 < nchunk; c0 += kBatch) {
+    float pf[kBatch], sf[kBatch], pr[kBatch], sr[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const size_t of = base + static_cast<size_t>(min(c0 + i, nchunk - 1)) * stride;            // forward: c0 + i
+      const size_t orr = base + static_cast<size_t>(max(nchunk - 1 - c0 - i, 0)) * stride;      // reverse
+      pf[i] = P[of];
+      sf[i] = Sf[of];
+      pr[i] = P[orr];
+      sr[i] = Sr[orr];
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (c0 + i < nchunk) {
+        Cf[base + static_cast<size_t>(c0 + i) * stride] = cf;
+        cf = fmaf(pf[i], cf, sf[i]);
+        Cr[base + static_cast<size_t>(nchunk - 1 - c0 - i) * stride] = cr;
+        cr = fmaf(pr[i], cr, sr[i]);
+      }
+    }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Explicit waits.  The tile buffers are filled by direct-to-LDS buffer loads,
+// whose completion the compiler does not track: the kernel waits for them
+// itself.  The memory clobber keeps the compiler from moving LDS accesses
+// across a wait.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lds_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Direct-to-LDS load of a [kSub x 64] tile of a token-major [*, D] tensor
+// (base = the tile's first row at this wavefront's first channel) into dst,
+// laid out [row][lane].  One instruction moves 16 bytes per lane, i.e. 1 KiB:
+// 8 rows of bf16 or 4 rows of fp32.  Rows past nvalid repeat the last valid
+// row (they are never used), so every read is in bounds.
+template <typename T>
+__device__ __forceinline__ void lds_load_tile(const T* base, int nvalid, uint32_t row_bytes, T (*dst)[64],
+                                              int lane) {
+  constexpr int kLanesPerRow = 64 * static_cast<int>(sizeof(T)) / 16;
+  constexpr int kRowsPerInst = 64 / kLanesPerRow;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, static_cast<size_t>(nvalid) * row_bytes);
+  const int rl = lane / kLanesPerRow;
+  const uint32_t cb = static_cast<uint32_t>(lane % kLanesPerRow) * 16u;
+#pragma unroll
+  for (int i = 0; i < static_cast<int>(kSub) / kRowsPerInst; ++i) {
+    const int row = min(i * kRowsPerInst + rl, nvalid - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)&dst[i * kRowsPerInst][0],
+                                             16, static_cast<uint32_t>(row) * row_bytes + cb, 0, 0, 0);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float lds_val(const T (*src)[64], int k, int lane);
+template <>
+__device__ __forceinline__ float lds_val<float>(const float (*src)[64], int k, int lane) { return src[k][lane]; }
+template <>
+__device__ __forceinline__ float lds_val<bf16_t>(const bf16_t (*src)[64], int k, int lane) {
+  return to_f32(src[k][lane]);
 }
 
 // ---------------------------------------------------------------------------
@@ -331,15 +406,15 @@ __global__ __launch_bounds__(256) void k_carry(const float* __restrict__ Sf, con
 // the zero-started boundary state Rj[n] (summary pass) and the chunk's carry
 // Cr[n]: hr = Rj[n] + exp(A[d,n] sigma_j) Cr[n], sigma_j being the sum of delta
 // from the tile's right edge to the chunk end (on the chunk's last tile, hr =
-// Cr[n]).  Rj and Cr are read with vector loads one state ahead; vector loads
-// complete in order, so only the older of the two in flight is waited for.
+// Cr[n]).  Rj, Cr and (general A) A[d,n] log2(e) are read with vector loads one
+// state ahead; vector loads complete in order, so only the oldest is waited for.
 // ---------------------------------------------------------------------------
 template <int SUB, int DIRS, bool GEO>
 __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const float (&w)[SUB],
                                                    const float (&u)[SUB], float (&y)[SUB],
-                                                   const float* __restrict__ bt, float (*sA2)[64],
-                                                   float (*sHf)[64], __amdgpu_buffer_rsrc_t rj_rsrc,
-                                                   __amdgpu_buffer_rsrc_t cr_rsrc, float qstep, float sj,
+                                                   const float* __restrict__ bt, float (*sHf)[64],
+                                                   __amdgpu_buffer_rsrc_t rj_rsrc, __amdgpu_buffer_rsrc_t cr_rsrc,
+                                                   __amdgpu_buffer_rsrc_t a2_rsrc, float qstep, float sj,
                                                    bool last) {
   constexpr bool kRev = (DIRS & 2) != 0;
   const uint32_t voff4 = static_cast<uint32_t>(lane) * 4u;
@@ -348,21 +423,26 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
 #pragma unroll
   for (int k = 0; k < SUB; ++k) a[k] = 1.0f;
   float q = 1.0f;
-  float rj_next = 0.0f, cr_next = 0.0f;
+  float rj_next = 0.0f, cr_next = 0.0f, a2_next = 0.0f;
   if (kRev) {
     rj_next = IO<float>::load(rj_rsrc, voff4, 0);
     cr_next = IO<float>::load(cr_rsrc, voff4, 0);
   }
+  if (!GEO) a2_next = IO<float>::load(a2_rsrc, voff4, 0);
 #pragma unroll 1
   for (int n = 0; n < N; ++n) {
     const sfloat* bn = scalar_ptr(bt + static_cast<size_t>(n) * 2 * SUB);
-    const float a2 = GEO ? 0.0f : sA2[n][lane];
+    const uint32_t s1 = static_cast<uint32_t>(min(n + 1, N - 1)) * nstride4;
+    float a2 = 0.0f;
+    if (!GEO) {
+      a2 = a2_next;
+      a2_next = IO<float>::load(a2_rsrc, voff4, s1);
+    }
     float hf = sHf[n][lane];
     float rj = 0.0f, cr = 0.0f;
     if (kRev) {
       rj = rj_next;
       cr = cr_next;
-      const uint32_t s1 = static_cast<uint32_t>(min(n + 1, N - 1)) * nstride4;
       rj_next = IO<float>::load(rj_rsrc, voff4, s1);
       cr_next = IO<float>::load(cr_rsrc, voff4, s1);
     }
@@ -392,7 +472,11 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
 }
 
 // ---------------------------------------------------------------------------
-// k_output: grid (d_inner / 64, nchunk, batch), block 64.
+// k_output: grid (d_inner / 64, nchunk, batch), block 64 (one wavefront).
+// x, dt and z tiles are brought into LDS one tile ahead with direct-to-LDS
+// loads, so the HBM stream of tile j+1 overlaps the state loop of tile j (all
+// wavefronts run the same loop in step; without this they would all wait for
+// memory at the same time and then all compute).
 // ---------------------------------------------------------------------------
 template <typename T, int NM, int DIRS, bool GEO>
 __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T* __restrict__ dt,
@@ -404,9 +488,10 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
                                                const float* __restrict__ R, const float* __restrict__ SIG,
                                                const float* __restrict__ A2T, float* __restrict__ h_out) {
   constexpr int SUB = static_cast<int>(kSub);
-  // per-lane forward state and A[d,n] log2(e) (general A), indexed by a runtime state index
-  __shared__ float sHf[NM][64];
-  __shared__ float sA2[GEO ? 1 : NM][64];
+  __shared__ float sHf[NM][64];  // per-lane forward state, indexed by a runtime state index
+  __shared__ __align__(16) T sX[SUB][64];
+  __shared__ __align__(16) T sDT[SUB][64];
+  __shared__ __align__(16) T sZ[SUB][64];
   const int lane = threadIdx.x;
   const int d = blockIdx.x * 64 + lane;
   const size_t col0 = static_cast<size_t>(blockIdx.x) * 64;
@@ -423,10 +508,7 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
   for (int n = 0; n < N; ++n) geo_lane = geo_lane && (Arow[n] == static_cast<float>(n + 1) * a0);
   // Each wavefront runs in exactly one of the two instantiations (general / geometric A).
   if (wave_geometric(geo_lane) != GEO) return;
-  for (int n = 0; n < N; ++n) {
-    sHf[n][lane] = Cf[(cbase * N + n) * D + d];
-    if (!GEO) sA2[GEO ? 0 : n][lane] = A2T[static_cast<size_t>(n) * D + d];
-  }
+  for (int n = 0; n < N; ++n) sHf[n][lane] = Cf[(cbase * N + n) * D + d];
   const float a20 = a0 * kLog2e;
   const float bias = dt_bias ? dt_bias[d] : 0.0f;
   constexpr float ndir = (DIRS == 3) ? 2.0f : 1.0f;
@@ -435,8 +517,16 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
   const uint32_t row_bytes = static_cast<uint32_t>(D) * IO<T>::kBytes;
   const size_t state_bytes = static_cast<size_t>(N) * D * 4;
   const __amdgpu_buffer_rsrc_t cr_rsrc = make_rsrc(Cr + cbase * N * D + col0, state_bytes);
+  const __amdgpu_buffer_rsrc_t a2_rsrc = make_rsrc(A2T + col0, state_bytes);
 
   const int nsub_c = (te - t0 + SUB - 1) / SUB;
+  {
+    const size_t tile = (row + t0) * D + col0;
+    const int nv = min(SUB, te - t0);
+    lds_load_tile<T>(x + tile, nv, row_bytes, sX, lane);
+    lds_load_tile<T>(dt + tile, nv, row_bytes, sDT, lane);
+    if (gate) lds_load_tile<T>(z + tile, nv, row_bytes, sZ, lane);
+  }
   for (int j = 0; j < nsub_c; ++j) {
     const int ts = t0 + j * SUB;
     const int nvalid = min(SUB, te - ts);
@@ -444,16 +534,28 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
     const size_t jb = cbase * nsub + j;
     const size_t tile = (row + ts) * D + col0;
     const size_t tile_bytes = static_cast<size_t>(nvalid) * row_bytes;
+    // this tile's x and dt are in LDS once every vector load issued so far is done
+    wait_vmem_all();
     float xr[SUB], dr[SUB];
-    load_col_raw<T, SUB>(make_rsrc(x + tile, tile_bytes), voff, row_bytes, nvalid, xr);
-    load_col_raw<T, SUB>(make_rsrc(dt + tile, tile_bytes), voff, row_bytes, nvalid, dr);
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) {
+      xr[k] = lds_val<T>(sX, k, lane);
+      dr[k] = lds_val<T>(sDT, k, lane);
+    }
+    wait_lds_all();  // the reads are done before the buffers are refilled
+    if (!last) {
+      const size_t tile1 = tile + static_cast<size_t>(SUB) * D;
+      const int nv1 = min(SUB, te - (ts + SUB));
+      lds_load_tile<T>(x + tile1, nv1, row_bytes, sX, lane);
+      lds_load_tile<T>(dt + tile1, nv1, row_bytes, sDT, lane);
+    }
     const float sj = last ? 0.0f : SIG[jb * D + d];
     const float* bt = bct + (static_cast<size_t>(b) * ntile + static_cast<size_t>(c) * nsub + j) * N * 2 * SUB;
     const __amdgpu_buffer_rsrc_t rj_rsrc = make_rsrc(R + jb * N * D + col0, state_bytes);
     float dl[SUB], u[SUB], y[SUB];
+    tile_delta<SUB>(dr, bias, nvalid, dl);
 #pragma unroll
     for (int k = 0; k < SUB; ++k) {
-      dl[k] = k < nvalid ? softplus_f32(dr[k] + bias) : 0.0f;
       u[k] = dl[k] * xr[k];
       y[k] = skip * xr[k];
     }
@@ -461,24 +563,27 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
       float w[SUB];
 #pragma unroll
       for (int k = 0; k < SUB; ++k) w[k] = fast_exp2(dl[k] * a20);
-      output_tile_states<SUB, DIRS, true>(N, D, lane, w, u, y, bt, sA2, sHf, rj_rsrc, cr_rsrc,
+      output_tile_states<SUB, DIRS, true>(N, D, lane, w, u, y, bt, sHf, rj_rsrc, cr_rsrc, a2_rsrc,
                                           fast_exp2(a20 * sj), sj, last);
     } else {
-      output_tile_states<SUB, DIRS, false>(N, D, lane, dl, u, y, bt, sA2, sHf, rj_rsrc, cr_rsrc, 1.0f, sj,
+      output_tile_states<SUB, DIRS, false>(N, D, lane, dl, u, y, bt, sHf, rj_rsrc, cr_rsrc, a2_rsrc, 1.0f, sj,
                                            last);
     }
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + tile, tile_bytes);
     if (gate) {
+      wait_vmem_all();  // this tile's z
       float zr[SUB];
-      load_col_raw<T, SUB>(make_rsrc(z + tile, tile_bytes), voff, row_bytes, nvalid, zr);
 #pragma unroll
-      for (int k = 0; k < SUB; ++k)
-        if (k < nvalid) IO<T>::store(y[k] * silu_f32(zr[k]), ro, voff, static_cast<uint32_t>(k) * row_bytes);
-    } else {
+      for (int k = 0; k < SUB; ++k) zr[k] = lds_val<T>(sZ, k, lane);
+      wait_lds_all();
+      if (!last) {
+        const size_t tile1 = tile + static_cast<size_t>(SUB) * D;
+        lds_load_tile<T>(z + tile1, min(SUB, te - (ts + SUB)), row_bytes, sZ, lane);
+      }
 #pragma unroll
-      for (int k = 0; k < SUB; ++k)
-        if (k < nvalid) IO<T>::store(y[k], ro, voff, static_cast<uint32_t>(k) * row_bytes);
+      for (int k = 0; k < SUB; ++k) y[k] *= silu_f32(zr[k]);
     }
+    store_col<T, SUB>(y, ro, voff, row_bytes, nvalid);
   }
   if (h_out != nullptr && c == nchunk - 1) {
     for (int n = 0; n < N; ++n) h_out[(static_cast<size_t>(b) * D + d) * N + n] = sHf[n][lane];
