@@ -61,31 +61,42 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, si
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, kRsrcWord3);
 }
 
+// Cache policy for data read or written exactly once (activations, outputs,
+// boundary states): non-temporal, the nt bit of the buffer instruction's
+// cache-policy field, so that these streams do not push data that is read
+// again (chunk carries, the B/C table) out of L2.
+constexpr int kStreamCpol = 2;
+
 template <typename T>
 struct IO;
 
 template <>
 struct IO<float> {
   static constexpr uint32_t kBytes = 4;
+  template <int CP = 0>
   static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, CP));
   }
+  template <int CP = 0>
   static __device__ __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, CP);
   }
 };
+
 
 template <>
 struct IO<bf16_t> {
   static constexpr uint32_t kBytes = 2;
+  template <int CP = 0>
   static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, CP);
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
   }
   // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN
+  template <int CP = 0>
   static __device__ __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     const __bf16 h = static_cast<__bf16>(v);
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), r, voff, soff, CP);
   }
 };
 
@@ -97,7 +108,8 @@ template <typename T, int SUB>
 __device__ __forceinline__ void load_col_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t row_bytes, int nvalid,
                                              float (&v)[SUB]) {
 #pragma unroll
-  for (int k = 0; k < SUB; ++k) v[k] = IO<T>::load(r, voff, static_cast<uint32_t>(min(k, nvalid - 1)) * row_bytes);
+  for (int k = 0; k < SUB; ++k)
+    v[k] = IO<T>::template load<kStreamCpol>(r, voff, static_cast<uint32_t>(min(k, nvalid - 1)) * row_bytes);
 }
 
 // delta = softplus(dt + dt_bias) for a tile's tokens; tokens past nvalid get
@@ -121,11 +133,11 @@ __device__ __forceinline__ void store_col(const float (&v)[SUB], __amdgpu_buffer
                                           uint32_t row_bytes, int nvalid) {
   if (nvalid == SUB) {
 #pragma unroll
-    for (int k = 0; k < SUB; ++k) IO<T>::store(v[k], r, voff, static_cast<uint32_t>(k) * row_bytes);
+    for (int k = 0; k < SUB; ++k) IO<T>::template store<kStreamCpol>(v[k], r, voff, static_cast<uint32_t>(k) * row_bytes);
   } else {
 #pragma unroll
     for (int k = 0; k < SUB; ++k)
-      if (k < nvalid) IO<T>::store(v[k], r, voff, static_cast<uint32_t>(k) * row_bytes);
+      if (k < nvalid) IO<T>::template store<kStreamCpol>(v[k], r, voff, static_cast<uint32_t>(k) * row_bytes);
   }
 }
 
@@ -219,7 +231,7 @@ __device__ __forceinline__ void summary_tile_states(int N, int lane, const float
     q = GEO ? q * qstep : fast_exp2(a2 * sigma);
     sS[n][lane] = fmaf(q, f, sS[n][lane]);
     sR[n][lane] = r;
-    if (store_r) Rdst[static_cast<size_t>(n) * r_stride] = r;
+    if (store_r) __builtin_nontemporal_store(r, &Rdst[static_cast<size_t>(n) * r_stride]);
   }
 }
 
@@ -300,7 +312,7 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
       summary_tile_states<SUB, false>(N, lane, dl, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, j > 0);
     }
     sigma += tile_sum;
-    if (j > 0) SIG[jb * D + d] = sigma;
+    if (j > 0) __builtin_nontemporal_store(sigma, &SIG[jb * D + d]);
   }
   for (int n = 0; n < N; ++n) {
     const size_t o = (cbase * N + n) * D + d;
@@ -384,7 +396,7 @@ __device__ __forceinline__ void lds_load_tile(const T* base, int nvalid, uint32_
   for (int i = 0; i < static_cast<int>(kSub) / kRowsPerInst; ++i) {
     const int row = min(i * kRowsPerInst + rl, nvalid - 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)&dst[i * kRowsPerInst][0],
-                                             16, static_cast<uint32_t>(row) * row_bytes + cb, 0, 0, 0);
+                                             16, static_cast<uint32_t>(row) * row_bytes + cb, 0, 0, kStreamCpol);
   }
 }
 
@@ -425,7 +437,7 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
   float q = 1.0f;
   float rj_next = 0.0f, cr_next = 0.0f, a2_next = 0.0f;
   if (kRev) {
-    rj_next = IO<float>::load(rj_rsrc, voff4, 0);
+    rj_next = IO<float>::load<kStreamCpol>(rj_rsrc, voff4, 0);
     cr_next = IO<float>::load(cr_rsrc, voff4, 0);
   }
   if (!GEO) a2_next = IO<float>::load(a2_rsrc, voff4, 0);
@@ -443,7 +455,7 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
     if (kRev) {
       rj = rj_next;
       cr = cr_next;
-      rj_next = IO<float>::load(rj_rsrc, voff4, s1);
+      rj_next = IO<float>::load<kStreamCpol>(rj_rsrc, voff4, s1);
       cr_next = IO<float>::load(cr_rsrc, voff4, s1);
     }
     float bb[SUB];
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
       lds_load_tile<T>(x + tile1, nv1, row_bytes, sX, lane);
       lds_load_tile<T>(dt + tile1, nv1, row_bytes, sDT, lane);
     }
-    const float sj = last ? 0.0f : SIG[jb * D + d];
+    const float sj = last ? 0.0f : __builtin_nontemporal_load(&SIG[jb * D + d]);
     const float* bt = bct + (static_cast<size_t>(b) * ntile + static_cast<size_t>(c) * nsub + j) * N * 2 * SUB;
     const __amdgpu_buffer_rsrc_t rj_rsrc = make_rsrc(R + jb * N * D + col0, state_bytes);
     float dl[SUB], u[SUB], y[SUB];
