@@ -91,8 +91,9 @@ int bimamba_scan_fwd(const void* x, const void* dt, const float* A, const void* 
 
 /* One stage of bimamba_scan_fwd, for callers that schedule other work between
  * the stages or attribute time per stage.  stage 0 = chunk summaries (reads
- * x, dt, B; writes the workspace), 1 = carries across chunks (workspace only),
- * 2 = output (reads x, dt, z, B, C and the workspace; writes out).  Calling
+ * B, C into an fp32 table in the workspace, then x, dt; writes the workspace),
+ * 1 = carries across chunks (workspace only), 2 = output (reads x, dt, z and
+ * the workspace; writes out).  Calling
  * stages 0, 1, 2 in this order on one stream with the same arguments and
  * workspace produces exactly what one bimamba_scan_fwd call produces.  Any
  * other stage value returns BIMAMBA_ERR_INVALID_ARGUMENT.  Arguments and
