@@ -129,6 +129,7 @@ int bimamba_scan_fwd_stage(int stage, const void* x, const void* dt, const float
 
 size_t bimamba_scan_block_workspace_bytes(int64_t batch, int64_t block_len, int64_t d_inner, int64_t d_state) {
   if (check_shape(batch, block_len, d_inner, d_state, BIMAMBA_F32) != BIMAMBA_OK) return 0;
+  if (block_len <= bimamba::kBlockFusedMax) return 0;  // single-kernel path
   return bimamba::make_plan(batch, block_len, d_inner, d_state).total;
 }
 
@@ -147,11 +148,15 @@ int bimamba_scan_block(const void* x, const void* dt, const float* A, const void
   const size_t es = io_dtype == BIMAMBA_BF16 ? 2 : 4;
   const size_t out_bytes = static_cast<size_t>(batch) * block_len * d_inner * es;
   if (h_out && overlap(range_of(h_out, st_bytes), range_of(out, out_bytes))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  bimamba::ScanArgs a{x, dt, A, B, C, D, z, dt_bias, out, h_in, h_out, io_dtype, flags};
+  if (block_len <= bimamba::kBlockFusedMax) {
+    // single-kernel path: the workspace is not used (it may be NULL)
+    return map_hip(bimamba::launch_block_fused(a, batch, block_len, d_inner, d_state, stream));
+  }
   const Plan p = bimamba::make_plan(batch, block_len, d_inner, d_state);
   s = check_workspace(p, workspace, workspace_bytes, out, out_bytes);
   if (s != BIMAMBA_OK) return s;
   if (h_out && overlap(range_of(h_out, st_bytes), range_of(workspace, p.total))) return BIMAMBA_ERR_INVALID_ARGUMENT;
-  bimamba::ScanArgs a{x, dt, A, B, C, D, z, dt_bias, out, h_in, h_out, io_dtype, flags};
   return map_hip(bimamba::launch_chunked(a, p, workspace, stream));
 }
 

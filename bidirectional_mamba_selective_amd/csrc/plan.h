@@ -15,6 +15,8 @@ constexpr int64_t kLanes = 64;
 // Wavefronts the chunking aims to give the summary and output kernels (four per
 // SIMD on a 256-CU part).
 constexpr int64_t kTargetWaves = 4096;
+// Longest block the single-kernel block path handles (it needs no workspace).
+constexpr int64_t kBlockFusedMax = 64;
 
 struct Plan {
   int64_t batch, seqlen, d_inner, d_state;

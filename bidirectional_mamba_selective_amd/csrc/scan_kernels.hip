@@ -603,6 +603,181 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
 }
 
 // ---------------------------------------------------------------------------
+// k_block: one short block of block-cache decoding in a single kernel (the
+// forward direction from the cached state, the reverse direction from zero at
+// the block's last token; the new cache is the forward state after the block).
+// grid (d_inner / 64, batch); a workgroup owns 64 channels (lane = channel) and
+// its wavefronts split the states, kSpw states each.  The block is padded to GM
+// tokens (GM in {16, 32, 64}); padding tokens have delta = 0 and no input, so
+// they leave every state unchanged and are never stored.
+//   1. all wavefronts: delta and delta*x of the block's tokens into LDS, B and C
+//      (fp32) into LDS;
+//   2. each wavefront, per state it owns: abar and delta*x*B for every token
+//      (kept in registers), the forward chain from h_in with its readout, then
+//      the reverse chain with its readout, into a per-wavefront partial y;
+//   3. the partials meet in LDS (the buffer of step 1, reused) and are summed in
+//      a fixed wavefront order (deterministic); skip term, gate, store.
+// With a few hundred wavefronts per call the block step costs one launch
+// instead of the chunked path's six.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ float ld_any(const T* p);
+template <>
+__device__ __forceinline__ float ld_any<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float ld_any<bf16_t>(const bf16_t* p) { return to_f32(*p); }
+
+template <typename T>
+__device__ __forceinline__ void st_any(T* p, float v);
+template <>
+__device__ __forceinline__ void st_any<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void st_any<bf16_t>(bf16_t* p, float v) {
+  const __bf16 h = static_cast<__bf16>(v);  // round to nearest even
+  p->bits = __builtin_bit_cast(unsigned short, h);
+}
+
+template <int GM>
+struct BlockSmem {
+  static constexpr int kSpw = GM <= 32 ? 1 : 2;        // states per wavefront
+  static constexpr int kMaxWaves = 16 / kSpw;          // d_state <= 16
+  union {
+    struct {
+      float dl[GM][64];
+      float u[GM][64];
+    } in;
+    float y[kMaxWaves][GM][64];
+  } s;
+  float b[16][GM];
+  float c[16][GM];
+};
+
+template <typename T, int GM>
+__global__ __launch_bounds__(GM <= 32 ? 1024 : 512) void k_block(
+    const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ z, const float* __restrict__ A,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dv,
+    const float* __restrict__ dt_bias, const float* h_in, float* h_out, T* __restrict__ out, int G, int D, int N,
+    int flags) {
+  using S = BlockSmem<GM>;
+  __shared__ S sm;
+  const int nw = static_cast<int>(blockDim.x) / 64;
+  const int wv = threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  const int d = blockIdx.x * 64 + lane;
+  const int b = blockIdx.y;
+  const size_t row = static_cast<size_t>(b) * G;  // first token row of this batch element
+  const bool gate = (flags & kNoGate) == 0;
+  const bool fwd = (flags & kRevOnly) == 0;
+  const bool rev = (flags & kFwdOnly) == 0;
+
+  // 1. delta, delta*x; B, C
+  const float bias = dt_bias ? dt_bias[d] : 0.0f;
+  for (int t = wv; t < GM; t += nw) {
+    float dl = 0.0f, u = 0.0f;
+    if (t < G) {
+      const size_t o = (row + t) * D + d;
+      dl = softplus_f32(ld_any(dt + o) + bias);
+      u = dl * ld_any(x + o);
+    }
+    sm.s.in.dl[t][lane] = dl;
+    sm.s.in.u[t][lane] = u;
+  }
+  for (int i = threadIdx.x; i < N * GM; i += blockDim.x) {
+    const int n = i / GM;
+    const int t = i - n * GM;
+    float bv = 0.0f, cv = 0.0f;
+    if (t < G) {
+      bv = ld_any(Bm + (row + t) * N + n);
+      cv = ld_any(Cm + (row + t) * N + n);
+    }
+    sm.b[n][t] = bv;
+    sm.c[n][t] = cv;
+  }
+  __syncthreads();
+
+  // 2. the states of this wavefront
+  float y[GM];
+#pragma unroll
+  for (int t = 0; t < GM; ++t) y[t] = 0.0f;
+#pragma unroll
+  for (int q = 0; q < S::kSpw; ++q) {
+    const int n = wv * S::kSpw + q;
+    if (n < N) {
+      const float a2 = A[static_cast<size_t>(d) * N + n] * kLog2e;
+      float a[GM];
+#pragma unroll
+      for (int t = 0; t < GM; ++t) a[t] = fast_exp2(sm.s.in.dl[t][lane] * a2);
+      const size_t hs = (static_cast<size_t>(b) * D + d) * N + n;
+      float hf = h_in ? h_in[hs] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < GM; ++t) {
+        hf = fmaf(a[t], hf, sm.s.in.u[t][lane] * sm.b[n][t]);
+        if (fwd) y[t] = fmaf(sm.c[n][t], hf, y[t]);
+      }
+      if (h_out) h_out[hs] = hf;  // padding tokens leave hf unchanged
+      if (rev) {
+        // delta*x*B is formed again from LDS rather than kept for every token in
+        // registers (the barrier keeps the compiler from reusing the first reads)
+        asm volatile("" ::: "memory");
+        float hr = 0.0f;
+#pragma unroll
+        for (int t = GM - 1; t >= 0; --t) {
+          hr = fmaf(a[t], hr, sm.s.in.u[t][lane] * sm.b[n][t]);
+          y[t] = fmaf(sm.c[n][t], hr, y[t]);
+        }
+      }
+    }
+  }
+
+  // 3. partials through LDS (reusing the step-1 buffer), fixed summation order
+  __syncthreads();  // every wavefront is done reading delta and delta*x
+#pragma unroll
+  for (int t = 0; t < GM; ++t) sm.s.y[wv][t][lane] = y[t];
+  __syncthreads();
+  const float ndir = (fwd && rev) ? 2.0f : 1.0f;
+  const float skip = Dv ? ndir * Dv[d] : 0.0f;
+  for (int t = wv; t < G; t += nw) {
+    float acc = 0.0f;
+    for (int w = 0; w < nw; ++w) acc += sm.s.y[w][t][lane];
+    const size_t o = (row + t) * D + d;
+    acc = fmaf(skip, ld_any(x + o), acc);
+    if (gate) acc *= silu_f32(ld_any(z + o));
+    st_any(out + o, acc);
+  }
+}
+
+template <typename T, int GM>
+static void launch_block_gm(const ScanArgs& a, int batch, int G, int D, int N, hipStream_t stream) {
+  using S = BlockSmem<GM>;
+  const int nw = (N + S::kSpw - 1) / S::kSpw;
+  const dim3 grid(static_cast<unsigned>(D / 64), static_cast<unsigned>(batch));
+  hipLaunchKernelGGL((k_block<T, GM>), grid, dim3(64 * nw), 0, stream, static_cast<const T*>(a.x),
+                     static_cast<const T*>(a.dt), static_cast<const T*>(a.z), a.A, static_cast<const T*>(a.B),
+                     static_cast<const T*>(a.C), a.D, a.dt_bias, a.h_in, a.h_out, static_cast<T*>(a.out), G, D, N,
+                     static_cast<int>(a.flags));
+}
+
+template <typename T>
+static hipError_t launch_block_typed(const ScanArgs& a, int batch, int G, int D, int N, hipStream_t stream) {
+  if (G <= 16) {
+    launch_block_gm<T, 16>(a, batch, G, D, N, stream);
+  } else if (G <= 32) {
+    launch_block_gm<T, 32>(a, batch, G, D, N, stream);
+  } else {
+    launch_block_gm<T, 64>(a, batch, G, D, N, stream);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_block_fused(const ScanArgs& a, int64_t batch, int64_t block_len, int64_t d_inner,
+                              int64_t d_state, hipStream_t stream) {
+  const int nb = static_cast<int>(batch), G = static_cast<int>(block_len), D = static_cast<int>(d_inner),
+            N = static_cast<int>(d_state);
+  if (a.io_dtype == 1) return launch_block_typed<bf16_t>(a, nb, G, D, N, stream);
+  return launch_block_typed<float>(a, nb, G, D, N, stream);
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
 template <typename T, int NM, int DIRS>

@@ -75,6 +75,29 @@ def test_block_small(G, flags):
     assert e_out <= 1e-4 and e_h <= 1e-5
 
 
+@pytest.mark.parametrize("N", [1, 5, 16])
+@pytest.mark.parametrize("G", [7, 33])
+@pytest.mark.parametrize("jitter", [0.0, 0.2])
+def test_block_state_counts(N, G, jitter):
+    """Blocks short enough for the single-kernel path, with state counts that leave the last wavefront
+    of a workgroup partly or wholly idle, general and geometric A, batch 2, cache updated in place."""
+    import torch
+
+    A, Dv, bias = I.make_params(128, N, a_jitter=jitter)
+    inp = I.make_activations(2, G, 128, N, "f32", seed=3 + G + N)
+    inp.update(A=A, D=Dv, dt_bias=bias)
+    dev = upload(inp, "f32")
+    rng = np.random.default_rng(N * 100 + G)
+    h0 = rng.standard_normal((2, 128, N)).astype(np.float32)
+    h = f32_dev(h0)
+    out = to_host64(_block_call(dev, dev, h, h))
+    want, want_h = oracle.scan_block(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                     inp["dt_bias"], h0)
+    e_out, e_h = rel_err(out, want), rel_err(to_host64(h), want_h)
+    say(f"block N={N} G={G} jitter={jitter}: out {e_out:.3e} h_out {e_h:.3e}")
+    assert e_out <= 1e-4 and e_h <= 1e-5
+
+
 def test_block_in_place_and_null_state():
     """h_out == h_in (in-place commit) and h_in == NULL (zero cache) behave like separate buffers."""
     import torch
