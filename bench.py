@@ -95,6 +95,13 @@ def cpu_baseline(inp, L, D, nch):
                       f"scaled by {D}/{nch} to the full channel count"}
 
 
+def up_arr(a, w, torch, I, dev):
+    """Host fp32 array (exact in the I/O dtype) -> device tensor of the workload's I/O dtype."""
+    if w.io_dtype == "bf16":
+        return torch.from_numpy(I.bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
 def bench_block(args, w, torch, bm, I, dev):
     """Block-decoding sweep: one bimamba_scan_block call per block of w.block_len tokens, the cached
     forward state carried in place from block to block.  A step is the whole sweep.  Reported: sweep
@@ -165,6 +172,44 @@ def bench_block(args, w, torch, bm, I, dev):
         same = torch.equal(torch.cat(outs, dim=1), ref_out) and torch.equal(h, ref_h)
         if not same:
             raise SystemExit(f"graph replay {r} differs from the eager sweep")
+    # latency of one block step at other block lengths: 200 re-runs of one block from the same cache
+    # (h_out = NULL, the denoising pattern before a commit), captured as a graph and replayed
+    call_us = {}
+    for Gc in (32, 64, 128):
+        act = I.make_activations(w.batch, Gc, w.d_inner, w.d_state, w.io_dtype, seed=9)
+        bl = {k: up_arr(act[k], w, torch, I, dev) for k in ("x", "dt", "z", "B", "C")}
+        o = torch.empty_like(bl["x"])
+        needc = bm.bimamba_scan_block_workspace_bytes(w.batch, Gc, w.d_inner, w.d_state)
+        wsc = torch.empty(needc, dtype=torch.uint8, device=dev) if needc else None
+
+        def one(s_):
+            bm.bimamba_scan_block(bl["x"], bl["dt"], A, bl["B"], bl["C"], Dv, bl["z"], bias, h_in=h, h_out=None,
+                                  out=o, workspace=wsc, stream=s_)
+
+        one(stream)
+        torch.cuda.synchronize()
+        ref = o.clone()
+        g2 = torch.cuda.CUDAGraph()
+        gs = torch.cuda.Stream(dev)
+        gs.wait_stream(stream)
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g2, stream=gs):
+                for _ in range(200):
+                    one(gs)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            o.zero_()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            g2.replay()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+            if not torch.equal(o, ref):
+                raise SystemExit(f"block G={Gc}: graph replay differs from the eager call")
+        call_us[str(Gc)] = round(float(np.median(ts)) * 1e6 / 200, 2)
+        log(f"block step G={Gc}: {call_us[str(Gc)]} us per call (graph of 200 re-runs)")
+
     tok = w.batch * w.seqlen
     te, tg = float(np.median(t_eager)), float(np.median(t_graph))
     log(f"sweep: eager {te * 1e3:.2f} ms, graph replay {tg * 1e3:.2f} ms (replays equal the eager result)")
@@ -187,6 +232,7 @@ def bench_block(args, w, torch, bm, I, dev):
         "us_per_block_eager": round(te * 1e6 / nblk, 2),
         "tokens_per_s_eager": round(tok / te, 1),
         "workspace_bytes": need,
+        "us_per_block_call_graph": call_us,
     }
     print(json.dumps(line), flush=True)
 

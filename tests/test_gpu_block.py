@@ -98,6 +98,38 @@ def test_block_state_counts(N, G, jitter):
     assert e_out <= 1e-4 and e_h <= 1e-5
 
 
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_block_reruns_then_commit(G):
+    """Block-diffusion decoding: the active block is denoised k = 4 times from the same cached state
+    (fresh x, z each time; the cache is not written), then committed once (cache updated). Blocks of 32
+    and 64 tokens take the single-kernel path, 128 the chunked one; bf16 I/O at d_inner 256."""
+    import torch
+
+    from bidirectional_mamba_selective_amd import bimamba_scan_block
+
+    D, N = 256, 16
+    A, Dv, bias = I.make_params(D, N)
+    rng = np.random.default_rng(G)
+    h0 = rng.standard_normal((1, D, N)).astype(np.float32)
+    h = f32_dev(h0)
+    for r in range(5):
+        inp = I.make_activations(1, G, D, N, "bf16", seed=7, xz_seed=500 + r)
+        inp.update(A=A, D=Dv, dt_bias=bias)
+        dev = upload(inp, "bf16")
+        commit = r == 4
+        out = bimamba_scan_block(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], dev["z"],
+                                 dev["dt_bias"], h_in=h, h_out=h if commit else None)
+        torch.cuda.synchronize()
+        want, want_h = oracle.scan_block(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                         inp["dt_bias"], h0)
+        err = rel_err(to_host64(out), want)
+        say(f"block G={G} run {r}{' (commit)' if commit else ''}: out {err:.3e}")
+        assert err <= tol_for("bf16")
+        if not commit:
+            assert np.array_equal(to_host64(h), h0.astype(np.float64)), "a re-run without h_out wrote the cache"
+    assert rel_err(to_host64(h), want_h) <= 1e-5
+
+
 def test_block_in_place_and_null_state():
     """h_out == h_in (in-place commit) and h_in == NULL (zero cache) behave like separate buffers."""
     import torch
