@@ -243,7 +243,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_64k_bf16")
-    ap.add_argument("--cpu-channels", type=int, default=512)
+    ap.add_argument("--cpu-channels", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
@@ -320,6 +320,30 @@ def main():
     ms_step_gen = (time.perf_counter() - t0) * 1e3 / args.steps
     log(f"general A: {ms_step_gen:.4f} ms/step")
 
+    # untied directions on the same shape: a second input and parameter set for the reverse layer
+    act_r = I.make_activations(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype, seed=2)
+    A_r, D_r, bias_r = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+                        for a in I.make_params(w.d_inner, w.d_state, seed=1))
+    rev_set = dict(x=up_arr(act_r["x"], w, torch, I, dev), dt=up_arr(act_r["dt"], w, torch, I, dev),
+                   z=up_arr(act_r["z"], w, torch, I, dev), B=up_arr(act_r["B"], w, torch, I, dev),
+                   C=up_arr(act_r["C"], w, torch, I, dev), A=A_r, D=D_r, dt_bias=bias_r)
+    del act_r
+    fwd_set = dict(x=x, dt=dt, z=z, B=B, C=C, A=A, D=Dv, dt_bias=bias)
+    out_r = torch.empty_like(x)
+
+    def step_untied():
+        bm.bimamba_scan_fwd_untied(fwd_set, rev_set, out_f=out, out_r=out_r, workspace=ws, stream=stream)
+
+    for _ in range(2):
+        step_untied()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_untied()
+    torch.cuda.synchronize()
+    ms_step_untied = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"untied directions: {ms_step_untied:.4f} ms/step")
+
     # per-kernel attribution on the same stream: staged entry point, events between stages
     names = ("k_summary", "k_carry", "k_output")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -378,6 +402,11 @@ def main():
                       "note": "A[d,n] = -(n+1)*(1+0.2*U(-1,1)): no per-channel geometric structure, one exp per "
                               "(token, channel, state) in each pass"},
         "ms_per_step_events": round(ms_step_ev, 4),
+        "untied": {"ms_per_step": round(ms_step_untied, 4),
+                   "tokens_per_s": round(tokens / (ms_step_untied * 1e-3), 1),
+                   "note": "each direction its own x, dt, B, C, z, A, D, dt_bias and its own gated output "
+                           "(bimamba_scan_fwd_untied): a forward-only and a reverse-only pass, twice the "
+                           "activation bytes and no shared abar"},
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_channels} channels")

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     bimamba_scan_block_workspace_bytes,
     bimamba_scan_fwd,
     bimamba_scan_fwd_stage,
+    bimamba_scan_fwd_untied,
     bimamba_scan_fwd_workspace_bytes,
     bimamba_status_string,
     bimamba_version,

@@ -34,6 +34,7 @@ EXPORTED = (
     "bimamba_scan_fwd_workspace_bytes",
     "bimamba_scan_fwd",
     "bimamba_scan_fwd_stage",
+    "bimamba_scan_fwd_untied",
     "bimamba_scan_block_workspace_bytes",
     "bimamba_scan_block",
 )
@@ -70,6 +71,8 @@ def load() -> ctypes.CDLL:
     lib.bimamba_scan_fwd_stage.restype = ctypes.c_int
     lib.bimamba_scan_fwd_stage.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                            ctypes.c_int, ctypes.c_uint32, vp, sz, vp]
+    lib.bimamba_scan_fwd_untied.restype = ctypes.c_int
+    lib.bimamba_scan_fwd_untied.argtypes = [vp] * 18 + [i64, i64, i64, i64, ctypes.c_int, ctypes.c_uint32, vp, sz, vp]
     lib.bimamba_scan_block.restype = ctypes.c_int
     lib.bimamba_scan_block.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                        ctypes.c_uint32, vp, sz, vp]
@@ -171,6 +174,30 @@ def bimamba_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, fla
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_scan_fwd")
     return out
+
+
+def bimamba_scan_fwd_untied(fwd, rev, out_f=None, out_r=None, flags: int = 0, workspace=None, stream=None):
+    """Untied directions: fwd and rev are dicts with keys x, dt, A, B, C and optionally D, z, dt_bias (each
+    direction's own tensors).  Returns (out_f, out_r): the forward layer's gated output and the reverse layer's."""
+    torch = _torch()
+    f = {k: fwd.get(k) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")}
+    r = {k: rev.get(k) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")}
+    nb, L, nd, ns, out_f = _common(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], f["z"], f["dt_bias"], out_f)
+    shape_r = _common(r["x"], r["dt"], r["A"], r["B"], r["C"], r["D"], r["z"], r["dt_bias"], out_r)
+    if shape_r[:4] != (nb, L, nd, ns) or r["x"].dtype != f["x"].dtype:
+        raise ValueError("the two directions must have the same shapes and I/O dtype")
+    out_r = shape_r[4]
+    lib = load()
+    need = int(lib.bimamba_scan_fwd_workspace_bytes(nb, L, nd, ns))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=f["x"].device)
+    ptrs = [_ptr(f[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")] + [_ptr(out_f)]
+    ptrs += [_ptr(r[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")] + [_ptr(out_r)]
+    st = lib.bimamba_scan_fwd_untied(*ptrs, nb, L, nd, ns, _io_dtype(f["x"]), flags, _ptr(workspace),
+                                     workspace.numel(), _stream(stream, f["x"].device))
+    if st != BIMAMBA_OK:
+        raise BimambaError(st, "bimamba_scan_fwd_untied")
+    return out_f, out_r
 
 
 def bimamba_scan_fwd_stage(stage: int, x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, flags: int = 0,

@@ -127,6 +127,51 @@ int bimamba_scan_fwd_stage(int stage, const void* x, const void* dt, const float
                        workspace, workspace_bytes, stream);
 }
 
+int bimamba_scan_fwd_untied(const void* x_f, const void* dt_f, const float* A_f, const void* B_f, const void* C_f,
+                            const float* D_f, const void* z_f, const float* dt_bias_f, void* out_f, const void* x_r,
+                            const void* dt_r, const float* A_r, const void* B_r, const void* C_r, const float* D_r,
+                            const void* z_r, const float* dt_bias_r, void* out_r, int64_t batch, int64_t seqlen,
+                            int64_t d_inner, int64_t d_state, int io_dtype, uint32_t flags, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  int s = check_shape(batch, seqlen, d_inner, d_state, io_dtype);
+  if (s != BIMAMBA_OK) return s;
+  if (flags & ~static_cast<uint32_t>(BIMAMBA_FLAG_NO_GATE)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  s = check_tensors(x_f, dt_f, A_f, B_f, C_f, D_f, z_f, dt_bias_f, out_f, batch, seqlen, d_inner, d_state, io_dtype,
+                    flags);
+  if (s != BIMAMBA_OK) return s;
+  s = check_tensors(x_r, dt_r, A_r, B_r, C_r, D_r, z_r, dt_bias_r, out_r, batch, seqlen, d_inner, d_state, io_dtype,
+                    flags);
+  if (s != BIMAMBA_OK) return s;
+  // the reverse pass runs after the forward one: out_f must not overlap anything the reverse pass
+  // reads or writes, nor out_r anything of the forward pass
+  const size_t es = io_dtype == BIMAMBA_BF16 ? 2 : 4;
+  const size_t act = static_cast<size_t>(batch) * seqlen * d_inner * es;
+  const size_t bc = static_cast<size_t>(batch) * seqlen * d_state * es;
+  const size_t par = static_cast<size_t>(d_inner) * d_state * 4, vec = static_cast<size_t>(d_inner) * 4;
+  auto hits = [&](const void* out, const void* x, const void* dt, const float* A, const void* B, const void* C,
+                  const float* D, const void* z, const float* bias) {
+    const Range o = range_of(out, act);
+    return overlap(o, range_of(x, act)) || overlap(o, range_of(dt, act)) || overlap(o, range_of(B, bc)) ||
+           overlap(o, range_of(C, bc)) || (z && overlap(o, range_of(z, act))) || overlap(o, range_of(A, par)) ||
+           (D && overlap(o, range_of(D, vec))) || (bias && overlap(o, range_of(bias, vec)));
+  };
+  if (hits(out_f, x_r, dt_r, A_r, B_r, C_r, D_r, z_r, dt_bias_r) ||
+      hits(out_r, x_f, dt_f, A_f, B_f, C_f, D_f, z_f, dt_bias_f) || overlap(range_of(out_f, act), range_of(out_r, act)))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const Plan p = bimamba::make_plan(batch, seqlen, d_inner, d_state);
+  s = check_workspace(p, workspace, workspace_bytes, out_f, act);
+  if (s != BIMAMBA_OK) return s;
+  if (overlap(range_of(workspace, p.total), range_of(out_r, act))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  // two one-direction passes in stream order, sharing the workspace
+  const bimamba::ScanArgs af{x_f, dt_f, A_f, B_f, C_f, D_f, z_f, dt_bias_f, out_f, nullptr, nullptr, io_dtype,
+                             flags | BIMAMBA_FLAG_FWD_ONLY};
+  s = map_hip(bimamba::launch_chunked(af, p, workspace, stream));
+  if (s != BIMAMBA_OK) return s;
+  const bimamba::ScanArgs ar{x_r, dt_r, A_r, B_r, C_r, D_r, z_r, dt_bias_r, out_r, nullptr, nullptr, io_dtype,
+                             flags | BIMAMBA_FLAG_REV_ONLY};
+  return map_hip(bimamba::launch_chunked(ar, p, workspace, stream));
+}
+
 size_t bimamba_scan_block_workspace_bytes(int64_t batch, int64_t block_len, int64_t d_inner, int64_t d_state) {
   if (check_shape(batch, block_len, d_inner, d_state, BIMAMBA_F32) != BIMAMBA_OK) return 0;
   if (block_len <= bimamba::kBlockFusedMax) return 0;  // single-kernel path

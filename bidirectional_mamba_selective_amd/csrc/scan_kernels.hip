@@ -195,8 +195,10 @@ __device__ __forceinline__ bool wave_geometric(bool lane_geo) { return __all(lan
 //   else: w[k] = delta_k and abar = exp2(delta_k A[d,n] log2 e); B comes from
 //         the scalar table (bt), which keeps LDS at the two per-lane state
 //         arrays; A[d,n] is read one state ahead.
+// DS: bit 0 = forward summary (f, S), bit 1 = reverse summary (r, boundary
+// states); a one-direction scan computes only what its output pass reads.
 // ---------------------------------------------------------------------------
-template <int SUB, bool GEO>
+template <int SUB, bool GEO, int DS>
 __device__ __forceinline__ void summary_tile_states(int N, int lane, const float (&w)[SUB], const float (&u)[SUB],
                                                     float sigma, float a20, float (*sB)[SUB],
                                                     const float* __restrict__ bt, const float* __restrict__ Arow,
@@ -222,23 +224,28 @@ __device__ __forceinline__ void summary_tile_states(int N, int lane, const float
     // the forward (ascending) and reverse (descending) chains are independent:
     // interleaving them doubles the instruction-level parallelism
     float f = 0.0f;
-    float r = sR[n][lane];
+    float r = (DS & 2) ? sR[n][lane] : 0.0f;
 #pragma unroll
     for (int t = 0; t < SUB; ++t) {
-      f = fmaf(a[t], f, bb[t]);
-      r = fmaf(a[SUB - 1 - t], r, bb[SUB - 1 - t]);
+      if (DS & 1) f = fmaf(a[t], f, bb[t]);
+      if (DS & 2) r = fmaf(a[SUB - 1 - t], r, bb[SUB - 1 - t]);
     }
-    q = GEO ? q * qstep : fast_exp2(a2 * sigma);
-    sS[n][lane] = fmaf(q, f, sS[n][lane]);
-    sR[n][lane] = r;
-    if (store_r) __builtin_nontemporal_store(r, &Rdst[static_cast<size_t>(n) * r_stride]);
+    if (DS & 1) {
+      q = GEO ? q * qstep : fast_exp2(a2 * sigma);
+      sS[n][lane] = fmaf(q, f, sS[n][lane]);
+    }
+    if (DS & 2) {
+      sR[n][lane] = r;
+      if (store_r) __builtin_nontemporal_store(r, &Rdst[static_cast<size_t>(n) * r_stride]);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// k_summary: grid (d_inner / 64, nchunk, batch), block 64.
+// k_summary: grid (d_inner / 64, nchunk, batch), block 64.  DS as above; P is
+// always written (both carries compose with it).
 // ---------------------------------------------------------------------------
-template <typename T, int NM, bool GEO>
+template <typename T, int NM, bool GEO, int DS>
 __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T* __restrict__ dt,
                                                 const float* __restrict__ A, const float* __restrict__ bct,
                                                 const float* __restrict__ dt_bias, int L, int D, int N, int chunk,
@@ -247,8 +254,8 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
                                                 float* __restrict__ R, float* __restrict__ SIG) {
   constexpr int SUB = static_cast<int>(kSub);
   static_assert(NM * SUB <= 64 * 4, "one float4 of B per lane");
-  __shared__ float sR[NM][64];
-  __shared__ float sS[NM][64];
+  __shared__ float sR[(DS & 2) ? NM : 1][64];
+  __shared__ float sS[(DS & 1) ? NM : 1][64];
   __shared__ __align__(16) float sB[GEO ? NM : 1][SUB];  // this tile's B, one row per state (GEO)
   const int lane = threadIdx.x;
   const int d = blockIdx.x * 64 + lane;
@@ -266,8 +273,8 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
   // Each wavefront runs in exactly one of the two instantiations (general / geometric A).
   if (wave_geometric(geo_lane) != GEO) return;
   for (int n = 0; n < N; ++n) {
-    sR[n][lane] = 0.0f;
-    sS[n][lane] = 0.0f;
+    if (DS & 2) sR[(DS & 2) ? n : 0][lane] = 0.0f;
+    if (DS & 1) sS[(DS & 1) ? n : 0][lane] = 0.0f;
   }
   const float a20 = a0 * kLog2e;
   const float bias = dt_bias ? dt_bias[d] : 0.0f;
@@ -307,17 +314,17 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
       float w[SUB];
 #pragma unroll
       for (int k = 0; k < SUB; ++k) w[k] = fast_exp2(dl[k] * a20);
-      summary_tile_states<SUB, true>(N, lane, w, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, j > 0);
+      summary_tile_states<SUB, true, DS>(N, lane, w, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, j > 0);
     } else {
-      summary_tile_states<SUB, false>(N, lane, dl, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, j > 0);
+      summary_tile_states<SUB, false, DS>(N, lane, dl, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, j > 0);
     }
     sigma += tile_sum;
-    if (j > 0) __builtin_nontemporal_store(sigma, &SIG[jb * D + d]);
+    if ((DS & 2) && j > 0) __builtin_nontemporal_store(sigma, &SIG[jb * D + d]);
   }
   for (int n = 0; n < N; ++n) {
     const size_t o = (cbase * N + n) * D + d;
-    Sf[o] = sS[n][lane];
-    Sr[o] = sR[n][lane];
+    if (DS & 1) Sf[o] = sS[(DS & 1) ? n : 0][lane];
+    if (DS & 2) Sr[o] = sR[(DS & 2) ? n : 0][lane];
     P[o] = fast_exp2(Arow[n] * kLog2e * sigma);
   }
 }
@@ -427,8 +434,10 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
                                                    const float* __restrict__ bt, float (*sHf)[64],
                                                    __amdgpu_buffer_rsrc_t rj_rsrc, __amdgpu_buffer_rsrc_t cr_rsrc,
                                                    __amdgpu_buffer_rsrc_t a2_rsrc, float qstep, float sj,
-                                                   bool last) {
+                                                   bool last, bool keep_hf) {
   constexpr bool kRev = (DIRS & 2) != 0;
+  // the forward chain runs for the forward readout or for the cached forward state
+  const bool fwd_chain = (DIRS & 1) != 0 || keep_hf;
   const uint32_t voff4 = static_cast<uint32_t>(lane) * 4u;
   const uint32_t nstride4 = static_cast<uint32_t>(D) * 4u;
   float a[SUB];
@@ -450,7 +459,7 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
       a2 = a2_next;
       a2_next = IO<float>::load(a2_rsrc, voff4, s1);
     }
-    float hf = sHf[n][lane];
+    float hf = fwd_chain ? sHf[n][lane] : 0.0f;
     float rj = 0.0f, cr = 0.0f;
     if (kRev) {
       rj = rj_next;
@@ -466,7 +475,7 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
     }
 #pragma unroll
     for (int k = 0; k < SUB; ++k) {
-      hf = fmaf(a[k], hf, bb[k]);
+      if (fwd_chain) hf = fmaf(a[k], hf, bb[k]);
       if (DIRS & 1) y[k] = fmaf(bn[SUB + k], hf, y[k]);
     }
     if (kRev) {
@@ -479,7 +488,7 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
         y[k] = fmaf(bn[SUB + k], hr, y[k]);
       }
     }
-    sHf[n][lane] = hf;
+    if (fwd_chain) sHf[n][lane] = hf;
   }
 }
 
@@ -576,10 +585,10 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
 #pragma unroll
       for (int k = 0; k < SUB; ++k) w[k] = fast_exp2(dl[k] * a20);
       output_tile_states<SUB, DIRS, true>(N, D, lane, w, u, y, bt, sHf, rj_rsrc, cr_rsrc, a2_rsrc,
-                                          fast_exp2(a20 * sj), sj, last);
+                                          fast_exp2(a20 * sj), sj, last, h_out != nullptr);
     } else {
       output_tile_states<SUB, DIRS, false>(N, D, lane, dl, u, y, bt, sHf, rj_rsrc, cr_rsrc, a2_rsrc, 1.0f, sj,
-                                           last);
+                                           last, h_out != nullptr);
     }
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + tile, tile_bytes);
     if (gate) {
@@ -791,6 +800,16 @@ static void launch_output(dim3 grid, hipStream_t stream, const T* x, const T* dt
                      out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf, Cr, R, SIG, A2T, a.h_out);
 }
 
+template <typename T, int NM, int DS>
+static void launch_summary(dim3 grid, hipStream_t stream, const T* x, const T* dt, const ScanArgs& a,
+                           const float* bct, int L, int D, int N, int chunk, int nchunk, int nsub, int ntile, float* Sf,
+                           float* Sr, float* P, float* R, float* SIG) {
+  hipLaunchKernelGGL((k_summary<T, NM, true, DS>), grid, dim3(64), 0, stream, x, dt, a.A, bct, a.dt_bias, L, D, N,
+                     chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG);
+  hipLaunchKernelGGL((k_summary<T, NM, false, DS>), grid, dim3(64), 0, stream, x, dt, a.A, bct, a.dt_bias, L, D, N,
+                     chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG);
+}
+
 template <typename T, int NM>
 static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipStream_t stream, int stage) {
   char* w = static_cast<char*>(ws);
@@ -821,10 +840,17 @@ static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipSt
     const size_t nbc = static_cast<size_t>(p.batch) * ntile * N * kSub;
     hipLaunchKernelGGL((k_stage_bc<T>), dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0, stream, Bm, Cm,
                        bct, L, N, ntile, nbc);
-    hipLaunchKernelGGL((k_summary<T, NM, true>), grid, dim3(64), 0, stream, x, dt, a.A, bct, a.dt_bias, L, D, N,
-                       chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG);
-    hipLaunchKernelGGL((k_summary<T, NM, false>), grid, dim3(64), 0, stream, x, dt, a.A, bct, a.dt_bias, L, D, N,
-                       chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG);
+    // the forward summary feeds the forward readout and the cached forward state;
+    // the reverse summary feeds the reverse readout
+    const bool need_f = (a.flags & kRevOnly) == 0 || a.h_out != nullptr;
+    const bool need_r = (a.flags & kFwdOnly) == 0;
+    if (need_f && need_r) {
+      launch_summary<T, NM, 3>(grid, stream, x, dt, a, bct, L, D, N, chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG);
+    } else if (need_f) {
+      launch_summary<T, NM, 1>(grid, stream, x, dt, a, bct, L, D, N, chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG);
+    } else {
+      launch_summary<T, NM, 2>(grid, stream, x, dt, a, bct, L, D, N, chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG);
+    }
     e = hipGetLastError();
     if (e != hipSuccess || stage == 0) return e;
   }

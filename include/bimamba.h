@@ -104,6 +104,30 @@ int bimamba_scan_fwd_stage(int stage, const void* x, const void* dt, const float
                            int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Bidirectional scan with untied directions: the forward and the reverse
+ * scans are two separate selective-SSM layers, each with its own input
+ * projection outputs (x, dt, B, C, z) and parameters (A, D, dt_bias), as in the
+ * paper (Section 3.2: two independent Mamba layers, eq. (4) with A_f, B_f, C_f
+ * and eq. (5) with A_b, B_b, C_b; Section 4.1 / Table 8: weights of the two
+ * directions are not tied).  Each direction keeps its own gate and output
+ * (each feeds its own output projection, outside this library):
+ *   out_f = (C_f . h_fwd + D_f * x_f) * SiLU(z_f),  h_fwd from set f, eq. (4)
+ *   out_r = (C_r . h_rev + D_r * x_r) * SiLU(z_r),  h_rev from set r, eq. (5)
+ * with the discretisation of bimamba_scan_fwd (delta = softplus(dt + dt_bias),
+ * abar = exp(delta A), input delta x B).  With both sets equal, out_f + out_r
+ * is the output of bimamba_scan_fwd.
+ * Shapes, dtypes, alignment, optional D / dt_bias and the workspace (size from
+ * bimamba_scan_fwd_workspace_bytes, used by the two passes in turn) are as for
+ * bimamba_scan_fwd; flags may only be BIMAMBA_FLAG_NO_GATE (then z_f and z_r
+ * may be NULL).  Neither output may overlap any tensor of either set, the other
+ * output or the workspace; a rejected call returns a status and enqueues nothing. */
+int bimamba_scan_fwd_untied(const void* x_f, const void* dt_f, const float* A_f, const void* B_f, const void* C_f,
+                            const float* D_f, const void* z_f, const float* dt_bias_f, void* out_f,
+                            const void* x_r, const void* dt_r, const float* A_r, const void* B_r, const void* C_r,
+                            const float* D_r, const void* z_r, const float* dt_bias_r, void* out_r,
+                            int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int io_dtype,
+                            uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of device workspace bimamba_scan_block needs for this shape; 0 when the
  * block is short enough for the single-kernel path (no workspace needed). */
 size_t bimamba_scan_block_workspace_bytes(int64_t batch, int64_t block_len, int64_t d_inner, int64_t d_state);

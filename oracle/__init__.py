@@ -9,6 +9,7 @@ from .scan import (  # noqa: F401
     reverse_scan,
     scan_block,
     scan_fwd,
+    scan_fwd_untied,
     silu,
     softplus,
 )

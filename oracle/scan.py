@@ -187,3 +187,23 @@ def scan_block(x, dt, A, B, C, D=None, z=None, dt_bias=None, h_in=None, *, gate=
     y_r = reverse_scan(delta, ubar, A, B, C)[0] if rev else None
     out = _combine(y_f if fwd else None, y_r, x, D, z, gate)
     return out, h_out
+
+
+def scan_fwd_untied(fwd_set, rev_set, *, gate=True):
+    """Bidirectional scan with untied directions.
+
+    The paper runs the two directions as two independent Mamba layers
+    (Section 3.2; eq. (4) carries A_f, B_f, C_f and eq. (5) A_b, B_b, C_b), and
+    its Table 8 (Section 4.1) lists the weights of the two directions as not
+    tied.  Each direction is then a complete layer with its own projection
+    outputs (x, dt, B, C, z) and parameters (A, D, dt_bias); each keeps its own
+    gate and output, because each feeds its own output projection before the
+    sum of eq. (6).  fwd_set and rev_set are dicts with keys x, dt, A, B, C and
+    optionally D, z, dt_bias.  Returns (out_f, out_r).
+    """
+    keys = ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")
+    f = [fwd_set.get(k) for k in keys]
+    r = [rev_set.get(k) for k in keys]
+    out_f = scan_fwd(*f, gate=gate, fwd=True, rev=False)
+    out_r = scan_fwd(*r, gate=gate, fwd=False, rev=True)
+    return out_f, out_r

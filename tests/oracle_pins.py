@@ -342,6 +342,25 @@ def pin_golden(impl):
     return worst < 1e-14, f"max abs err {worst:.3e}"
 
 
+def pin_untied(impl):
+    """P11: untied directions.  With two different parameter/input sets, out_f equals the forward
+    closed form of the first set and out_r the reverse closed form of the second (brute force); with
+    both sets equal, out_f + out_r is the tied bidirectional result (the gate distributes over the sum,
+    and each direction carries its own D x)."""
+    worst = 0.0
+    for seed in range(3):
+        rng = np.random.default_rng(300 + seed)
+        cf = _rand_case(rng, 1 + seed % 2, 6 + 3 * seed, 2, 1 + seed % 3)
+        cr = _rand_case(rng, 1 + seed % 2, 6 + 3 * seed, 2, 1 + seed % 3)
+        out_f, out_r = impl.scan_fwd_untied(cf, cr)
+        worst = max(worst, _rel(out_f, brute_force(cf, fwd=True, rev=False)))
+        worst = max(worst, _rel(out_r, brute_force(cr, fwd=False, rev=True)))
+        both = _call(impl, cf)
+        f2, r2 = impl.scan_fwd_untied(cf, cf)
+        worst = max(worst, _rel(f2 + r2, both))
+    return worst < 1e-12, f"max rel err {worst:.3e}"
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_flip,
@@ -354,4 +373,5 @@ ALL_PINS = [
     pin_channel_independence,
     pin_impulse,
     pin_golden,
+    pin_untied,
 ]

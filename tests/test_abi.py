@@ -162,3 +162,35 @@ def test_scan_block_allows_in_place_state():
     # a block past the single-kernel limit: the call then stops at the workspace size check
     assert call_block(L=100, h_out=fake(10), wsb=0) == WS  # h_out == h_in is accepted
     assert call_block(L=100, h_in=None, h_out=None, wsb=0) == WS
+
+
+def call_untied(**kw):
+    lib = _lib.load()
+    a = dict(xf=fake(0), dtf=fake(1), Af=fake(2), Bf=fake(3), Cf=fake(4), Df=fake(5), zf=fake(6), bf=fake(7),
+             of=fake(8), xr=fake(12), dtr=fake(13), Ar=fake(14), Br=fake(15), Cr=fake(16), Dr=fake(17),
+             zr=fake(18), br=fake(19), orr=fake(20), flags=0, ws=fake(9), wsb=0)
+    a.update(kw)
+    return lib.bimamba_scan_fwd_untied(a["xf"], a["dtf"], a["Af"], a["Bf"], a["Cf"], a["Df"], a["zf"], a["bf"],
+                                       a["of"], a["xr"], a["dtr"], a["Ar"], a["Br"], a["Cr"], a["Dr"], a["zr"],
+                                       a["br"], a["orr"], 1, 64, 64, 16, _lib.BIMAMBA_BF16, a["flags"], a["ws"],
+                                       a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(flags=_lib.FLAG_FWD_ONLY), INV),  # only NO_GATE is meaningful here
+    (dict(flags=_lib.FLAG_REV_ONLY), INV),
+    (dict(zf=None), INV),  # gate without z
+    (dict(zr=None), INV),
+    (dict(xr=None), INV),
+    (dict(of=fake(12)), INV),  # out_f over the reverse set's x
+    (dict(orr=fake(3)), INV),  # out_r over the forward set's B
+    (dict(orr=fake(8)), INV),  # the two outputs overlap
+    (dict(wsb=0), WS),
+])
+def test_untied_rejects(kw, want):
+    assert call_untied(**kw) == want
+
+
+def test_untied_checks_run_in_order():
+    # without the gate both z may be NULL; the call then stops at the workspace check
+    assert call_untied(zf=None, zr=None, flags=_lib.FLAG_NO_GATE) == WS

@@ -109,6 +109,22 @@ def _r(**kw):
     return lambda *a, **k: _rev_generic(*a, **k, **kw)
 
 
+def _untied_rev_uses_fwd_params(fwd_set, rev_set, *, gate=True):
+    mixed = dict(rev_set)
+    for k in ("A", "D", "dt_bias"):
+        mixed[k] = fwd_set.get(k)
+    return _untied_orig(fwd_set, mixed, gate=gate)
+
+
+def _untied_shared_gate(fwd_set, rev_set, *, gate=True):
+    mixed = dict(rev_set)
+    mixed["z"] = fwd_set.get("z")
+    return _untied_orig(fwd_set, mixed, gate=gate)
+
+
+_untied_orig = oscan.scan_fwd_untied
+
+
 MUTANTS = {
     "reverse uses abar of the next token": [("reverse_scan", _r(abar_next=True))],
     "reverse reads C of the next token": [("reverse_scan", _r(c_next=True))],
@@ -124,6 +140,8 @@ MUTANTS = {
     "sigmoid gate instead of silu": [("_combine", _combine_sigmoid)],
     "block cache returns the reverse state": [("scan_block", _scan_block_hout_rev)],
     "block reverse starts from the cache": [("scan_block", _scan_block_rev_from_hin)],
+    "untied reverse uses the forward parameters": [("scan_fwd_untied", _untied_rev_uses_fwd_params)],
+    "untied directions share the forward gate": [("scan_fwd_untied", _untied_shared_gate)],
 }
 
 
