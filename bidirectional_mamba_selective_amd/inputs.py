@@ -15,6 +15,15 @@ Recipe (shapes follow the 1.3B-layer workloads the library is measured on):
     drawn in fp32 and rounded once, round-to-nearest-even, to the I/O dtype.
 Every tensor uses its own PCG64 stream keyed by (seed, tensor id), so a
 tensor does not change when another one changes size.
+
+Mamba-2 (SSD) workloads, at the 1.3B layer's shape (120 heads of 32 channels,
+state size 128):
+  parameters (seed 0), one scalar per head:
+    A[h]       = -Uniform(1, 16)
+    dt_bias[h] = log(expm1(u_h)),  u_h = exp(Uniform(ln 1e-3, ln 1e-1))
+    D[h]       = 1
+  activations (seed 1): x, z [B, L, H*P] and B, C [B, L, N] ~ N(0, 1);
+    dt [B, L, H] ~ 0.5 * N(0, 1); rounded to the I/O dtype as above.
 """
 from __future__ import annotations
 
@@ -22,7 +31,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-_TENSOR_IDS = {"x": 1, "dt": 2, "z": 3, "B": 4, "C": 5, "dt_bias": 11, "A_jitter": 12}
+_TENSOR_IDS = {"x": 1, "dt": 2, "z": 3, "B": 4, "C": 5, "dt_bias": 11, "A_jitter": 12, "A_head": 13}
 
 
 @dataclass(frozen=True)
@@ -121,5 +130,55 @@ def make_workload_inputs(w: Workload, seed: int = 1, xz_seed: int | None = None,
     """Parameters and activations for one workload (fp32 arrays)."""
     A, D, dt_bias = make_params(w.d_inner, w.d_state, a_jitter=a_jitter)
     act = make_activations(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype, seed=seed, xz_seed=xz_seed)
+    act.update(A=A, D=D, dt_bias=dt_bias)
+    return act
+
+
+@dataclass(frozen=True)
+class SSDWorkload:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    d_state: int
+    io_dtype: str = "bf16"
+
+
+SSD_WORKLOADS = {
+    w.name: w
+    for w in (
+        SSDWorkload("ssd_layer_2k_bf16", 1, 2048, 120, 32, 128),
+        SSDWorkload("ssd_long_64k_bf16", 1, 65536, 120, 32, 128),
+    )
+}
+
+
+def make_ssd_params(nheads: int, seed: int = 0):
+    """A, D, dt_bias [nheads] as fp32 arrays (one scalar per head)."""
+    A = -_rng(seed, "A_head").uniform(1.0, 16.0, size=nheads).astype(np.float32)
+    u = np.exp(_rng(seed, "dt_bias").uniform(np.log(1e-3), np.log(1e-1), size=nheads))
+    dt_bias = np.log(np.expm1(u)).astype(np.float32)
+    D = np.ones(nheads, dtype=np.float32)
+    return np.ascontiguousarray(A), D, dt_bias
+
+
+def make_ssd_activations(batch: int, seqlen: int, nheads: int, headdim: int, d_state: int, io_dtype: str,
+                         seed: int = 1):
+    """x, z [B, L, H*P], dt [B, L, H] and B, C [B, L, N] as fp32 arrays exact in io_dtype."""
+    nc = nheads * headdim
+    return {
+        "x": normal(seed, "x", (batch, seqlen, nc), 1.0, io_dtype),
+        "dt": normal(seed, "dt", (batch, seqlen, nheads), 0.5, io_dtype),
+        "z": normal(seed, "z", (batch, seqlen, nc), 1.0, io_dtype),
+        "B": normal(seed, "B", (batch, seqlen, d_state), 1.0, io_dtype),
+        "C": normal(seed, "C", (batch, seqlen, d_state), 1.0, io_dtype),
+    }
+
+
+def make_ssd_inputs(w: SSDWorkload, seed: int = 1):
+    """Parameters and activations for one SSD workload (fp32 arrays)."""
+    A, D, dt_bias = make_ssd_params(w.nheads)
+    act = make_ssd_activations(w.batch, w.seqlen, w.nheads, w.headdim, w.d_state, w.io_dtype, seed=seed)
     act.update(A=A, D=D, dt_bias=dt_bias)
     return act

@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the bidirectional selective scan.
+"""fp64 CPU oracle for the bidirectional selective scan (per-channel S6 and per-head Mamba-2).
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, by the graft entry point's
 smoke check and by the benchmark's CPU-baseline leg, never by the library.
@@ -13,3 +13,4 @@ from .scan import (  # noqa: F401
     silu,
     softplus,
 )
+from .ssd import ssd_discretise, ssd_forward_scan, ssd_reverse_scan, ssd_scan_fwd  # noqa: F401
