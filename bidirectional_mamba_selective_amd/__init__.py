@@ -17,6 +17,9 @@ from ._lib import (  # noqa: F401
     bimamba_scan_fwd_stage,
     bimamba_scan_fwd_untied,
     bimamba_scan_fwd_workspace_bytes,
+    bimamba_ssd_fwd,
+    bimamba_ssd_fwd_stage,
+    bimamba_ssd_fwd_workspace_bytes,
     bimamba_status_string,
     bimamba_version,
     load,

@@ -37,6 +37,9 @@ EXPORTED = (
     "bimamba_scan_fwd_untied",
     "bimamba_scan_block_workspace_bytes",
     "bimamba_scan_block",
+    "bimamba_ssd_fwd_workspace_bytes",
+    "bimamba_ssd_fwd",
+    "bimamba_ssd_fwd_stage",
 )
 
 _lib = None
@@ -76,6 +79,13 @@ def load() -> ctypes.CDLL:
     lib.bimamba_scan_block.restype = ctypes.c_int
     lib.bimamba_scan_block.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                        ctypes.c_uint32, vp, sz, vp]
+    lib.bimamba_ssd_fwd_workspace_bytes.restype = sz
+    lib.bimamba_ssd_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.bimamba_ssd_fwd.restype = ctypes.c_int
+    lib.bimamba_ssd_fwd.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_int, ctypes.c_uint32, vp, sz, vp]
+    lib.bimamba_ssd_fwd_stage.restype = ctypes.c_int
+    lib.bimamba_ssd_fwd_stage.argtypes = [ctypes.c_int] + [vp] * 9 + [i64] * 5 + [ctypes.c_int, ctypes.c_uint32, vp,
+                                                                                    sz, vp]
     _lib = lib
     return lib
 
@@ -233,4 +243,66 @@ def bimamba_scan_block(x, dt, A, B, C, D=None, z=None, dt_bias=None, h_in=None, 
                                 _ptr(workspace), wbytes, _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_scan_block")
+    return out
+
+
+def bimamba_ssd_fwd_workspace_bytes(batch: int, seqlen: int, nheads: int, headdim: int, d_state: int) -> int:
+    return int(load().bimamba_ssd_fwd_workspace_bytes(batch, seqlen, nheads, headdim, d_state))
+
+
+def _ssd_common(x, dt, A, B, C, D, z, dt_bias, out):
+    torch = _torch()
+    if x.dim() != 3 or A.dim() != 1:
+        raise ValueError("x must be [batch, seqlen, nheads*headdim] and A [nheads]")
+    nb, L, nc = x.shape
+    nh = A.shape[0]
+    if nh == 0 or nc % nh:
+        raise ValueError("the channel count must be a multiple of the head count")
+    hp = nc // nh
+    ns = B.shape[-1] if B.dim() == 3 else -1
+    io = x.dtype
+    dev = x.device
+    _check(x, "x", (nb, L, nc), io, dev)
+    _check(dt, "dt", (nb, L, nh), io, dev)
+    _check(z, "z", (nb, L, nc), io, dev)
+    _check(B, "B", (nb, L, ns), io, dev)
+    _check(C, "C", (nb, L, ns), io, dev)
+    _check(A, "A", (nh,), torch.float32, dev)
+    _check(D, "D", (nh,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (nh,), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (nb, L, nc), io, dev)
+    return nb, L, nh, hp, ns, out
+
+
+def bimamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, flags: int = 0, workspace=None,
+                    stream=None):
+    """Bidirectional Mamba-2 (SSD) scan over heads; returns out ([batch, seqlen, nheads*headdim], bf16).
+    dt is [batch, seqlen, nheads]; A, D, dt_bias are [nheads] fp32."""
+    torch = _torch()
+    nb, L, nh, hp, ns, out = _ssd_common(x, dt, A, B, C, D, z, dt_bias, out)
+    lib = load()
+    need = int(lib.bimamba_ssd_fwd_workspace_bytes(nb, L, nh, hp, ns))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib.bimamba_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                             _ptr(out), nb, L, nh, hp, ns, _io_dtype(x), flags, _ptr(workspace), workspace.numel(),
+                             _stream(stream, x.device))
+    if st != BIMAMBA_OK:
+        raise BimambaError(st, "bimamba_ssd_fwd")
+    return out
+
+
+def bimamba_ssd_fwd_stage(stage: int, x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, flags: int = 0,
+                          workspace=None, stream=None):
+    """One stage (0 B/C tiles, 1 summaries, 2 carry, 3 output) of bimamba_ssd_fwd with a caller-kept workspace."""
+    nb, L, nh, hp, ns, out = _ssd_common(x, dt, A, B, C, D, z, dt_bias, out)
+    if workspace is None:
+        raise ValueError("the staged entry point needs a caller-kept workspace")
+    st = load().bimamba_ssd_fwd_stage(int(stage), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                      _ptr(dt_bias), _ptr(out), nb, L, nh, hp, ns, _io_dtype(x), flags,
+                                      _ptr(workspace), workspace.numel(), _stream(stream, x.device))
+    if st != BIMAMBA_OK:
+        raise BimambaError(st, f"bimamba_ssd_fwd_stage({stage})")
     return out

@@ -205,4 +205,75 @@ int bimamba_scan_block(const void* x, const void* dt, const float* A, const void
   return map_hip(bimamba::launch_chunked(a, p, workspace, stream));
 }
 
+// ---- Mamba-2 (SSD) heads ----
+
+static int ssd_check_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
+                           int io_dtype) {
+  namespace ssd = bimamba::ssd;
+  if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 || d_state <= 0) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (io_dtype != BIMAMBA_F32 && io_dtype != BIMAMBA_BF16) return BIMAMBA_ERR_UNSUPPORTED;
+  if (io_dtype != BIMAMBA_BF16 || headdim != ssd::kHeadDim || d_state != ssd::kState) return BIMAMBA_ERR_UNSUPPORTED;
+  // grid limits: (sub-chunks, batch) for the tiling kernel, one workgroup per (batch, chunk, head) otherwise
+  if (batch > 65535 || nheads > (1 << 20) || seqlen > INT32_MAX / 2) return BIMAMBA_ERR_UNSUPPORTED;
+  const bimamba::ssd::SsdPlan p = bimamba::ssd::make_ssd_plan(batch, seqlen, nheads);
+  if (static_cast<double>(batch) * p.nchunk * nheads > 2.0e9 ||
+      static_cast<double>(batch) * nheads * ssd::kStateFloats > 2.0e9)
+    return BIMAMBA_ERR_UNSUPPORTED;
+  return BIMAMBA_OK;
+}
+
+static int ssd_impl(int stage, const void* x, const void* dt, const float* A, const void* B, const void* C,
+                    const float* D, const void* z, const float* dt_bias, void* out, int64_t batch, int64_t seqlen,
+                    int64_t nheads, int64_t headdim, int64_t d_state, int io_dtype, uint32_t flags, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  if (stage < -1 || stage > 3) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  int s = ssd_check_shape(batch, seqlen, nheads, headdim, d_state, io_dtype);
+  if (s != BIMAMBA_OK) return s;
+  if (flags & ~kKnownFlags) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if ((flags & BIMAMBA_FLAG_FWD_ONLY) && (flags & BIMAMBA_FLAG_REV_ONLY)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (!x || !dt || !A || !B || !C || !out) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (!z && !(flags & BIMAMBA_FLAG_NO_GATE)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(B, 16) || !aligned(C, 16) || (z && !aligned(z, 16)) ||
+      !aligned(dt, 2) || !aligned(A, 4) || (D && !aligned(D, 4)) || (dt_bias && !aligned(dt_bias, 4)))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const size_t act = static_cast<size_t>(batch) * seqlen * nheads * headdim * 2;
+  const size_t dtb = static_cast<size_t>(batch) * seqlen * nheads * 2;
+  const size_t bc = static_cast<size_t>(batch) * seqlen * d_state * 2;
+  const size_t par = static_cast<size_t>(nheads) * 4;
+  const Range o = range_of(out, act);
+  if (overlap(o, range_of(x, act)) || overlap(o, range_of(dt, dtb)) || overlap(o, range_of(B, bc)) ||
+      overlap(o, range_of(C, bc)) || (z && overlap(o, range_of(z, act))) || overlap(o, range_of(A, par)) ||
+      (D && overlap(o, range_of(D, par))) || (dt_bias && overlap(o, range_of(dt_bias, par))))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const bimamba::ssd::SsdPlan p = bimamba::ssd::make_ssd_plan(batch, seqlen, nheads);
+  if (workspace_bytes < p.total) return BIMAMBA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 256)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (overlap(range_of(workspace, p.total), o)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const bimamba::ssd::SsdArgs a{x, dt, A, B, C, D, z, dt_bias, out, flags};
+  return map_hip(bimamba::ssd::launch_ssd(a, p, workspace, stream, stage));
+}
+
+size_t bimamba_ssd_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                       int64_t d_state) {
+  if (ssd_check_shape(batch, seqlen, nheads, headdim, d_state, BIMAMBA_BF16) != BIMAMBA_OK) return 0;
+  return bimamba::ssd::make_ssd_plan(batch, seqlen, nheads).total;
+}
+
+int bimamba_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                    const void* z, const float* dt_bias, void* out, int64_t batch, int64_t seqlen, int64_t nheads,
+                    int64_t headdim, int64_t d_state, int io_dtype, uint32_t flags, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  return ssd_impl(-1, x, dt, A, B, C, D, z, dt_bias, out, batch, seqlen, nheads, headdim, d_state, io_dtype, flags,
+                  workspace, workspace_bytes, stream);
+}
+
+int bimamba_ssd_fwd_stage(int stage, const void* x, const void* dt, const float* A, const void* B, const void* C,
+                          const float* D, const void* z, const float* dt_bias, void* out, int64_t batch,
+                          int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state, int io_dtype,
+                          uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (stage < 0) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  return ssd_impl(stage, x, dt, A, B, C, D, z, dt_bias, out, batch, seqlen, nheads, headdim, d_state, io_dtype,
+                  flags, workspace, workspace_bytes, stream);
+}
+
 }  // extern "C"

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "plan.h"
+#include "ssd_plan.h"
 
 namespace bimamba {
 
@@ -34,5 +35,27 @@ hipError_t launch_chunked(const ScanArgs& a, const Plan& p, void* workspace, hip
 // (64 channels, batch element), its wavefronts splitting the states; no workspace.
 hipError_t launch_block_fused(const ScanArgs& a, int64_t batch, int64_t block_len, int64_t d_inner,
                               int64_t d_state, hipStream_t stream);
+
+namespace ssd {
+
+// Mamba-2 (SSD) scan: bf16 x, dt, B, C, z, out; fp32 A, D, dt_bias per head.
+struct SsdArgs {
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* dt_bias;
+  void* out;
+  uint32_t flags;
+};
+
+// Staged chunked scan: stage 0 tiles B and C, 1 chunk summaries, 2 carry,
+// 3 output; stage < 0 launches all four.
+hipError_t launch_ssd(const SsdArgs& a, const SsdPlan& p, void* workspace, hipStream_t stream, int stage = -1);
+
+}  // namespace ssd
 
 }  // namespace bimamba

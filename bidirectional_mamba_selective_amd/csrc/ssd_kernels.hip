@@ -1,0 +1,676 @@
+// Bidirectional Mamba-2 (SSD) scan for gfx950 on the matrix cores.
+//
+// Operation: "DiffuMamba: High-Throughput Diffusion LMs with Mamba Backbone"
+// (arXiv v4), Section 3.2 eq. (4)-(6) with the Mamba-2 mixer of Section 1:
+// heads of 32 channels, a scalar transition abar = exp(delta * A[h]) per
+// (token, head), delta = softplus(dt + dt_bias[h]), B_t and C_t (state size
+// 128) shared by all heads, readout C . state + D[h] x per direction, the two
+// directions summed and gated by SiLU(z) (Appendix A Table 7; Appendix C
+// Table 12 and its caption).
+//
+// Because the transition is a scalar per head, a run of Q = 64 tokens is a
+// handful of dense products (s = running sum of delta*A inside the run, e the
+// exclusive one, S the run total, "o" = outer product over (channel, state)):
+//   intra-run   y_i += sum_j  W_ij (C_i . B_j) delta_j x_j, with
+//                 W_ij = exp(s_i - s_j) for j < i (forward), exp(e_j - e_i)
+//                 for j > i (reverse), and the number of directions on the
+//                 diagonal;
+//   readout     y_i += exp(s_i) C_i . H_in      (forward state entering the run)
+//               y_i += exp(S - e_i) C_i . G_in  (reverse state entering from the right)
+//   update      H_out = exp(S) H_in + sum_j exp(S - s_j) delta_j x_j o B_j
+//               G_out = exp(S) G_in + sum_j exp(e_j) delta_j x_j o B_j
+// The products take bf16 operands with fp32 accumulation
+// (v_mfma_f32_16x16x32_bf16); the states stay in fp32 accumulators and only
+// their operand copies are rounded to bf16.
+//
+// Passes:
+//   k_ssd_stage    per run: C into a zero-padded tile, B transposed (the state
+//                  update contracts over tokens), and C B^T in fp32 (it does
+//                  not depend on the head, so it is formed once here).
+//   k_ssd_summary  per (chunk, head), 4 wavefronts: walks the chunk's runs
+//                  right to left for its forward end state and reverse start
+//                  state from zero, the product of abar, and the reverse state
+//                  at every segment boundary (a segment is 8 runs).
+//   k_ssd_carry    chains the chunk maps across the sequence in both directions.
+//   k_ssd_output   per (chunk, head), 8 wavefronts: per segment a right-to-left
+//                  sweep (intra-run products and the reverse readout, stashed in
+//                  LDS), then a left-to-right sweep (forward readout, skip term,
+//                  gate, store).
+// Both walking kernels keep the next run's global data in flight while the
+// current run computes: every step commits the registers loaded during the
+// previous step to LDS, issues the next step's loads, then computes; one
+// wavefront forms the next run's per-token terms at the end of the step.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_math.h"
+#include "launch.h"
+#include "ssd_plan.h"
+
+namespace bimamba {
+namespace ssd {
+
+namespace {
+
+constexpr int P = static_cast<int>(kHeadDim);
+constexpr int N = static_cast<int>(kState);
+constexpr int Q = static_cast<int>(kQ);
+constexpr int SEG = static_cast<int>(kSeg);
+constexpr int kSF = static_cast<int>(kStateFloats);
+constexpr int kStageThreads = 256;
+constexpr int kSumThreads = 256;
+constexpr int kOutThreads = 512;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 raw bytes (arrays of it stay in registers)
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+
+__device__ __forceinline__ uint16_t to_bf(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// LDS tiles of bf16 rows, in 16-byte chunks of 8 elements.  Chunk c of row r is
+// stored at a swizzled chunk position so that 16 lanes reading the same chunk
+// of 16 consecutive rows hit different banks.
+__device__ __forceinline__ int sw256(int r, int c) { return r * 128 + ((c ^ (r & 15)) << 3); }      // 128-element rows
+__device__ __forceinline__ int sw128(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }  // 64-element rows
+
+__device__ __forceinline__ bf16x8 lds8(const uint16_t* s, int idx) {
+  return *reinterpret_cast<const bf16x8*>(s + idx);
+}
+
+__device__ __forceinline__ float ex(float v) { return fast_exp2(v * kLog2e); }
+
+// Per-token quantities of one run, one lane per token, in LDS rows of 64.
+enum Tok { kDl = 0, kS, kE, kWr, kWf, kRr, kRf, kTokRows };
+
+struct Args {
+  const uint16_t* x;   // [batch, L, H*P]
+  const uint16_t* dt;  // [batch, L, H]
+  const float* A;      // [H]
+  const uint16_t* B;   // [batch, L, N]
+  const uint16_t* C;
+  const float* D;      // [H] or null
+  const uint16_t* z;   // [batch, L, H*P] or null
+  const float* dt_bias;
+  uint16_t* out;
+  int64_t L, H;
+  int64_t nsub, spc, nchunk;
+  float* g;      // [batch, nsub, 4, 4, 64, 4]: C B^T per run in accumulator order
+  uint16_t* cp;  // [batch, nsub, Q, N]
+  uint16_t* bt;  // [batch, nsub, N, Q]
+  float* S;      // [batch, nchunk, H, 2, kSF]  (chunk-local, then entering states)
+  float* Pc;     // [batch, nchunk, H]
+  float* R;      // [batch, nchunk, H, spc-1, kSF]
+  float* qd;     // [batch, nchunk, H, spc]
+  int gate;
+};
+
+// (batch, chunk, head) of a workgroup.  Workgroups are dispatched round-robin
+// over the 8 XCDs; the mapping gives each XCD a contiguous range of
+// (chunk, head) items, chunk-major, so the heads of a chunk share one L2 for
+// the chunk's tiles.
+__device__ __forceinline__ void decode_item(const Args& a, int64_t& b, int64_t& c, int64_t& h) {
+  const int64_t total = static_cast<int64_t>(gridDim.x);
+  const int64_t i = blockIdx.x;
+  const int64_t item = (total % 8 == 0) ? (i % 8) * (total / 8) + i / 8 : i;
+  h = item % a.H;
+  c = (item / a.H) % a.nchunk;
+  b = item / (a.H * a.nchunk);
+}
+
+__device__ __forceinline__ uint16_t load_dt(const Args& a, int64_t b, int64_t t0, int64_t h, int l) {
+  return (t0 + l < a.L) ? a.dt[(b * a.L + t0 + l) * a.H + h] : static_cast<uint16_t>(0);
+}
+
+// One run's per-token quantities, computed by one wavefront (lane = token).
+// Tokens past the sequence end get delta = 0: no decay and no input.
+__device__ __forceinline__ void token_prep(float* tok, uint16_t dtv, bool valid, float Ah, float bias, int l) {
+  const float dl = valid ? softplus_f32(bf(dtv) + bias) : 0.0f;
+  const float av = dl * Ah;
+  float s = av;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(s, o, 64);
+    if (l >= o) s += t;
+  }
+  const float S = __shfl(s, 63, 64);
+  const float e = s - av;
+  tok[kDl * 64 + l] = dl;
+  tok[kS * 64 + l] = s;
+  tok[kE * 64 + l] = e;
+  tok[kWr * 64 + l] = ex(e) * dl;
+  tok[kWf * 64 + l] = ex(S - s) * dl;
+  tok[kRr * 64 + l] = ex(S - e);
+  tok[kRf * 64 + l] = ex(s);
+}
+
+__device__ __forceinline__ uint4 load_x_chunk(const Args& a, int64_t b, int64_t t0, int64_t h, int tid) {
+  const int j = tid >> 2, pc = tid & 3;
+  if (t0 + j >= a.L) return make_uint4(0, 0, 0, 0);
+  return *reinterpret_cast<const uint4*>(a.x + (b * a.L + t0 + j) * (a.H * P) + h * P + 8 * pc);
+}
+
+// Thread tid's x chunk (token j = tid/4, channels 8(tid%4)..+7) into LDS rows of
+// 64 tokens per channel; scaled by a per-token weight when wtok is given.
+__device__ __forceinline__ void put_xt(uint16_t* dst, uint4 v, int tid, const float* wtok, float wscale) {
+  const int j = tid >> 2, pc = tid & 3;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const float f = wtok ? wtok[j] * wscale : 1.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint16_t raw = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+    dst[sw128(8 * pc + e, j >> 3) + (j & 7)] = wtok ? to_bf(bf(raw) * f) : raw;
+  }
+}
+
+// Head states are held transposed (rows = state index n, columns = channel p)
+// in 16x16 accumulator tiles.  Tile (nb, tp) element r in lane l is
+// n = 16nb + 4(l/16) + r, p = 16tp + l%16; in memory a state is stored as
+// [nb][tp][lane][r] (nb = 0..7, tp = 0..1), 4096 floats.
+__device__ __forceinline__ int state_off(int nb, int tp, int l) { return ((nb * 2 + tp) * 64 + l) * 4; }
+
+// bf16 copy of state tile (nb, tp) into LDS rows p of 128 states (the B operand of the readout).
+__device__ __forceinline__ void tile_to_lds(const f32x4& v, uint16_t* sHs, int nb, int tp, int l) {
+  const int p = 16 * tp + (l & 15);
+  const int n0 = 16 * nb + 4 * (l >> 4);
+  const uint32_t lo = static_cast<uint32_t>(to_bf(v[0])) | (static_cast<uint32_t>(to_bf(v[1])) << 16);
+  const uint32_t hi = static_cast<uint32_t>(to_bf(v[2])) | (static_cast<uint32_t>(to_bf(v[3])) << 16);
+  *reinterpret_cast<uint2*>(sHs + sw256(p, n0 >> 3) + (n0 & 7)) = make_uint2(lo, hi);
+}
+
+// tile(nb, tp) += B^T[n-block nb] (weighted x)[tp]: contraction over the run's 64 tokens.
+__device__ __forceinline__ f32x4 tile_update(f32x4 acc, const uint16_t* sBT, const uint16_t* sXW, int nb, int tp,
+                                             int l) {
+  const int q4 = l >> 4, l16 = l & 15;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    acc = mfma(lds8(sBT, sw128(16 * nb + l16, 4 * k + q4)), lds8(sXW, sw128(16 * tp + l16, 4 * k + q4)), acc);
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// k_ssd_stage: per run, C -> zero-padded tile [Q][N], B -> B^T [N][Q], and
+// G = C B^T in fp32, stored per 16-row block of i in accumulator order:
+// g[ib][tj][lane][r] = C_i . B_j with i = 16ib + lane%16, j = 16tj + 4(lane/16) + r.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kStageThreads) void k_ssd_stage(const uint16_t* Bm, const uint16_t* Cm, float* g,
+                                                             uint16_t* cp, uint16_t* bt, int64_t L, int64_t nsub) {
+  __shared__ __attribute__((aligned(16))) uint16_t sBs[Q * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sCs[Q * N];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q4 = l >> 4, l16 = l & 15;
+  const int64_t sub = blockIdx.x, b = blockIdx.y;
+  const int64_t t0 = sub * Q;
+  const int64_t tile = (b * nsub + sub) * static_cast<int64_t>(Q * N);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ci = tid + kStageThreads * i;
+    const int j = ci >> 4, cc = ci & 15;
+    uint4 vb = make_uint4(0, 0, 0, 0), vc = make_uint4(0, 0, 0, 0);
+    if (t0 + j < L) {
+      vb = *reinterpret_cast<const uint4*>(Bm + (b * L + t0 + j) * N + 8 * cc);
+      vc = *reinterpret_cast<const uint4*>(Cm + (b * L + t0 + j) * N + 8 * cc);
+    }
+    *reinterpret_cast<uint4*>(cp + tile + j * N + 8 * cc) = vc;
+    *reinterpret_cast<uint4*>(sBs + sw256(j, cc)) = vb;
+    *reinterpret_cast<uint4*>(sCs + sw256(j, cc)) = vc;
+  }
+  __syncthreads();
+  // B^T rows n, 8 tokens per 16-byte chunk
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ci = tid + kStageThreads * i;
+    const int n = ci >> 3, jc = ci & 7;
+    uint32_t w2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j0 = 8 * jc + 2 * e;
+      w2[e] = static_cast<uint32_t>(sBs[sw256(j0, n >> 3) + (n & 7)]) |
+              (static_cast<uint32_t>(sBs[sw256(j0 + 1, n >> 3) + (n & 7)]) << 16);
+    }
+    *reinterpret_cast<uint4*>(bt + tile + n * Q + 8 * jc) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+  }
+  // C B^T: wavefront w forms the 4 tiles of row block ib = w
+  bf16x8 cf[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) cf[k] = lds8(sCs, sw256(16 * w + l16, 4 * k + q4));
+  float* gout = g + (b * nsub + sub) * static_cast<int64_t>(Q * Q);
+#pragma unroll
+  for (int tj = 0; tj < 4; ++tj) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = mfma(lds8(sBs, sw256(16 * tj + l16, 4 * k + q4)), cf[k], acc);
+    *reinterpret_cast<f32x4*>(gout + ((w * 4 + tj) * 64 + l) * 4) = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_ssd_summary: chunk-local states, 4 wavefronts; wavefront w owns the state
+// row blocks nb = 2w, 2w+1.  DIRS bit 0 = forward, bit 1 = reverse.
+// ---------------------------------------------------------------------------
+template <int DIRS>
+__global__ __launch_bounds__(kSumThreads) void k_ssd_summary(Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sBT[N * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sXWr[P * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sXWf[P * Q];
+  __shared__ __attribute__((aligned(16))) float sTok[2][kTokRows * 64];
+  constexpr bool kFwd = DIRS & 1, kRev = DIRS & 2;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  int64_t b, c, h;
+  decode_item(a, b, c, h);
+  const float Ah = a.A[h];
+  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const int64_t sub0 = c * a.spc * SEG;
+  const int64_t nvalid = a.nsub - sub0 < a.spc * SEG ? a.nsub - sub0 : a.spc * SEG;
+  const int64_t item = (b * a.nchunk + c) * a.H + h;
+  f32x4 G[2][2], F[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) G[i][tp] = F[i][tp] = zero4();
+  float tau = 1.0f;  // product of abar over the chunk's tokens to the right of the current run
+
+  // step st handles local run k = nvalid-1-st
+  u32x4 pbt[4];
+  uint4 px;
+  uint16_t pdt = 0;
+  auto issue = [&](int64_t st) {
+    const int64_t sub = sub0 + (nvalid - 1 - st);
+    const u32x4* g4 = reinterpret_cast<const u32x4*>(a.bt + (b * a.nsub + sub) * static_cast<int64_t>(Q * N));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pbt[i] = g4[tid + kSumThreads * i];
+    px = load_x_chunk(a, b, sub * Q, h, tid);
+    if (w == 0) pdt = load_dt(a, b, sub * Q, h, l);
+  };
+  issue(0);
+  if (w == 0) token_prep(sTok[0], pdt, (sub0 + nvalid - 1) * Q + l < a.L, Ah, bias, l);
+  for (int64_t st = 0; st < nvalid; ++st) {
+    const int64_t k = nvalid - 1 - st;
+    const float* tok = sTok[st & 1];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = tid + kSumThreads * i;
+      *reinterpret_cast<u32x4*>(sBT + sw128(ci >> 3, ci & 7)) = pbt[i];
+    }
+    if (kRev) put_xt(sXWr, px, tid, tok + kWr * 64, 1.0f);
+    if (kFwd) put_xt(sXWf, px, tid, tok + kWf * 64, tau);
+    __syncthreads();
+    if (st + 1 < nvalid) issue(st + 1);
+    const float eS = ex(tok[kS * 64 + 63]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) {
+        if (kRev) G[i][tp] = tile_update(G[i][tp] * eS, sBT, sXWr, 2 * w + i, tp, l);
+        if (kFwd) F[i][tp] = tile_update(F[i][tp], sBT, sXWf, 2 * w + i, tp, l);
+      }
+    tau *= eS;
+    if (kRev && k % SEG == 0 && k > 0) {
+      float* r = a.R + (item * (a.spc - 1) + (k / SEG - 1)) * kSF;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) *reinterpret_cast<f32x4*>(r + state_off(2 * w + i, tp, l)) = G[i][tp];
+      if (tid == 0) a.qd[item * a.spc + (k / SEG - 1)] = tau;
+    }
+    if (w == 0 && st + 1 < nvalid)
+      token_prep(sTok[(st + 1) & 1], pdt, (sub0 + k - 1) * Q + l < a.L, Ah, bias, l);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+      if (kFwd) *reinterpret_cast<f32x4*>(a.S + (item * 2 + 0) * kSF + state_off(2 * w + i, tp, l)) = F[i][tp];
+      if (kRev) *reinterpret_cast<f32x4*>(a.S + (item * 2 + 1) * kSF + state_off(2 * w + i, tp, l)) = G[i][tp];
+    }
+  if (tid == 0) a.Pc[item] = tau;
+}
+
+// ---------------------------------------------------------------------------
+// k_ssd_carry: chunk-local states -> states entering each chunk (in place).
+// One thread per (batch, head, state element); sequential over chunks.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_ssd_carry(float* S, const float* Pc, int64_t batch, int64_t H,
+                                                   int64_t nchunk, int dirs) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t e = gid % kSF, bh = gid / kSF;
+  if (bh >= batch * H) return;
+  const int64_t b = bh / H, h = bh % H;
+  if (dirs & 1) {
+    float acc = 0.0f;
+    for (int64_t c = 0; c < nchunk; ++c) {
+      const int64_t item = (b * nchunk + c) * H + h;
+      float* p = S + (item * 2 + 0) * kSF + e;
+      const float t = *p;
+      *p = acc;
+      acc = Pc[item] * acc + t;
+    }
+  }
+  if (dirs & 2) {
+    float acc = 0.0f;
+    for (int64_t c = nchunk - 1; c >= 0; --c) {
+      const int64_t item = (b * nchunk + c) * H + h;
+      float* p = S + (item * 2 + 1) * kSF + e;
+      const float t = *p;
+      *p = acc;
+      acc = Pc[item] * acc + t;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_ssd_output, 8 wavefronts.  Wavefront w owns output rows i in
+// [16(w/2), +16) and channels p in [16(w%2), +16) of each run, and the state
+// row block nb = w (both channel tiles).  DIRS bit 0 = forward, bit 1 = reverse.
+// The steps of a workgroup: per segment, its runs right to left (reverse
+// sweep), then left to right (forward sweep).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void decode_step(int64_t st, int64_t nvalid, int64_t& s, bool& rsweep, int64_t& k,
+                                            int64_t& nk) {
+  s = st / (2 * SEG);
+  const int64_t rem = st - s * 2 * SEG;
+  nk = nvalid - s * SEG < SEG ? nvalid - s * SEG : SEG;
+  rsweep = rem < nk;
+  k = rsweep ? nk - 1 - rem : rem - nk;
+}
+
+template <int DIRS>
+__global__ __launch_bounds__(kOutThreads, 1) void k_ssd_output(Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sC[Q * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sBT[N * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sXT[P * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sXW[P * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sHs[P * N];
+  __shared__ __attribute__((aligned(16))) float sStash[SEG * 8 * 64 * 4];
+  __shared__ __attribute__((aligned(16))) uint16_t sZO[8 * 16 * 16];
+  __shared__ __attribute__((aligned(16))) float sTok[2][kTokRows * 64];
+  constexpr bool kFwd = DIRS & 1, kRev = DIRS & 2;
+  constexpr float kDiag = (kFwd && kRev) ? 2.0f : 1.0f;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q4 = l >> 4, l16 = l & 15;
+  const int ib = w >> 1, pt = w & 1;
+  int64_t b, c, h;
+  decode_item(a, b, c, h);
+  const float Ah = a.A[h];
+  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const float Dfac = a.D ? a.D[h] * kDiag : 0.0f;
+  const int64_t sub0 = c * a.spc * SEG;
+  const int64_t nvalid = a.nsub - sub0 < a.spc * SEG ? a.nsub - sub0 : a.spc * SEG;
+  const int64_t nseg_valid = (nvalid + SEG - 1) / SEG;
+  const int64_t item = (b * a.nchunk + c) * a.H + h;
+  const int64_t HP = a.H * P;
+  uint16_t* zo = sZO + w * 256;
+  const int zr = l >> 1, zh = l & 1;  // z / out row and half-row of lanes 0..31
+
+  // states: forward H and reverse G (this wavefront's row block), reverse state entering the chunk
+  f32x4 H[2], G[2], Gin[2];
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp) {
+    H[tp] = kFwd ? *reinterpret_cast<const f32x4*>(a.S + (item * 2 + 0) * kSF + state_off(w, tp, l)) : zero4();
+    Gin[tp] = kRev ? *reinterpret_cast<const f32x4*>(a.S + (item * 2 + 1) * kSF + state_off(w, tp, l)) : zero4();
+    G[tp] = zero4();
+  }
+
+  // registers loaded one step ahead
+  u32x4 pc[2], pbt[2];
+  uint4 px, pz;
+  f32x4 pg[4], pr[2];
+  float pq = 0.0f;
+  uint16_t pdt = 0;
+  const int64_t nsteps = 2 * nvalid;
+  auto issue = [&](int64_t st) {
+    int64_t s, k, nk;
+    bool rs;
+    decode_step(st, nvalid, s, rs, k, nk);
+    const int64_t sub = sub0 + s * SEG + k, t0 = sub * Q;
+    const int64_t tile = (b * a.nsub + sub) * static_cast<int64_t>(Q * N);
+    if (rs ? kRev : kFwd) {
+      const u32x4* c4 = reinterpret_cast<const u32x4*>(a.cp + tile);
+      const u32x4* b4 = reinterpret_cast<const u32x4*>(a.bt + tile);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        pc[i] = c4[tid + kOutThreads * i];
+        pbt[i] = b4[tid + kOutThreads * i];
+      }
+    }
+    if (tid < 256) px = load_x_chunk(a, b, t0, h, tid);
+    if (rs) {
+      const float* g = a.g + (b * a.nsub + sub) * static_cast<int64_t>(Q * Q);
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) pg[tj] = *reinterpret_cast<const f32x4*>(g + ((ib * 4 + tj) * 64 + l) * 4);
+      if (kRev && k == nk - 1 && s < nseg_valid - 1) {
+        const float* r = a.R + (item * (a.spc - 1) + s) * kSF;
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) pr[tp] = *reinterpret_cast<const f32x4*>(r + state_off(w, tp, l));
+        pq = a.qd[item * a.spc + s];
+      }
+    } else if (a.gate && l < 32) {
+      const int64_t tz = t0 + 16 * ib + zr;
+      pz = tz < a.L ? *reinterpret_cast<const uint4*>(a.z + (b * a.L + tz) * HP + h * P + 16 * pt + 8 * zh)
+                    : make_uint4(0, 0, 0, 0);
+    }
+    if (w == 0) pdt = load_dt(a, b, t0, h, l);
+  };
+  issue(0);
+  if (w == 0) {
+    int64_t s0, k0, nk0;
+    bool rs0;
+    decode_step(0, nvalid, s0, rs0, k0, nk0);
+    token_prep(sTok[0], pdt, (sub0 + s0 * SEG + k0) * Q + l < a.L, Ah, bias, l);
+  }
+
+  for (int64_t st = 0; st < nsteps; ++st) {
+    int64_t s, k, nk;
+    bool rs;
+    decode_step(st, nvalid, s, rs, k, nk);
+    const int64_t t0 = (sub0 + s * SEG + k) * Q;
+    const float* tok = sTok[st & 1];
+    const bool dir_on = rs ? kRev : kFwd;
+    f32x4 gcur[4];
+    __syncthreads();
+    // ---- commit the prefetched registers ----
+    if (dir_on) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ci = tid + kOutThreads * i;
+        *reinterpret_cast<u32x4*>(sC + sw256(ci >> 4, ci & 15)) = pc[i];
+        *reinterpret_cast<u32x4*>(sBT + sw128(ci >> 3, ci & 7)) = pbt[i];
+      }
+    }
+    if (tid < 256) {
+      put_xt(sXT, px, tid, nullptr, 1.0f);
+      if (dir_on) put_xt(sXW, px, tid, tok + (rs ? kWr : kWf) * 64, 1.0f);
+    }
+    if (rs) {
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) gcur[tj] = pg[tj];
+      if (kRev) {
+        if (k == nk - 1) {
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp) G[tp] = (s < nseg_valid - 1) ? pr[tp] + pq * Gin[tp] : Gin[tp];
+        }
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) tile_to_lds(G[tp], sHs, w, tp, l);
+      }
+    } else {
+      if (a.gate && l < 32) *reinterpret_cast<uint4*>(zo + zr * 16 + 8 * zh) = pz;
+      if (kFwd) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) tile_to_lds(H[tp], sHs, w, tp, l);
+      }
+    }
+    __syncthreads();
+    if (st + 1 < nsteps) issue(st + 1);
+
+    // ---- compute ----
+    const float eS = ex(tok[kS * 64 + 63]);
+    f32x4 y;
+    if (rs) {
+      // W = mask o (C B^T) o delta_j, rows i = 16ib + l16 as the A operand (k-slots permuted to match the
+      // accumulator layout: slot e < 4 -> j = 32k2 + 4q4 + e, slot e >= 4 -> j = 32k2 + 16 + 4q4 + e - 4)
+      const int i = 16 * ib + l16;
+      const float si = tok[kS * 64 + i], ei = tok[kE * 64 + i];
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) {
+        const int j0 = 16 * tj + 4 * q4;
+        const f32x4 sj = *reinterpret_cast<const f32x4*>(tok + kS * 64 + j0);
+        const f32x4 ej = *reinterpret_cast<const f32x4*>(tok + kE * 64 + j0);
+        const f32x4 dj = *reinterpret_cast<const f32x4*>(tok + kDl * 64 + j0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = j0 + r;
+          float m;
+          if (j < i) m = kFwd ? ex(si - sj[r]) : 0.0f;
+          else if (j > i) m = kRev ? ex(ej[r] - ei) : 0.0f;
+          else m = kDiag;
+          gcur[tj][r] *= m * dj[r];
+        }
+      }
+      y = zero4();
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        bf16x8 wa;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          wa[r] = static_cast<__bf16>(gcur[2 * k2][r]);
+          wa[4 + r] = static_cast<__bf16>(gcur[2 * k2 + 1][r]);
+        }
+        const int p = 16 * pt + l16;
+        const int jlo = 32 * k2 + 4 * q4;
+        const uint2 lo = *reinterpret_cast<const uint2*>(sXT + sw128(p, jlo >> 3) + (jlo & 7));
+        const uint2 hi = *reinterpret_cast<const uint2*>(sXT + sw128(p, (jlo + 16) >> 3) + (jlo & 7));
+        y = mfma(wa, __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), y);
+      }
+      if (kRev) {
+        f32x4 yr = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          yr = mfma(lds8(sC, sw256(16 * ib + l16, 4 * kk + q4)), lds8(sHs, sw256(16 * pt + l16, 4 * kk + q4)), yr);
+        const f32x4 rr = *reinterpret_cast<const f32x4*>(tok + kRr * 64 + 16 * ib + 4 * q4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] += rr[r] * yr[r];
+      }
+      *reinterpret_cast<f32x4*>(sStash + ((k * 8 + w) * 64 + l) * 4) = y;
+      if (kRev) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) G[tp] = tile_update(G[tp] * eS, sBT, sXW, w, tp, l);
+      }
+    } else {
+      y = *reinterpret_cast<const f32x4*>(sStash + ((k * 8 + w) * 64 + l) * 4);
+      if (kFwd) {
+        f32x4 yf = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          yf = mfma(lds8(sC, sw256(16 * ib + l16, 4 * kk + q4)), lds8(sHs, sw256(16 * pt + l16, 4 * kk + q4)), yf);
+        const f32x4 rf = *reinterpret_cast<const f32x4*>(tok + kRf * 64 + 16 * ib + 4 * q4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] += rf[r] * yf[r];
+      }
+      // skip term and gate; the wavefront's 16 x 16 tile leaves through LDS as 16-byte rows
+      const int p = 16 * pt + l16;
+      const int i0 = 16 * ib + 4 * q4;
+      const uint2 xv = *reinterpret_cast<const uint2*>(sXT + sw128(p, i0 >> 3) + (i0 & 7));
+      const float xs[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xffff0000u),
+                           __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xffff0000u)};
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        o[r] = y[r] + Dfac * xs[r];
+        if (a.gate) o[r] *= silu_f32(bf(zo[(4 * q4 + r) * 16 + l16]));
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bf16_t ob;
+        from_f32(o[r], &ob);
+        zo[(4 * q4 + r) * 16 + l16] = ob.bits;
+      }
+      if (l < 32) {
+        const int64_t tz = t0 + 16 * ib + zr;
+        if (tz < a.L)
+          *reinterpret_cast<uint4*>(a.out + (b * a.L + tz) * HP + h * P + 16 * pt + 8 * zh) =
+              *reinterpret_cast<const uint4*>(zo + zr * 16 + 8 * zh);
+      }
+      if (kFwd) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) H[tp] = tile_update(H[tp] * eS, sBT, sXW, w, tp, l);
+      }
+    }
+    // per-token terms of the next step
+    if (w == 0 && st + 1 < nsteps) {
+      int64_t s1, k1, nk1;
+      bool rs1;
+      decode_step(st + 1, nvalid, s1, rs1, k1, nk1);
+      token_prep(sTok[(st + 1) & 1], pdt, (sub0 + s1 * SEG + k1) * Q + l < a.L, Ah, bias, l);
+    }
+  }
+}
+
+template <int DIRS>
+hipError_t launch_dirs(const Args& a, int64_t batch, hipStream_t stream, int stage) {
+  const unsigned groups = static_cast<unsigned>(batch * a.nchunk * a.H);
+  if (stage < 0 || stage == 1) {
+    hipLaunchKernelGGL(k_ssd_summary<DIRS>, dim3(groups), dim3(kSumThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage < 0 || stage == 2) {
+    const int64_t threads = batch * a.H * kSF;
+    hipLaunchKernelGGL(k_ssd_carry, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream, a.S,
+                       a.Pc, batch, a.H, a.nchunk, DIRS);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage < 0 || stage == 3) {
+    hipLaunchKernelGGL(k_ssd_output<DIRS>, dim3(groups), dim3(kOutThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_ssd(const SsdArgs& in, const SsdPlan& p, void* workspace, hipStream_t stream, int stage) {
+  char* ws = static_cast<char*>(workspace);
+  Args a{};
+  a.x = static_cast<const uint16_t*>(in.x);
+  a.dt = static_cast<const uint16_t*>(in.dt);
+  a.A = in.A;
+  a.B = static_cast<const uint16_t*>(in.B);
+  a.C = static_cast<const uint16_t*>(in.C);
+  a.D = in.D;
+  a.z = static_cast<const uint16_t*>(in.z);
+  a.dt_bias = in.dt_bias;
+  a.out = static_cast<uint16_t*>(in.out);
+  a.L = p.seqlen;
+  a.H = p.nheads;
+  a.nsub = p.nsub;
+  a.spc = p.spc;
+  a.nchunk = p.nchunk;
+  a.g = reinterpret_cast<float*>(ws + p.off_g);
+  a.cp = reinterpret_cast<uint16_t*>(ws + p.off_cp);
+  a.bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
+  a.S = reinterpret_cast<float*>(ws + p.off_s);
+  a.Pc = reinterpret_cast<float*>(ws + p.off_p);
+  a.R = reinterpret_cast<float*>(ws + p.off_r);
+  a.qd = reinterpret_cast<float*>(ws + p.off_q);
+  a.gate = (in.flags & kNoGate) ? 0 : 1;
+  if (stage < 0 || stage == 0) {
+    hipLaunchKernelGGL(k_ssd_stage, dim3(static_cast<unsigned>(p.nsub), static_cast<unsigned>(p.batch)),
+                       dim3(kStageThreads), 0, stream, a.B, a.C, a.g, a.cp, a.bt, p.seqlen, p.nsub);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (in.flags & kFwdOnly) return launch_dirs<1>(a, p.batch, stream, stage);
+  if (in.flags & kRevOnly) return launch_dirs<2>(a, p.batch, stream, stage);
+  return launch_dirs<3>(a, p.batch, stream, stage);
+}
+
+}  // namespace ssd
+}  // namespace bimamba

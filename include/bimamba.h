@@ -152,6 +152,45 @@ int bimamba_scan_block(const void* x, const void* dt, const float* A, const void
                        int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* ---- Mamba-2 (SSD) heads ------------------------------------------------
+ * The mixer the paper actually runs is a bidirectional Mamba-2 layer (Section
+ * 1; Appendix A Table 7: SSM head size 32 and state size 128; Appendix C
+ * Table 12 and its caption: d_inner = 3840, d_state = 128, a per-head bias on
+ * Delta).  Channels form nheads heads of headdim channels (channel c = h *
+ * headdim + p); the transition is one scalar per (token, head):
+ *   delta[t,h] = softplus(dt[t,h] + dt_bias[h]),  abar = exp(delta[t,h] * A[h])
+ *   H_fwd[t]   = abar * H_fwd[t-1] + delta[t,h] * x[t,h,:] (outer) B[t,:]   (H_fwd[-1] = 0)
+ *   H_rev[t]   = abar * H_rev[t+1] + delta[t,h] * x[t,h,:] (outer) B[t,:]   (H_rev[L]  = 0)
+ *   y_dir[t,c] = sum_n C[t,n] * H_dir[t,h,p,n] + D[h] * x[t,c]
+ *   out[t,c]   = (y_fwd + y_rev) * z * sigmoid(z)
+ * (Section 3.2 eq. (4)-(6) with Mamba-2's scalar-per-head transition; B_t and
+ * C_t are shared by all heads.)  The products inside each 64-token run run on
+ * the matrix cores with bf16 operands and fp32 accumulation; every state is
+ * carried in fp32.
+ * Layouts: x, z, out [batch, seqlen, nheads * headdim]; dt [batch, seqlen,
+ * nheads]; B, C [batch, seqlen, d_state]; A, D, dt_bias [nheads] fp32.
+ * Supported: io_dtype BIMAMBA_BF16, headdim 32, d_state 128, any nheads >= 1,
+ * seqlen >= 1, batch >= 1 (others return BIMAMBA_ERR_UNSUPPORTED).  x, z, out,
+ * B and C must be 16-byte aligned, dt 2-byte aligned, A, D, dt_bias 4-byte
+ * aligned.  Flags, D == NULL, dt_bias == NULL, z == NULL, ownership,
+ * asynchrony and the no-overlap rules are as for bimamba_scan_fwd. */
+size_t bimamba_ssd_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                       int64_t d_state);
+
+int bimamba_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                    const float* D, const void* z, const float* dt_bias, void* out,
+                    int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
+                    int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One stage of bimamba_ssd_fwd, for per-kernel timing: 0 tiles B and C, 1 the
+ * chunk summaries, 2 the carry across chunks, 3 the output pass.  Running 0..3
+ * in order with the same workspace equals one bimamba_ssd_fwd call. */
+int bimamba_ssd_fwd_stage(int stage, const void* x, const void* dt, const float* A, const void* B, const void* C,
+                          const float* D, const void* z, const float* dt_bias, void* out,
+                          int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
+                          int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

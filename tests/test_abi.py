@@ -194,3 +194,69 @@ def test_untied_rejects(kw, want):
 def test_untied_checks_run_in_order():
     # without the gate both z may be NULL; the call then stops at the workspace check
     assert call_untied(zf=None, zr=None, flags=_lib.FLAG_NO_GATE) == WS
+
+
+def call_ssd(stage=None, **kw):
+    lib = _lib.load()
+    a = dict(x=fake(0), dt=fake(1), A=fake(2), B=fake(3), C=fake(4), D=fake(5), z=fake(6), dt_bias=fake(7),
+             out=fake(8), batch=1, L=640, h=4, p=32, n=128, io=_lib.BIMAMBA_BF16, flags=0, ws=fake(9), wsb=0)
+    a.update(kw)
+    args = (a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["dt_bias"], a["out"], a["batch"], a["L"],
+            a["h"], a["p"], a["n"], a["io"], a["flags"], a["ws"], a["wsb"], None)
+    if stage is None:
+        return lib.bimamba_ssd_fwd(*args)
+    return lib.bimamba_ssd_fwd_stage(stage, *args)
+
+
+def test_ssd_workspace_size():
+    f = _lib.bimamba_ssd_fwd_workspace_bytes
+    sizes = [f(1, L, 120, 32, 128) for L in (1, 64, 65, 512, 2048, 65536)]
+    assert all(s > 0 and s % 256 == 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    assert f(1, 64, 4, 64, 128) == 0  # head size other than 32
+    assert f(1, 64, 4, 32, 64) == 0  # state size other than 128
+    assert f(0, 64, 4, 32, 128) == 0
+    # the B/C tiles and the per-chunk states fit in what the plan promises for the 64K-token layer
+    assert f(1, 65536, 120, 32, 128) < 512 << 20
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), INV),
+    (dict(dt=None), INV),
+    (dict(A=None), INV),
+    (dict(B=None), INV),
+    (dict(C=None), INV),
+    (dict(out=None), INV),
+    (dict(z=None), INV),
+    (dict(flags=_lib.FLAG_FWD_ONLY | _lib.FLAG_REV_ONLY), INV),
+    (dict(flags=64), INV),
+    (dict(batch=0), INV),
+    (dict(L=0), INV),
+    (dict(h=0), INV),
+    (dict(io=_lib.BIMAMBA_F32), UNS),  # bf16 I/O only
+    (dict(io=7), UNS),
+    (dict(p=64), UNS),
+    (dict(n=16), UNS),
+    (dict(batch=70000), UNS),
+    (dict(x=fake(0, 8)), INV),  # activations need 16-byte alignment
+    (dict(B=fake(3, 2)), INV),
+    (dict(dt=fake(1, 1)), INV),
+    (dict(A=fake(2, 2)), INV),
+    (dict(out=fake(0, 64)), INV),  # out overlaps x
+    (dict(out=fake(1, 0)), INV),  # out overlaps dt
+    (dict(wsb=0), WS),
+    (dict(ws=None, wsb=1 << 40), INV),
+    (dict(ws=fake(9, 16), wsb=1 << 40), INV),
+])
+def test_ssd_rejects(kw, want):
+    assert call_ssd(**kw) == want
+
+
+def test_ssd_checks_run_in_order_and_stages_validate():
+    assert call_ssd(z=None, flags=_lib.FLAG_NO_GATE) == WS
+    assert call_ssd(D=None, dt_bias=None) == WS
+    for bad in (-1, 4, 99):
+        assert call_ssd(stage=bad) == INV
+    for st in range(4):
+        assert call_ssd(stage=st) == WS
+        assert call_ssd(stage=st, x=None) == INV
