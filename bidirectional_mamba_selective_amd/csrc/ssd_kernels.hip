@@ -23,23 +23,27 @@
 // (v_mfma_f32_16x16x32_bf16); the states stay in fp32 accumulators and only
 // their operand copies are rounded to bf16.
 //
-// Passes:
-//   k_ssd_stage    per run: C into a zero-padded tile, B transposed (the state
-//                  update contracts over tokens), and C B^T in fp32 (it does
-//                  not depend on the head, so it is formed once here).
-//   k_ssd_summary  per (chunk, head), 4 wavefronts: walks the chunk's runs
-//                  right to left for its forward end state and reverse start
-//                  state from zero, the product of abar, and the reverse state
-//                  at every segment boundary (a segment is 8 runs).
-//   k_ssd_carry    chains the chunk maps across the sequence in both directions.
-//   k_ssd_output   per (chunk, head), 8 wavefronts: per segment a right-to-left
-//                  sweep (intra-run products and the reverse readout, stashed in
-//                  LDS), then a left-to-right sweep (forward readout, skip term,
-//                  gate, store).
-// Both walking kernels keep the next run's global data in flight while the
-// current run computes: every step commits the registers loaded during the
-// previous step to LDS, issues the next step's loads, then computes; one
-// wavefront forms the next run's per-token terms at the end of the step.
+// Passes (the sequence is cut into chunks of whole runs):
+//   k_ssd_stage   per run: C into a zero-padded tile, B transposed (the state
+//                 update contracts over tokens), and C B^T in fp32 (it does not
+//                 depend on the head, so it is formed once here).
+//   k_ssd_rsweep  per (chunk, head), right to left over the runs: the
+//                 intra-run products of both directions plus the readout of
+//                 the reverse state from zero at the chunk end; this partial
+//                 output goes to `out` in bf16.  It also leaves the chunk's
+//                 forward end state and reverse start state from zero, the
+//                 product of abar over the chunk, and for every run the product
+//                 of abar over the chunk's tokens to its right.
+//   k_ssd_carry   chains the chunk maps across the sequence in both directions.
+//   k_ssd_fsweep  per (chunk, head), left to right: adds the readout of the
+//                 forward state, the readout of the reverse state entering the
+//                 chunk from the right (decayed to each token), the skip term
+//                 and the gate, and writes `out`.
+// Both sweeps keep the next run's global data in flight while the current run
+// computes: a step commits the registers loaded during the previous step to
+// LDS, issues the next step's loads, then computes; one wavefront forms the
+// next run's per-token terms at the end of the step.  Two workgroups fit on a
+// CU, so one computes while the other waits.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,11 +59,8 @@ namespace {
 constexpr int P = static_cast<int>(kHeadDim);
 constexpr int N = static_cast<int>(kState);
 constexpr int Q = static_cast<int>(kQ);
-constexpr int SEG = static_cast<int>(kSeg);
 constexpr int kSF = static_cast<int>(kStateFloats);
-constexpr int kStageThreads = 256;
-constexpr int kSumThreads = 256;
-constexpr int kOutThreads = 512;
+constexpr int kThreads = 256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -99,16 +100,15 @@ struct Args {
   const float* D;      // [H] or null
   const uint16_t* z;   // [batch, L, H*P] or null
   const float* dt_bias;
-  uint16_t* out;
+  uint16_t* out;       // [batch, L, H*P]; holds the reverse sweep's partial output between the sweeps
   int64_t L, H;
-  int64_t nsub, spc, nchunk;
-  float* g;      // [batch, nsub, 4, 4, 64, 4]: C B^T per run in accumulator order
-  uint16_t* cp;  // [batch, nsub, Q, N]
-  uint16_t* bt;  // [batch, nsub, N, Q]
-  float* S;      // [batch, nchunk, H, 2, kSF]  (chunk-local, then entering states)
-  float* Pc;     // [batch, nchunk, H]
-  float* R;      // [batch, nchunk, H, spc-1, kSF]
-  float* qd;     // [batch, nchunk, H, spc]
+  int64_t nsub, rpc, nchunk;
+  float* g;       // [batch, nsub, 4, 4, 64, 4]: C B^T per run in accumulator order
+  uint16_t* cp;   // [batch, nsub, Q, N]
+  uint16_t* bt;   // [batch, nsub, N, Q]
+  float* S;       // [batch, nchunk, H, 2, kSF]  (chunk-local, then entering states)
+  float* Pc;      // [batch, nchunk, H]
+  float* tau;     // [batch, nchunk, H, rpc]: product of abar over the chunk's tokens right of each run
   int gate;
 };
 
@@ -151,10 +151,13 @@ __device__ __forceinline__ void token_prep(float* tok, uint16_t dtv, bool valid,
   tok[kRf * 64 + l] = ex(s);
 }
 
-__device__ __forceinline__ uint4 load_x_chunk(const Args& a, int64_t b, int64_t t0, int64_t h, int tid) {
-  const int j = tid >> 2, pc = tid & 3;
+// 16 bytes of a [batch, L, H*P] tensor: token t0 + j of the run with j = q/4 and
+// channels 8(q%4)..+7 of head h; zero past the sequence end.
+__device__ __forceinline__ uint4 load_act(const uint16_t* base, const Args& a, int64_t b, int64_t t0, int64_t h,
+                                          int q) {
+  const int j = q >> 2, pc = q & 3;
   if (t0 + j >= a.L) return make_uint4(0, 0, 0, 0);
-  return *reinterpret_cast<const uint4*>(a.x + (b * a.L + t0 + j) * (a.H * P) + h * P + 8 * pc);
+  return *reinterpret_cast<const uint4*>(base + (b * a.L + t0 + j) * (a.H * P) + h * P + 8 * pc);
 }
 
 // Thread tid's x chunk (token j = tid/4, channels 8(tid%4)..+7) into LDS rows of
@@ -173,26 +176,104 @@ __device__ __forceinline__ void put_xt(uint16_t* dst, uint4 v, int tid, const fl
 // Head states are held transposed (rows = state index n, columns = channel p)
 // in 16x16 accumulator tiles.  Tile (nb, tp) element r in lane l is
 // n = 16nb + 4(l/16) + r, p = 16tp + l%16; in memory a state is stored as
-// [nb][tp][lane][r] (nb = 0..7, tp = 0..1), 4096 floats.
+// [nb][tp][lane][r] (nb = 0..7, tp = 0..1), 4096 floats.  Wavefront w of a
+// workgroup owns the row blocks nb = 2w and 2w + 1.
 __device__ __forceinline__ int state_off(int nb, int tp, int l) { return ((nb * 2 + tp) * 64 + l) * 4; }
 
-// bf16 copy of state tile (nb, tp) into LDS rows p of 128 states (the B operand of the readout).
-__device__ __forceinline__ void tile_to_lds(const f32x4& v, uint16_t* sHs, int nb, int tp, int l) {
-  const int p = 16 * tp + (l & 15);
-  const int n0 = 16 * nb + 4 * (l >> 4);
-  const uint32_t lo = static_cast<uint32_t>(to_bf(v[0])) | (static_cast<uint32_t>(to_bf(v[1])) << 16);
-  const uint32_t hi = static_cast<uint32_t>(to_bf(v[2])) | (static_cast<uint32_t>(to_bf(v[3])) << 16);
-  *reinterpret_cast<uint2*>(sHs + sw256(p, n0 >> 3) + (n0 & 7)) = make_uint2(lo, hi);
+struct State {
+  f32x4 t[2][2];  // [row block 2w + i][channel tile]
+};
+
+__device__ __forceinline__ void state_load(State& s, const float* g, int w, int l) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) s.t[i][tp] = *reinterpret_cast<const f32x4*>(g + state_off(2 * w + i, tp, l));
 }
 
-// tile(nb, tp) += B^T[n-block nb] (weighted x)[tp]: contraction over the run's 64 tokens.
-__device__ __forceinline__ f32x4 tile_update(f32x4 acc, const uint16_t* sBT, const uint16_t* sXW, int nb, int tp,
+__device__ __forceinline__ void state_store(const State& s, float* g, int w, int l) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) *reinterpret_cast<f32x4*>(g + state_off(2 * w + i, tp, l)) = s.t[i][tp];
+}
+
+__device__ __forceinline__ void state_zero(State& s) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) s.t[i][tp] = zero4();
+}
+
+// bf16 copy of the wavefront's part of a state into LDS rows p of 128 states
+// (the B operand of the readout).
+__device__ __forceinline__ void state_to_lds(const State& s, uint16_t* sHs, int w, int l) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+      const f32x4 v = s.t[i][tp];
+      const int p = 16 * tp + (l & 15);
+      const int n0 = 16 * (2 * w + i) + 4 * (l >> 4);
+      const uint32_t lo = static_cast<uint32_t>(to_bf(v[0])) | (static_cast<uint32_t>(to_bf(v[1])) << 16);
+      const uint32_t hi = static_cast<uint32_t>(to_bf(v[2])) | (static_cast<uint32_t>(to_bf(v[3])) << 16);
+      *reinterpret_cast<uint2*>(sHs + sw256(p, n0 >> 3) + (n0 & 7)) = make_uint2(lo, hi);
+    }
+}
+
+// state = scale * state + B^T (weighted x): contraction over the run's 64 tokens.
+__device__ __forceinline__ void state_update(State& s, float scale, const uint16_t* sBT, const uint16_t* sXW, int w,
                                              int l) {
   const int q4 = l >> 4, l16 = l & 15;
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
-    acc = mfma(lds8(sBT, sw128(16 * nb + l16, 4 * k + q4)), lds8(sXW, sw128(16 * tp + l16, 4 * k + q4)), acc);
-  return acc;
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) s.t[i][tp] *= scale;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    bf16x8 xb[2];
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) xb[tp] = lds8(sXW, sw128(16 * tp + l16, 4 * k + q4));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bf16x8 ab = lds8(sBT, sw128(16 * (2 * w + i) + l16, 4 * k + q4));
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) s.t[i][tp] = mfma(ab, xb[tp], s.t[i][tp]);
+    }
+  }
+}
+
+// y tiles of the wavefront (rows i = 16w + 4(l/16) + r, channels p = 16tp + l%16)
+// = C_i . state(p, :), with cf the wavefront's C rows as A operands.
+__device__ __forceinline__ void readout(f32x4 y[2], const bf16x8 cf[4], const uint16_t* sHs, int l) {
+  const int q4 = l >> 4, l16 = l & 15;
+  y[0] = y[1] = zero4();
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) y[tp] = mfma(cf[k], lds8(sHs, sw256(16 * tp + l16, 4 * k + q4)), y[tp]);
+}
+
+// The wavefront's 16 x 32 output tile goes through its LDS slot (rows of 32
+// bf16) so that each lane moves 16 contiguous bytes.
+__device__ __forceinline__ void tile_rows_to_lds(uint16_t* slot, const float v[2][4], int l) {
+  const int q4 = l >> 4, l16 = l & 15;
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      bf16_t ob;
+      from_f32(v[tp][r], &ob);
+      slot[(4 * q4 + r) * P + 16 * tp + l16] = ob.bits;
+    }
+}
+
+// The wavefront's C rows i = 16w + l%16 as readout A operands, straight from the
+// run's zero-padded C tile: operand kk holds states 32kk + 8(l/16) .. +7.
+__device__ __forceinline__ void load_cfrag(u32x4 cf[4], const uint16_t* ctile, int w, int l) {
+  const uint16_t* row = ctile + (16 * w + (l & 15)) * N + 8 * (l >> 4);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) cf[kk] = *reinterpret_cast<const u32x4*>(row + 32 * kk);
 }
 
 // ---------------------------------------------------------------------------
@@ -200,8 +281,8 @@ __device__ __forceinline__ f32x4 tile_update(f32x4 acc, const uint16_t* sBT, con
 // G = C B^T in fp32, stored per 16-row block of i in accumulator order:
 // g[ib][tj][lane][r] = C_i . B_j with i = 16ib + lane%16, j = 16tj + 4(lane/16) + r.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kStageThreads) void k_ssd_stage(const uint16_t* Bm, const uint16_t* Cm, float* g,
-                                                             uint16_t* cp, uint16_t* bt, int64_t L, int64_t nsub) {
+__global__ __launch_bounds__(kThreads) void k_ssd_stage(const uint16_t* Bm, const uint16_t* Cm, float* g,
+                                                        uint16_t* cp, uint16_t* bt, int64_t L, int64_t nsub) {
   __shared__ __attribute__((aligned(16))) uint16_t sBs[Q * N];
   __shared__ __attribute__((aligned(16))) uint16_t sCs[Q * N];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q4 = l >> 4, l16 = l & 15;
@@ -210,7 +291,7 @@ __global__ __launch_bounds__(kStageThreads) void k_ssd_stage(const uint16_t* Bm,
   const int64_t tile = (b * nsub + sub) * static_cast<int64_t>(Q * N);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int ci = tid + kStageThreads * i;
+    const int ci = tid + kThreads * i;
     const int j = ci >> 4, cc = ci & 15;
     uint4 vb = make_uint4(0, 0, 0, 0), vc = make_uint4(0, 0, 0, 0);
     if (t0 + j < L) {
@@ -225,7 +306,7 @@ __global__ __launch_bounds__(kStageThreads) void k_ssd_stage(const uint16_t* Bm,
   // B^T rows n, 8 tokens per 16-byte chunk
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int ci = tid + kStageThreads * i;
+    const int ci = tid + kThreads * i;
     const int n = ci >> 3, jc = ci & 7;
     uint32_t w2[4];
 #pragma unroll
@@ -251,85 +332,149 @@ __global__ __launch_bounds__(kStageThreads) void k_ssd_stage(const uint16_t* Bm,
 }
 
 // ---------------------------------------------------------------------------
-// k_ssd_summary: chunk-local states, 4 wavefronts; wavefront w owns the state
-// row blocks nb = 2w, 2w+1.  DIRS bit 0 = forward, bit 1 = reverse.
+// k_ssd_rsweep: right to left over a chunk's runs.  Wavefront w owns output
+// rows i in [16w, 16w+16) (both channel tiles) and state row blocks 2w, 2w+1.
+// DIRS bit 0 = forward, bit 1 = reverse.
 // ---------------------------------------------------------------------------
 template <int DIRS>
-__global__ __launch_bounds__(kSumThreads) void k_ssd_summary(Args a) {
+__global__ __launch_bounds__(kThreads, 2) void k_ssd_rsweep(Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t sBT[N * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sXT[P * Q];
   __shared__ __attribute__((aligned(16))) uint16_t sXWr[P * Q];
   __shared__ __attribute__((aligned(16))) uint16_t sXWf[P * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sHs[P * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sOut[4 * 16 * P];
   __shared__ __attribute__((aligned(16))) float sTok[2][kTokRows * 64];
   constexpr bool kFwd = DIRS & 1, kRev = DIRS & 2;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  constexpr float kDiag = (kFwd && kRev) ? 2.0f : 1.0f;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q4 = l >> 4, l16 = l & 15;
   int64_t b, c, h;
   decode_item(a, b, c, h);
   const float Ah = a.A[h];
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-  const int64_t sub0 = c * a.spc * SEG;
-  const int64_t nvalid = a.nsub - sub0 < a.spc * SEG ? a.nsub - sub0 : a.spc * SEG;
+  const int64_t sub0 = c * a.rpc;
+  const int64_t nrun = a.nsub - sub0 < a.rpc ? a.nsub - sub0 : a.rpc;
   const int64_t item = (b * a.nchunk + c) * a.H + h;
-  f32x4 G[2][2], F[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int tp = 0; tp < 2; ++tp) G[i][tp] = F[i][tp] = zero4();
+  uint16_t* slot = sOut + w * 16 * P;
+  State G, F;
+  state_zero(G);
+  state_zero(F);
   float tau = 1.0f;  // product of abar over the chunk's tokens to the right of the current run
 
-  // step st handles local run k = nvalid-1-st
-  u32x4 pbt[4];
+  // step st handles run k = nrun-1-st; its loads are issued one step ahead
+  u32x4 pc[4], pbt[4];
+  f32x4 pg[4];
   uint4 px;
   uint16_t pdt = 0;
   auto issue = [&](int64_t st) {
-    const int64_t sub = sub0 + (nvalid - 1 - st);
-    const u32x4* g4 = reinterpret_cast<const u32x4*>(a.bt + (b * a.nsub + sub) * static_cast<int64_t>(Q * N));
+    const int64_t sub = sub0 + (nrun - 1 - st);
+    const int64_t tile = (b * a.nsub + sub) * static_cast<int64_t>(Q * N);
+    const u32x4* b4 = reinterpret_cast<const u32x4*>(a.bt + tile);
+    if (kRev) load_cfrag(pc, a.cp + tile, w, l);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pbt[i] = g4[tid + kSumThreads * i];
-    px = load_x_chunk(a, b, sub * Q, h, tid);
+    for (int i = 0; i < 4; ++i) pbt[i] = b4[tid + kThreads * i];
+    const float* gg = a.g + (b * a.nsub + sub) * static_cast<int64_t>(Q * Q);
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) pg[tj] = *reinterpret_cast<const f32x4*>(gg + ((w * 4 + tj) * 64 + l) * 4);
+    px = load_act(a.x, a, b, sub * Q, h, tid);
     if (w == 0) pdt = load_dt(a, b, sub * Q, h, l);
   };
   issue(0);
-  if (w == 0) token_prep(sTok[0], pdt, (sub0 + nvalid - 1) * Q + l < a.L, Ah, bias, l);
-  for (int64_t st = 0; st < nvalid; ++st) {
-    const int64_t k = nvalid - 1 - st;
+  if (w == 0) token_prep(sTok[0], pdt, (sub0 + nrun - 1) * Q + l < a.L, Ah, bias, l);
+
+  for (int64_t st = 0; st < nrun; ++st) {
+    const int64_t k = nrun - 1 - st;
+    const int64_t t0 = (sub0 + k) * Q;
     const float* tok = sTok[st & 1];
+    f32x4 gcur[4];
+    bf16x8 cf[4];
     __syncthreads();
+    // ---- commit the prefetched registers ----
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ci = tid + kSumThreads * i;
+      const int ci = tid + kThreads * i;
       *reinterpret_cast<u32x4*>(sBT + sw128(ci >> 3, ci & 7)) = pbt[i];
+      if (kRev) cf[i] = __builtin_bit_cast(bf16x8, pc[i]);
     }
+    put_xt(sXT, px, tid, nullptr, 1.0f);
     if (kRev) put_xt(sXWr, px, tid, tok + kWr * 64, 1.0f);
     if (kFwd) put_xt(sXWf, px, tid, tok + kWf * 64, tau);
-    __syncthreads();
-    if (st + 1 < nvalid) issue(st + 1);
-    const float eS = ex(tok[kS * 64 + 63]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int tj = 0; tj < 4; ++tj) gcur[tj] = pg[tj];
+    if (kRev) state_to_lds(G, sHs, w, l);
+    __syncthreads();
+    if (st + 1 < nrun) issue(st + 1);
+
+    // ---- compute ----
+    // W = mask o (C B^T) o delta_j for rows i = 16w + l16, used as the A operand with permuted
+    // k-slots: slot e < 4 -> j = 32k2 + 4q4 + e, slot e >= 4 -> j = 32k2 + 16 + 4q4 + e - 4
+    const int i = 16 * w + l16;
+    const float si = tok[kS * 64 + i], ei = tok[kE * 64 + i];
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      const int j0 = 16 * tj + 4 * q4;
+      const f32x4 sj = *reinterpret_cast<const f32x4*>(tok + kS * 64 + j0);
+      const f32x4 ej = *reinterpret_cast<const f32x4*>(tok + kE * 64 + j0);
+      const f32x4 dj = *reinterpret_cast<const f32x4*>(tok + kDl * 64 + j0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + r;
+        float m;
+        if (j < i) m = kFwd ? ex(si - sj[r]) : 0.0f;
+        else if (j > i) m = kRev ? ex(ej[r] - ei) : 0.0f;
+        else m = kDiag;
+        gcur[tj][r] *= m * dj[r];
+      }
+    }
+    f32x4 y[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      bf16x8 wa;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        wa[r] = static_cast<__bf16>(gcur[2 * k2][r]);
+        wa[4 + r] = static_cast<__bf16>(gcur[2 * k2 + 1][r]);
+      }
+      const int jlo = 32 * k2 + 4 * q4;
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
-        if (kRev) G[i][tp] = tile_update(G[i][tp] * eS, sBT, sXWr, 2 * w + i, tp, l);
-        if (kFwd) F[i][tp] = tile_update(F[i][tp], sBT, sXWf, 2 * w + i, tp, l);
+        const int p = 16 * tp + l16;
+        const uint2 lo = *reinterpret_cast<const uint2*>(sXT + sw128(p, jlo >> 3) + (jlo & 7));
+        const uint2 hi = *reinterpret_cast<const uint2*>(sXT + sw128(p, (jlo + 16) >> 3) + (jlo & 7));
+        y[tp] = mfma(wa, __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), y[tp]);
       }
+    }
+    if (kRev) {
+      f32x4 yr[2];
+      readout(yr, cf, sHs, l);
+      const f32x4 rr = *reinterpret_cast<const f32x4*>(tok + kRr * 64 + 16 * w + 4 * q4);
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[tp][r] += rr[r] * yr[tp][r];
+    }
+    // the partial output of the run (bf16) into out
+    {
+      float v[2][4];
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[tp][r] = y[tp][r];
+      tile_rows_to_lds(slot, v, l);
+      const int64_t t = t0 + 16 * w + (l >> 2);
+      if (t < a.L)
+        *reinterpret_cast<uint4*>(a.out + (b * a.L + t) * (a.H * P) + h * P + 8 * (l & 3)) =
+            *reinterpret_cast<const uint4*>(slot + (l >> 2) * P + 8 * (l & 3));
+    }
+    const float eS = ex(tok[kS * 64 + 63]);
+    if (kRev) state_update(G, eS, sBT, sXWr, w, l);
+    if (kFwd) state_update(F, 1.0f, sBT, sXWf, w, l);
+    if (tid == 0) a.tau[item * a.rpc + k] = tau;
     tau *= eS;
-    if (kRev && k % SEG == 0 && k > 0) {
-      float* r = a.R + (item * (a.spc - 1) + (k / SEG - 1)) * kSF;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp) *reinterpret_cast<f32x4*>(r + state_off(2 * w + i, tp, l)) = G[i][tp];
-      if (tid == 0) a.qd[item * a.spc + (k / SEG - 1)] = tau;
-    }
-    if (w == 0 && st + 1 < nvalid)
-      token_prep(sTok[(st + 1) & 1], pdt, (sub0 + k - 1) * Q + l < a.L, Ah, bias, l);
+    if (w == 0 && st + 1 < nrun) token_prep(sTok[(st + 1) & 1], pdt, (sub0 + k - 1) * Q + l < a.L, Ah, bias, l);
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int tp = 0; tp < 2; ++tp) {
-      if (kFwd) *reinterpret_cast<f32x4*>(a.S + (item * 2 + 0) * kSF + state_off(2 * w + i, tp, l)) = F[i][tp];
-      if (kRev) *reinterpret_cast<f32x4*>(a.S + (item * 2 + 1) * kSF + state_off(2 * w + i, tp, l)) = G[i][tp];
-    }
+  if (kFwd) state_store(F, a.S + (item * 2 + 0) * kSF, w, l);
+  if (kRev) state_store(G, a.S + (item * 2 + 1) * kSF, w, l);
   if (tid == 0) a.Pc[item] = tau;
 }
 
@@ -366,248 +511,137 @@ __global__ __launch_bounds__(256) void k_ssd_carry(float* S, const float* Pc, in
 }
 
 // ---------------------------------------------------------------------------
-// k_ssd_output, 8 wavefronts.  Wavefront w owns output rows i in
-// [16(w/2), +16) and channels p in [16(w%2), +16) of each run, and the state
-// row block nb = w (both channel tiles).  DIRS bit 0 = forward, bit 1 = reverse.
-// The steps of a workgroup: per segment, its runs right to left (reverse
-// sweep), then left to right (forward sweep).
+// k_ssd_fsweep: left to right over a chunk's runs; same wavefront roles as the
+// reverse sweep.  DIRS bit 0 = forward, bit 1 = reverse.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void decode_step(int64_t st, int64_t nvalid, int64_t& s, bool& rsweep, int64_t& k,
-                                            int64_t& nk) {
-  s = st / (2 * SEG);
-  const int64_t rem = st - s * 2 * SEG;
-  nk = nvalid - s * SEG < SEG ? nvalid - s * SEG : SEG;
-  rsweep = rem < nk;
-  k = rsweep ? nk - 1 - rem : rem - nk;
-}
-
 template <int DIRS>
-__global__ __launch_bounds__(kOutThreads, 1) void k_ssd_output(Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sC[Q * N];
+__global__ __launch_bounds__(kThreads, 2) void k_ssd_fsweep(Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t sBT[N * Q];
   __shared__ __attribute__((aligned(16))) uint16_t sXT[P * Q];
   __shared__ __attribute__((aligned(16))) uint16_t sXW[P * Q];
   __shared__ __attribute__((aligned(16))) uint16_t sHs[P * N];
-  __shared__ __attribute__((aligned(16))) float sStash[SEG * 8 * 64 * 4];
-  __shared__ __attribute__((aligned(16))) uint16_t sZO[8 * 16 * 16];
+  __shared__ __attribute__((aligned(16))) uint16_t sHg[P * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sZ[4 * 16 * P];
+  __shared__ __attribute__((aligned(16))) uint16_t sY[4 * 16 * P];
   __shared__ __attribute__((aligned(16))) float sTok[2][kTokRows * 64];
   constexpr bool kFwd = DIRS & 1, kRev = DIRS & 2;
   constexpr float kDiag = (kFwd && kRev) ? 2.0f : 1.0f;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q4 = l >> 4, l16 = l & 15;
-  const int ib = w >> 1, pt = w & 1;
   int64_t b, c, h;
   decode_item(a, b, c, h);
   const float Ah = a.A[h];
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
   const float Dfac = a.D ? a.D[h] * kDiag : 0.0f;
-  const int64_t sub0 = c * a.spc * SEG;
-  const int64_t nvalid = a.nsub - sub0 < a.spc * SEG ? a.nsub - sub0 : a.spc * SEG;
-  const int64_t nseg_valid = (nvalid + SEG - 1) / SEG;
+  const int64_t sub0 = c * a.rpc;
+  const int64_t nrun = a.nsub - sub0 < a.rpc ? a.nsub - sub0 : a.rpc;
   const int64_t item = (b * a.nchunk + c) * a.H + h;
   const int64_t HP = a.H * P;
-  uint16_t* zo = sZO + w * 256;
-  const int zr = l >> 1, zh = l & 1;  // z / out row and half-row of lanes 0..31
-
-  // states: forward H and reverse G (this wavefront's row block), reverse state entering the chunk
-  f32x4 H[2], G[2], Gin[2];
-#pragma unroll
-  for (int tp = 0; tp < 2; ++tp) {
-    H[tp] = kFwd ? *reinterpret_cast<const f32x4*>(a.S + (item * 2 + 0) * kSF + state_off(w, tp, l)) : zero4();
-    Gin[tp] = kRev ? *reinterpret_cast<const f32x4*>(a.S + (item * 2 + 1) * kSF + state_off(w, tp, l)) : zero4();
-    G[tp] = zero4();
+  uint16_t* zslot = sZ + w * 16 * P;
+  uint16_t* yslot = sY + w * 16 * P;
+  State H;
+  if (kFwd) state_load(H, a.S + (item * 2 + 0) * kSF, w, l);
+  if (kRev) {
+    // the reverse state entering the chunk from the right is fixed for the whole chunk
+    State Gin;
+    state_load(Gin, a.S + (item * 2 + 1) * kSF, w, l);
+    state_to_lds(Gin, sHg, w, l);
   }
 
-  // registers loaded one step ahead
-  u32x4 pc[2], pbt[2];
-  uint4 px, pz;
-  f32x4 pg[4], pr[2];
-  float pq = 0.0f;
+  u32x4 pc[4], pbt[4];
+  uint4 px, pz, py;
+  float ptau = 0.0f;
   uint16_t pdt = 0;
-  const int64_t nsteps = 2 * nvalid;
-  auto issue = [&](int64_t st) {
-    int64_t s, k, nk;
-    bool rs;
-    decode_step(st, nvalid, s, rs, k, nk);
-    const int64_t sub = sub0 + s * SEG + k, t0 = sub * Q;
+  auto issue = [&](int64_t k) {
+    const int64_t sub = sub0 + k, t0 = sub * Q;
     const int64_t tile = (b * a.nsub + sub) * static_cast<int64_t>(Q * N);
-    if (rs ? kRev : kFwd) {
-      const u32x4* c4 = reinterpret_cast<const u32x4*>(a.cp + tile);
-      const u32x4* b4 = reinterpret_cast<const u32x4*>(a.bt + tile);
+    const u32x4* b4 = reinterpret_cast<const u32x4*>(a.bt + tile);
+    load_cfrag(pc, a.cp + tile, w, l);
+    if (kFwd) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        pc[i] = c4[tid + kOutThreads * i];
-        pbt[i] = b4[tid + kOutThreads * i];
-      }
+      for (int i = 0; i < 4; ++i) pbt[i] = b4[tid + kThreads * i];
     }
-    if (tid < 256) px = load_x_chunk(a, b, t0, h, tid);
-    if (rs) {
-      const float* g = a.g + (b * a.nsub + sub) * static_cast<int64_t>(Q * Q);
-#pragma unroll
-      for (int tj = 0; tj < 4; ++tj) pg[tj] = *reinterpret_cast<const f32x4*>(g + ((ib * 4 + tj) * 64 + l) * 4);
-      if (kRev && k == nk - 1 && s < nseg_valid - 1) {
-        const float* r = a.R + (item * (a.spc - 1) + s) * kSF;
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp) pr[tp] = *reinterpret_cast<const f32x4*>(r + state_off(w, tp, l));
-        pq = a.qd[item * a.spc + s];
-      }
-    } else if (a.gate && l < 32) {
-      const int64_t tz = t0 + 16 * ib + zr;
-      pz = tz < a.L ? *reinterpret_cast<const uint4*>(a.z + (b * a.L + tz) * HP + h * P + 16 * pt + 8 * zh)
-                    : make_uint4(0, 0, 0, 0);
-    }
+    px = load_act(a.x, a, b, t0, h, tid);
+    const int q = 64 * w + l;  // this wavefront's rows 16w..16w+15 (q/4 = 16w + l/4)
+    py = load_act(a.out, a, b, t0, h, q);
+    if (a.gate) pz = load_act(a.z, a, b, t0, h, q);
+    if (kRev) ptau = a.tau[item * a.rpc + k];
     if (w == 0) pdt = load_dt(a, b, t0, h, l);
   };
   issue(0);
-  if (w == 0) {
-    int64_t s0, k0, nk0;
-    bool rs0;
-    decode_step(0, nvalid, s0, rs0, k0, nk0);
-    token_prep(sTok[0], pdt, (sub0 + s0 * SEG + k0) * Q + l < a.L, Ah, bias, l);
-  }
+  if (w == 0) token_prep(sTok[0], pdt, sub0 * Q + l < a.L, Ah, bias, l);
 
-  for (int64_t st = 0; st < nsteps; ++st) {
-    int64_t s, k, nk;
-    bool rs;
-    decode_step(st, nvalid, s, rs, k, nk);
-    const int64_t t0 = (sub0 + s * SEG + k) * Q;
-    const float* tok = sTok[st & 1];
-    const bool dir_on = rs ? kRev : kFwd;
-    f32x4 gcur[4];
+  for (int64_t k = 0; k < nrun; ++k) {
+    const int64_t t0 = (sub0 + k) * Q;
+    const float* tok = sTok[k & 1];
+    bf16x8 cf[4];
     __syncthreads();
     // ---- commit the prefetched registers ----
-    if (dir_on) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ci = tid + kOutThreads * i;
-        *reinterpret_cast<u32x4*>(sC + sw256(ci >> 4, ci & 15)) = pc[i];
-        *reinterpret_cast<u32x4*>(sBT + sw128(ci >> 3, ci & 7)) = pbt[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int ci = tid + kThreads * i;
+      if (kFwd) *reinterpret_cast<u32x4*>(sBT + sw128(ci >> 3, ci & 7)) = pbt[i];
+      cf[i] = __builtin_bit_cast(bf16x8, pc[i]);
     }
-    if (tid < 256) {
-      put_xt(sXT, px, tid, nullptr, 1.0f);
-      if (dir_on) put_xt(sXW, px, tid, tok + (rs ? kWr : kWf) * 64, 1.0f);
-    }
-    if (rs) {
-#pragma unroll
-      for (int tj = 0; tj < 4; ++tj) gcur[tj] = pg[tj];
-      if (kRev) {
-        if (k == nk - 1) {
-#pragma unroll
-          for (int tp = 0; tp < 2; ++tp) G[tp] = (s < nseg_valid - 1) ? pr[tp] + pq * Gin[tp] : Gin[tp];
-        }
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp) tile_to_lds(G[tp], sHs, w, tp, l);
-      }
-    } else {
-      if (a.gate && l < 32) *reinterpret_cast<uint4*>(zo + zr * 16 + 8 * zh) = pz;
-      if (kFwd) {
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp) tile_to_lds(H[tp], sHs, w, tp, l);
-      }
-    }
+    put_xt(sXT, px, tid, nullptr, 1.0f);
+    if (kFwd) put_xt(sXW, px, tid, tok + kWf * 64, 1.0f);
+    *reinterpret_cast<uint4*>(yslot + (l >> 2) * P + 8 * (l & 3)) = py;
+    if (a.gate) *reinterpret_cast<uint4*>(zslot + (l >> 2) * P + 8 * (l & 3)) = pz;
+    const float tau_run = ptau;
+    if (kFwd) state_to_lds(H, sHs, w, l);
     __syncthreads();
-    if (st + 1 < nsteps) issue(st + 1);
+    if (k + 1 < nrun) issue(k + 1);
 
     // ---- compute ----
-    const float eS = ex(tok[kS * 64 + 63]);
-    f32x4 y;
-    if (rs) {
-      // W = mask o (C B^T) o delta_j, rows i = 16ib + l16 as the A operand (k-slots permuted to match the
-      // accumulator layout: slot e < 4 -> j = 32k2 + 4q4 + e, slot e >= 4 -> j = 32k2 + 16 + 4q4 + e - 4)
-      const int i = 16 * ib + l16;
-      const float si = tok[kS * 64 + i], ei = tok[kE * 64 + i];
+    f32x4 y[2];
 #pragma unroll
-      for (int tj = 0; tj < 4; ++tj) {
-        const int j0 = 16 * tj + 4 * q4;
-        const f32x4 sj = *reinterpret_cast<const f32x4*>(tok + kS * 64 + j0);
-        const f32x4 ej = *reinterpret_cast<const f32x4*>(tok + kE * 64 + j0);
-        const f32x4 dj = *reinterpret_cast<const f32x4*>(tok + kDl * 64 + j0);
+    for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = j0 + r;
-          float m;
-          if (j < i) m = kFwd ? ex(si - sj[r]) : 0.0f;
-          else if (j > i) m = kRev ? ex(ej[r] - ei) : 0.0f;
-          else m = kDiag;
-          gcur[tj][r] *= m * dj[r];
-        }
-      }
-      y = zero4();
+      for (int r = 0; r < 4; ++r) y[tp][r] = bf(yslot[(4 * q4 + r) * P + 16 * tp + l16]);
+    if (kFwd) {
+      f32x4 yf[2];
+      readout(yf, cf, sHs, l);
+      const f32x4 rf = *reinterpret_cast<const f32x4*>(tok + kRf * 64 + 16 * w + 4 * q4);
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        bf16x8 wa;
+      for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          wa[r] = static_cast<__bf16>(gcur[2 * k2][r]);
-          wa[4 + r] = static_cast<__bf16>(gcur[2 * k2 + 1][r]);
-        }
-        const int p = 16 * pt + l16;
-        const int jlo = 32 * k2 + 4 * q4;
-        const uint2 lo = *reinterpret_cast<const uint2*>(sXT + sw128(p, jlo >> 3) + (jlo & 7));
-        const uint2 hi = *reinterpret_cast<const uint2*>(sXT + sw128(p, (jlo + 16) >> 3) + (jlo & 7));
-        y = mfma(wa, __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), y);
-      }
-      if (kRev) {
-        f32x4 yr = zero4();
+        for (int r = 0; r < 4; ++r) y[tp][r] += rf[r] * yf[tp][r];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kRev) {
+      f32x4 yg[2];
+      readout(yg, cf, sHg, l);
+      const f32x4 rr = *reinterpret_cast<const f32x4*>(tok + kRr * 64 + 16 * w + 4 * q4);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          yr = mfma(lds8(sC, sw256(16 * ib + l16, 4 * kk + q4)), lds8(sHs, sw256(16 * pt + l16, 4 * kk + q4)), yr);
-        const f32x4 rr = *reinterpret_cast<const f32x4*>(tok + kRr * 64 + 16 * ib + 4 * q4);
+      for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] += rr[r] * yr[r];
-      }
-      *reinterpret_cast<f32x4*>(sStash + ((k * 8 + w) * 64 + l) * 4) = y;
-      if (kRev) {
+        for (int r = 0; r < 4; ++r) y[tp][r] += (tau_run * rr[r]) * yg[tp][r];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // skip term and gate
+    float o[2][4];
+    const int i0 = 16 * w + 4 * q4;
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp) G[tp] = tile_update(G[tp] * eS, sBT, sXW, w, tp, l);
-      }
-    } else {
-      y = *reinterpret_cast<const f32x4*>(sStash + ((k * 8 + w) * 64 + l) * 4);
-      if (kFwd) {
-        f32x4 yf = zero4();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          yf = mfma(lds8(sC, sw256(16 * ib + l16, 4 * kk + q4)), lds8(sHs, sw256(16 * pt + l16, 4 * kk + q4)), yf);
-        const f32x4 rf = *reinterpret_cast<const f32x4*>(tok + kRf * 64 + 16 * ib + 4 * q4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] += rf[r] * yf[r];
-      }
-      // skip term and gate; the wavefront's 16 x 16 tile leaves through LDS as 16-byte rows
-      const int p = 16 * pt + l16;
-      const int i0 = 16 * ib + 4 * q4;
+    for (int tp = 0; tp < 2; ++tp) {
+      const int p = 16 * tp + l16;
       const uint2 xv = *reinterpret_cast<const uint2*>(sXT + sw128(p, i0 >> 3) + (i0 & 7));
       const float xs[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xffff0000u),
                            __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xffff0000u)};
-      float o[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        o[r] = y[r] + Dfac * xs[r];
-        if (a.gate) o[r] *= silu_f32(bf(zo[(4 * q4 + r) * 16 + l16]));
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        bf16_t ob;
-        from_f32(o[r], &ob);
-        zo[(4 * q4 + r) * 16 + l16] = ob.bits;
-      }
-      if (l < 32) {
-        const int64_t tz = t0 + 16 * ib + zr;
-        if (tz < a.L)
-          *reinterpret_cast<uint4*>(a.out + (b * a.L + tz) * HP + h * P + 16 * pt + 8 * zh) =
-              *reinterpret_cast<const uint4*>(zo + zr * 16 + 8 * zh);
-      }
-      if (kFwd) {
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp) H[tp] = tile_update(H[tp] * eS, sBT, sXW, w, tp, l);
+        o[tp][r] = y[tp][r] + Dfac * xs[r];
+        if (a.gate) o[tp][r] *= silu_f32(bf(zslot[(4 * q4 + r) * P + p]));
       }
     }
-    // per-token terms of the next step
-    if (w == 0 && st + 1 < nsteps) {
-      int64_t s1, k1, nk1;
-      bool rs1;
-      decode_step(st + 1, nvalid, s1, rs1, k1, nk1);
-      token_prep(sTok[(st + 1) & 1], pdt, (sub0 + s1 * SEG + k1) * Q + l < a.L, Ah, bias, l);
+    tile_rows_to_lds(yslot, o, l);
+    {
+      const int64_t t = t0 + 16 * w + (l >> 2);
+      if (t < a.L)
+        *reinterpret_cast<uint4*>(a.out + (b * a.L + t) * HP + h * P + 8 * (l & 3)) =
+            *reinterpret_cast<const uint4*>(yslot + (l >> 2) * P + 8 * (l & 3));
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kFwd) state_update(H, ex(tok[kS * 64 + 63]), sBT, sXW, w, l);
+    if (w == 0 && k + 1 < nrun) token_prep(sTok[(k + 1) & 1], pdt, (sub0 + k + 1) * Q + l < a.L, Ah, bias, l);
   }
 }
 
@@ -615,7 +649,7 @@ template <int DIRS>
 hipError_t launch_dirs(const Args& a, int64_t batch, hipStream_t stream, int stage) {
   const unsigned groups = static_cast<unsigned>(batch * a.nchunk * a.H);
   if (stage < 0 || stage == 1) {
-    hipLaunchKernelGGL(k_ssd_summary<DIRS>, dim3(groups), dim3(kSumThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_ssd_rsweep<DIRS>, dim3(groups), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -627,7 +661,7 @@ hipError_t launch_dirs(const Args& a, int64_t batch, hipStream_t stream, int sta
     if (e != hipSuccess) return e;
   }
   if (stage < 0 || stage == 3) {
-    hipLaunchKernelGGL(k_ssd_output<DIRS>, dim3(groups), dim3(kOutThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_ssd_fsweep<DIRS>, dim3(groups), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -651,19 +685,18 @@ hipError_t launch_ssd(const SsdArgs& in, const SsdPlan& p, void* workspace, hipS
   a.L = p.seqlen;
   a.H = p.nheads;
   a.nsub = p.nsub;
-  a.spc = p.spc;
+  a.rpc = p.rpc;
   a.nchunk = p.nchunk;
   a.g = reinterpret_cast<float*>(ws + p.off_g);
   a.cp = reinterpret_cast<uint16_t*>(ws + p.off_cp);
   a.bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
   a.S = reinterpret_cast<float*>(ws + p.off_s);
   a.Pc = reinterpret_cast<float*>(ws + p.off_p);
-  a.R = reinterpret_cast<float*>(ws + p.off_r);
-  a.qd = reinterpret_cast<float*>(ws + p.off_q);
+  a.tau = reinterpret_cast<float*>(ws + p.off_tau);
   a.gate = (in.flags & kNoGate) ? 0 : 1;
   if (stage < 0 || stage == 0) {
     hipLaunchKernelGGL(k_ssd_stage, dim3(static_cast<unsigned>(p.nsub), static_cast<unsigned>(p.batch)),
-                       dim3(kStageThreads), 0, stream, a.B, a.C, a.g, a.cp, a.bt, p.seqlen, p.nsub);
+                       dim3(kThreads), 0, stream, a.B, a.C, a.g, a.cp, a.bt, p.seqlen, p.nsub);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -98,8 +98,7 @@ def test_ssd_delta_to_zero_limit():
 
 @pytest.mark.parametrize("L", [13312, 65536])
 def test_ssd_all_heads_sampled(L):
-    """120 heads at the 1.3B layer's shape; chunks of several segments (with reverse checkpoints) appear once
-    the sequence is long.  Sampled heads are compared in full."""
+    """120 heads at the 1.3B layer's shape (chunks of 13 and 61 runs).  Sampled heads are compared in full."""
     say(f"ssd 120 heads L={L}")
     inp = _inputs(1, L, 120, seed=2)
     got = _run(_upload(inp))
