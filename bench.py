@@ -237,6 +237,85 @@ def bench_block(args, w, torch, bm, I, dev):
     print(json.dumps(line), flush=True)
 
 
+# matrix-core products per (64-token run, head) of the two SSD sweeps, and per run of the tiling kernel
+SSD_Q, SSD_P, SSD_N = 64, 32, 128
+SSD_FLOP_RSWEEP = 2 * SSD_Q * SSD_Q * SSD_P + 2 * SSD_Q * SSD_N * SSD_P + 2 * (2 * SSD_N * SSD_Q * SSD_P)
+SSD_FLOP_FSWEEP = 2 * (2 * SSD_Q * SSD_N * SSD_P) + 2 * SSD_N * SSD_Q * SSD_P
+SSD_FLOP_STAGE = 2 * SSD_Q * SSD_Q * SSD_N
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_ssd(args, torch, bm, I, dev, stream):
+    """Mamba-2 (SSD) heads at the 1.3B layer's shape: one bimamba_ssd_fwd call per step."""
+    w = I.SSD_WORKLOADS["ssd_long_64k_bf16"]
+    log(f"ssd workload {w.name}: batch {w.batch} L {w.seqlen} heads {w.nheads} x {w.headdim} d_state {w.d_state}")
+    inp = I.make_ssd_inputs(w)
+
+    def up(a, io=True):
+        if io:
+            return torch.from_numpy(I.bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    x, dt, z, B, C = (up(inp[k]) for k in ("x", "dt", "z", "B", "C"))
+    A, Dv, bias = (up(inp[k], False) for k in ("A", "D", "dt_bias"))
+    del inp
+    out = torch.empty_like(x)
+    ws = torch.empty(bm.bimamba_ssd_fwd_workspace_bytes(w.batch, w.seqlen, w.nheads, w.headdim, w.d_state),
+                     dtype=torch.uint8, device=dev)
+    args_t = (x, dt, A, B, C, Dv, z, bias)
+
+    def step():
+        bm.bimamba_ssd_fwd(*args_t, out=out, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    names = ("k_ssd_stage", "k_ssd_rsweep", "k_ssd_carry", "k_ssd_fsweep")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s_ in range(args.steps):
+        e = evs[s_]
+        e[0].record(stream)
+        for st in range(4):
+            bm.bimamba_ssd_fwd_stage(st, *args_t, out=out, workspace=ws, stream=stream)
+            e[st + 1].record(stream)
+    torch.cuda.synchronize()
+    per = {n: float(np.mean([evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)]))
+           for i, n in enumerate(names)}
+    log(f"ssd: {ms:.4f} ms/call; per-kernel ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per.items()))
+    runs = w.batch * ((w.seqlen + SSD_Q - 1) // SSD_Q)
+    flop = {"k_ssd_rsweep": SSD_FLOP_RSWEEP * runs * w.nheads, "k_ssd_fsweep": SSD_FLOP_FSWEEP * runs * w.nheads,
+            "k_ssd_stage": SSD_FLOP_STAGE * runs}
+    dom = max(("k_ssd_rsweep", "k_ssd_fsweep"), key=lambda k: per[k])
+    achieved = flop[dom] / (per[dom] * 1e-3) / 1e12
+    tokens = w.batch * w.seqlen
+    nc = w.nheads * w.headdim
+    # HBM bytes the call must move: x twice (one per sweep), z once, out written twice and read once (the
+    # reverse sweep's partial output), dt twice, B and C once; per run the tiling kernel writes C and B^T
+    # (bf16) and C B^T (fp32), which the reverse sweep reads once and the forward sweep reads without C B^T
+    tile = SSD_Q * SSD_N * 2
+    io_bytes = (tokens * (nc * 2 * (2 + 1 + 3) + w.nheads * 2 * 2 + 2 * w.d_state * 2)
+                + runs * (2 * tile + SSD_Q * SSD_Q * 4) * 2 + runs * 2 * tile)
+    pages_flop = 2 * 2 * nc * w.d_state * tokens  # the paper's count: 2 d_inner d_state per token and direction
+    return {
+        "workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "nheads": w.nheads, "headdim": w.headdim,
+        "d_state": w.d_state, "io_dtype": "bf16", "state_dtype": "f32",
+        "ms_per_call": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+        "kernels_ms": {k: round(v, 4) for k, v in per.items()},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "flop_per_launch": flop[dom]},
+        "hbm": {"bytes_per_call": io_bytes, "achieved_gbs": round(io_bytes / (ms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(io_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "scan_tflops_pages_count": round(pages_flop / (ms * 1e-3) / 1e12, 2),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +324,7 @@ def main():
     ap.add_argument("--workload", default="long_64k_bf16")
     ap.add_argument("--cpu-channels", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ssd", action="store_true", help="skip the Mamba-2 (SSD) heads measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
     args = ap.parse_args()
@@ -408,6 +488,10 @@ def main():
                            "(bimamba_scan_fwd_untied): a forward-only and a reverse-only pass, twice the "
                            "activation bytes and no shared abar"},
     }
+    if not args.no_ssd:
+        del x, dt, z, B, C, out, out_r, rev_set, fwd_set, ws
+        torch.cuda.empty_cache()
+        line["ssd"] = bench_ssd(args, torch, bm, I, dev, stream)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_channels} channels")
         line["cpu_baseline"] = cpu_baseline(inp, w.seqlen, w.d_inner, min(args.cpu_channels, w.d_inner))

@@ -365,9 +365,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_rsweep(Args a) {
   u32x4 pc[4], pbt[4];
   f32x4 pg[4];
   uint4 px;
-  uint16_t pdt = 0;
+  // step sizes run two steps ahead of the other loads, so that forming the next run's per-token terms
+  // at the end of a step never waits for the loads issued in that step
+  uint16_t pdt = 0, pdt2 = 0;
   auto issue = [&](int64_t st) {
     const int64_t sub = sub0 + (nrun - 1 - st);
+    if (w == 0 && st + 1 < nrun) pdt2 = load_dt(a, b, (sub - 1) * Q, h, l);
     const int64_t tile = (b * a.nsub + sub) * static_cast<int64_t>(Q * N);
     const u32x4* b4 = reinterpret_cast<const u32x4*>(a.bt + tile);
     if (kRev) load_cfrag(pc, a.cp + tile, w, l);
@@ -377,10 +380,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_rsweep(Args a) {
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) pg[tj] = *reinterpret_cast<const f32x4*>(gg + ((w * 4 + tj) * 64 + l) * 4);
     px = load_act(a.x, a, b, sub * Q, h, tid);
-    if (w == 0) pdt = load_dt(a, b, sub * Q, h, l);
   };
+  if (w == 0) pdt = load_dt(a, b, (sub0 + nrun - 1) * Q, h, l);
   issue(0);
   if (w == 0) token_prep(sTok[0], pdt, (sub0 + nrun - 1) * Q + l < a.L, Ah, bias, l);
+  pdt = pdt2;
 
   for (int64_t st = 0; st < nrun; ++st) {
     const int64_t k = nrun - 1 - st;
@@ -472,6 +476,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_rsweep(Args a) {
     if (tid == 0) a.tau[item * a.rpc + k] = tau;
     tau *= eS;
     if (w == 0 && st + 1 < nrun) token_prep(sTok[(st + 1) & 1], pdt, (sub0 + k - 1) * Q + l < a.L, Ah, bias, l);
+    pdt = pdt2;
   }
   if (kFwd) state_store(F, a.S + (item * 2 + 0) * kSF, w, l);
   if (kRev) state_store(G, a.S + (item * 2 + 1) * kSF, w, l);
@@ -550,9 +555,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_fsweep(Args a) {
   u32x4 pc[4], pbt[4];
   uint4 px, pz, py;
   float ptau = 0.0f;
-  uint16_t pdt = 0;
+  uint16_t pdt = 0, pdt2 = 0;  // step sizes two steps ahead, as in the reverse sweep
   auto issue = [&](int64_t k) {
     const int64_t sub = sub0 + k, t0 = sub * Q;
+    if (w == 0 && k + 1 < nrun) pdt2 = load_dt(a, b, t0 + Q, h, l);
     const int64_t tile = (b * a.nsub + sub) * static_cast<int64_t>(Q * N);
     const u32x4* b4 = reinterpret_cast<const u32x4*>(a.bt + tile);
     load_cfrag(pc, a.cp + tile, w, l);
@@ -565,10 +571,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_fsweep(Args a) {
     py = load_act(a.out, a, b, t0, h, q);
     if (a.gate) pz = load_act(a.z, a, b, t0, h, q);
     if (kRev) ptau = a.tau[item * a.rpc + k];
-    if (w == 0) pdt = load_dt(a, b, t0, h, l);
   };
+  if (w == 0) pdt = load_dt(a, b, sub0 * Q, h, l);
   issue(0);
   if (w == 0) token_prep(sTok[0], pdt, sub0 * Q + l < a.L, Ah, bias, l);
+  pdt = pdt2;
 
   for (int64_t k = 0; k < nrun; ++k) {
     const int64_t t0 = (sub0 + k) * Q;
@@ -642,6 +649,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_fsweep(Args a) {
     __builtin_amdgcn_sched_barrier(0);
     if (kFwd) state_update(H, ex(tok[kS * 64 + 63]), sBT, sXW, w, l);
     if (w == 0 && k + 1 < nrun) token_prep(sTok[(k + 1) & 1], pdt, (sub0 + k + 1) * Q + l < a.L, Ah, bias, l);
+    pdt = pdt2;
   }
 }
 
