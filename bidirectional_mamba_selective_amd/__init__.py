@@ -8,9 +8,12 @@ from ._lib import (  # noqa: F401
     BIMAMBA_BF16,
     BIMAMBA_F32,
     FLAG_FWD_ONLY,
+    FLAG_NO_SILU,
     FLAG_NO_GATE,
     FLAG_REV_ONLY,
     BimambaError,
+    bimamba_conv1d_bidir,
+    bimamba_conv1d_block,
     bimamba_scan_block,
     bimamba_scan_block_workspace_bytes,
     bimamba_scan_fwd,

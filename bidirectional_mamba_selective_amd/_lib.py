@@ -26,6 +26,7 @@ BIMAMBA_BF16 = 1
 FLAG_NO_GATE = 1
 FLAG_FWD_ONLY = 2
 FLAG_REV_ONLY = 4
+FLAG_NO_SILU = 16
 
 # every symbol include/bimamba.h declares
 EXPORTED = (
@@ -40,6 +41,8 @@ EXPORTED = (
     "bimamba_ssd_fwd_workspace_bytes",
     "bimamba_ssd_fwd",
     "bimamba_ssd_fwd_stage",
+    "bimamba_conv1d_bidir",
+    "bimamba_conv1d_block",
 )
 
 _lib = None
@@ -86,6 +89,10 @@ def load() -> ctypes.CDLL:
     lib.bimamba_ssd_fwd_stage.restype = ctypes.c_int
     lib.bimamba_ssd_fwd_stage.argtypes = [ctypes.c_int] + [vp] * 9 + [i64] * 5 + [ctypes.c_int, ctypes.c_uint32, vp,
                                                                                     sz, vp]
+    lib.bimamba_conv1d_bidir.restype = ctypes.c_int
+    lib.bimamba_conv1d_bidir.argtypes = [vp] * 7 + [i64] * 4 + [ctypes.c_int, ctypes.c_uint32, vp]
+    lib.bimamba_conv1d_block.restype = ctypes.c_int
+    lib.bimamba_conv1d_block.argtypes = [vp] * 9 + [i64] * 4 + [ctypes.c_int, ctypes.c_uint32, vp]
     _lib = lib
     return lib
 
@@ -306,3 +313,52 @@ def bimamba_ssd_fwd_stage(stage: int, x, dt, A, B, C, D=None, z=None, dt_bias=No
     if st != BIMAMBA_OK:
         raise BimambaError(st, f"bimamba_ssd_fwd_stage({stage})")
     return out
+
+
+def _conv_common(u, w_f, b_f, w_r, b_r, out_f, out_r):
+    torch = _torch()
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, seqlen, channels]")
+    nb, L, nc = u.shape
+    if w_f is None and w_r is None:
+        raise ValueError("at least one direction's filter is required")
+    K = (w_f if w_f is not None else w_r).shape[-1]
+    dev = u.device
+    _check(u, "u", (nb, L, nc), u.dtype, dev)
+    for name, t, shape in (("w_f", w_f, (nc, K)), ("w_r", w_r, (nc, K)), ("b_f", b_f, (nc,)), ("b_r", b_r, (nc,))):
+        _check(t, name, shape, torch.float32, dev)
+    if w_f is not None and out_f is None:
+        out_f = torch.empty_like(u)
+    if w_r is not None and out_r is None:
+        out_r = torch.empty_like(u)
+    _check(out_f, "out_f", (nb, L, nc), u.dtype, dev)
+    _check(out_r, "out_r", (nb, L, nc), u.dtype, dev)
+    return nb, L, nc, K, (out_f if w_f is not None else None), (out_r if w_r is not None else None)
+
+
+def bimamba_conv1d_bidir(u, w_f=None, b_f=None, w_r=None, b_r=None, out_f=None, out_r=None, flags: int = 0,
+                         stream=None):
+    """Causal (w_f) and anti-causal (w_r) depthwise convolution of u with SiLU; returns (out_f, out_r), None for a
+    direction whose filter is None."""
+    nb, L, nc, K, out_f, out_r = _conv_common(u, w_f, b_f, w_r, b_r, out_f, out_r)
+    st = load().bimamba_conv1d_bidir(_ptr(u), _ptr(w_f), _ptr(b_f), _ptr(w_r), _ptr(b_r), _ptr(out_f), _ptr(out_r),
+                                     nb, L, nc, K, _io_dtype(u), flags, _stream(stream, u.device))
+    if st != BIMAMBA_OK:
+        raise BimambaError(st, "bimamba_conv1d_bidir")
+    return out_f, out_r
+
+
+def bimamba_conv1d_block(u, w_f=None, b_f=None, w_r=None, b_r=None, cache_in=None, cache_out=None, out_f=None,
+                         out_r=None, flags: int = 0, stream=None):
+    """One block of block decoding: the causal filter continues from cache_in ([batch, 3, channels], u's dtype;
+    None = zeros), the anti-causal one stops at the block end; cache_out (may be cache_in) receives the last 3
+    tokens.  Returns (out_f, out_r)."""
+    nb, L, nc, K, out_f, out_r = _conv_common(u, w_f, b_f, w_r, b_r, out_f, out_r)
+    _check(cache_in, "cache_in", (nb, K - 1, nc), u.dtype, u.device)
+    _check(cache_out, "cache_out", (nb, K - 1, nc), u.dtype, u.device)
+    st = load().bimamba_conv1d_block(_ptr(u), _ptr(w_f), _ptr(b_f), _ptr(w_r), _ptr(b_r), _ptr(cache_in),
+                                     _ptr(cache_out), _ptr(out_f), _ptr(out_r), nb, L, nc, K, _io_dtype(u), flags,
+                                     _stream(stream, u.device))
+    if st != BIMAMBA_OK:
+        raise BimambaError(st, "bimamba_conv1d_block")
+    return out_f, out_r

@@ -276,4 +276,67 @@ int bimamba_ssd_fwd_stage(int stage, const void* x, const void* dt, const float*
                   flags, workspace, workspace_bytes, stream);
 }
 
+// ---- Short causal / anti-causal convolution ----
+
+static int conv_impl(const void* u, const float* w_f, const float* b_f, const float* w_r, const float* b_r,
+                     const void* cache_in, void* cache_out, void* out_f, void* out_r, int64_t batch, int64_t L,
+                     int64_t C, int64_t d_conv, int io_dtype, uint32_t flags, hipStream_t stream, bool block) {
+  if (batch <= 0 || L <= 0 || C <= 0 || d_conv <= 0) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (io_dtype != BIMAMBA_F32 && io_dtype != BIMAMBA_BF16) return BIMAMBA_ERR_UNSUPPORTED;
+  if (d_conv != 4 || C % 4 != 0) return BIMAMBA_ERR_UNSUPPORTED;
+  if (batch > 65535 || C / 4 / 256 >= 65535 || L > INT32_MAX / 2) return BIMAMBA_ERR_UNSUPPORTED;
+  if (flags & ~static_cast<uint32_t>(BIMAMBA_FLAG_NO_SILU)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (!u || (!out_f && !out_r)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if ((out_f && !w_f) || (out_r && !w_r)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (!block && (cache_in || cache_out)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const size_t es = io_dtype == BIMAMBA_BF16 ? 2 : 4;
+  const uintptr_t va = 4 * es;
+  if (!aligned(u, va) || (out_f && !aligned(out_f, va)) || (out_r && !aligned(out_r, va)) ||
+      (cache_in && !aligned(cache_in, va)) || (cache_out && !aligned(cache_out, va)))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if ((w_f && !aligned(w_f, 4)) || (w_r && !aligned(w_r, 4)) || (b_f && !aligned(b_f, 4)) ||
+      (b_r && !aligned(b_r, 4)))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const size_t act = static_cast<size_t>(batch) * L * C * es;
+  const size_t cb = static_cast<size_t>(batch) * 3 * C * es;
+  const size_t wb = static_cast<size_t>(C) * d_conv * 4, bb = static_cast<size_t>(C) * 4;
+  // everything an output may not touch
+  auto clash = [&](Range o) {
+    return overlap(o, range_of(u, act)) || (w_f && overlap(o, range_of(w_f, wb))) ||
+           (w_r && overlap(o, range_of(w_r, wb))) || (b_f && overlap(o, range_of(b_f, bb))) ||
+           (b_r && overlap(o, range_of(b_r, bb))) || (cache_in && overlap(o, range_of(cache_in, cb)));
+  };
+  if (out_f && (clash(range_of(out_f, act)) || (out_r && overlap(range_of(out_f, act), range_of(out_r, act))) ||
+                (cache_out && overlap(range_of(out_f, act), range_of(cache_out, cb)))))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (out_r && (clash(range_of(out_r, act)) || (cache_out && overlap(range_of(out_r, act), range_of(cache_out, cb)))))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (cache_out) {
+    const Range co = range_of(cache_out, cb);
+    const bool in_place = cache_in == cache_out;
+    if (overlap(co, range_of(u, act)) || (w_f && overlap(co, range_of(w_f, wb))) ||
+        (w_r && overlap(co, range_of(w_r, wb))) || (b_f && overlap(co, range_of(b_f, bb))) ||
+        (b_r && overlap(co, range_of(b_r, bb))) || (cache_in && !in_place && overlap(co, range_of(cache_in, cb))))
+      return BIMAMBA_ERR_INVALID_ARGUMENT;
+  }
+  const bimamba::conv::ConvArgs a{u, w_f, b_f, w_r, b_r, cache_in, cache_out, out_f, out_r,
+                                  (flags & BIMAMBA_FLAG_NO_SILU) ? 0 : 1};
+  return map_hip(bimamba::conv::launch_conv(a, batch, L, C, io_dtype, stream));
+}
+
+int bimamba_conv1d_bidir(const void* u, const float* w_f, const float* b_f, const float* w_r, const float* b_r,
+                         void* out_f, void* out_r, int64_t batch, int64_t seqlen, int64_t channels, int64_t d_conv,
+                         int io_dtype, uint32_t flags, hipStream_t stream) {
+  return conv_impl(u, w_f, b_f, w_r, b_r, nullptr, nullptr, out_f, out_r, batch, seqlen, channels, d_conv, io_dtype,
+                   flags, stream, false);
+}
+
+int bimamba_conv1d_block(const void* u, const float* w_f, const float* b_f, const float* w_r, const float* b_r,
+                         const void* cache_in, void* cache_out, void* out_f, void* out_r, int64_t batch,
+                         int64_t block_len, int64_t channels, int64_t d_conv, int io_dtype, uint32_t flags,
+                         hipStream_t stream) {
+  return conv_impl(u, w_f, b_f, w_r, b_r, cache_in, cache_out, out_f, out_r, batch, block_len, channels, d_conv,
+                   io_dtype, flags, stream, true);
+}
+
 }  // extern "C"

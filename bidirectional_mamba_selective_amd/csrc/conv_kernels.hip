@@ -1,0 +1,211 @@
+// Short causal / anti-causal depthwise convolution with SiLU, both directions
+// from one read of the input, for gfx950.
+//
+// Operation: the Conv1d of width d_conv = 4 that each direction of the
+// DiffuMamba mixer runs ahead of its scan ("DiffuMamba: High-Throughput
+// Diffusion LMs with Mamba Backbone", arXiv v4, Appendix C Table 12; width and
+// untied directions in Section 4.1 Table 8; the reverse layer is the forward
+// one on the flipped sequence, Section 3.2):
+//   fwd[t, c] = silu(b_f[c] + sum_k w_f[c, k] * u[t - 3 + k, c])
+//   rev[t, c] = silu(b_r[c] + sum_k w_r[c, k] * u[t + 3 - k, c])
+// with u = 0 outside the sequence, or in block decoding u before the block
+// taken from a 3-token cache and u after the block taken as 0 (Section 4.3,
+// block-cache paragraph).
+//
+// One thread owns 4 channels of a 64-token tile.  It walks the tile in blocks
+// of 8 tokens with a 14-row window in registers (the 3 rows before the block,
+// the block, and 3 rows after it), so every input row is read once (plus a
+// 6-row halo per tile) and both outputs are written once: the kernel is a
+// pure HBM stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_math.h"
+#include "launch.h"
+
+namespace bimamba {
+namespace conv {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 64;   // tokens per thread
+constexpr int kBlk = 8;     // tokens per window step
+constexpr int kK = 4;       // filter width
+constexpr int kWin = kBlk + 2 * (kK - 1);
+
+// 4 consecutive elements of one row, as fp32.
+__device__ __forceinline__ void load4(const float* p, float v[4]) {
+  const float4 q = *reinterpret_cast<const float4*>(p);
+  v[0] = q.x;
+  v[1] = q.y;
+  v[2] = q.z;
+  v[3] = q.w;
+}
+
+__device__ __forceinline__ void load4(const bf16_t* p, float v[4]) {
+  const uint2 q = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(q.x << 16);
+  v[1] = __uint_as_float(q.x & 0xffff0000u);
+  v[2] = __uint_as_float(q.y << 16);
+  v[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+
+__device__ __forceinline__ void store4(float* p, const float v[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void store4(bf16_t* p, const float v[4]) {
+  bf16_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) from_f32(v[i], &o[i]);
+  *reinterpret_cast<uint2*>(p) = make_uint2(static_cast<uint32_t>(o[0].bits) | (static_cast<uint32_t>(o[1].bits) << 16),
+                                            static_cast<uint32_t>(o[2].bits) | (static_cast<uint32_t>(o[3].bits) << 16));
+}
+
+__device__ __forceinline__ void copy4(float* dst, const float* src) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = src[i];
+}
+
+template <typename T>
+struct Args {
+  const T* u;          // [batch, L, C]
+  const float* w_f;    // [C, 4]
+  const float* b_f;    // [C] or null
+  const float* w_r;
+  const float* b_r;
+  const T* cache_in;   // [batch, 3, C] or null (block decoding)
+  T* cache_out;        // [batch, 3, C] or null
+  T* out_f;            // [batch, L, C] or null
+  T* out_r;
+  int64_t L, C;
+  int act;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_conv(Args<T> a) {
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.y) * kThreads + threadIdx.x) * 4;
+  if (c0 >= a.C) return;  // no barriers below
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTile;
+  const int64_t b = blockIdx.z;
+  const bool do_f = a.out_f != nullptr, do_r = a.out_r != nullptr;
+
+  float wf[4][kK], wr[4][kK], bfv[4], brv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int k = 0; k < kK; ++k) {
+      wf[i][k] = do_f ? a.w_f[(c0 + i) * kK + k] : 0.0f;
+      wr[i][k] = do_r ? a.w_r[(c0 + i) * kK + k] : 0.0f;
+    }
+    bfv[i] = (do_f && a.b_f) ? a.b_f[c0 + i] : 0.0f;
+    brv[i] = (do_r && a.b_r) ? a.b_r[c0 + i] : 0.0f;
+  }
+
+  // row t of the (cache ++ sequence ++ zeros) input, channels c0..c0+3
+  auto row = [&](int64_t t, float v[4]) {
+    if (t >= 0 && t < a.L) {
+      load4(a.u + (b * a.L + t) * a.C + c0, v);
+    } else if (t < 0 && t >= -(kK - 1) && a.cache_in) {
+      load4(a.cache_in + (b * (kK - 1) + (kK - 1) + t) * a.C + c0, v);
+    } else {
+      v[0] = v[1] = v[2] = v[3] = 0.0f;
+    }
+  };
+
+  // cache rows are read before anything is written, so cache_out may alias cache_in
+  float cache[kK - 1][4];
+  const bool first_tile = blockIdx.x == 0;
+  if (first_tile && a.cache_out) {
+#pragma unroll
+    for (int m = 0; m < kK - 1; ++m) row(m - (kK - 1), cache[m]);
+  }
+
+  float win[kWin][4];  // win[m] = row t_blk - 3 + m
+#pragma unroll
+  for (int m = 0; m < 2 * (kK - 1); ++m) row(t0 - (kK - 1) + m, win[m]);
+  for (int blk = 0; blk < kTile / kBlk; ++blk) {
+    const int64_t tb = t0 + blk * kBlk;
+    if (tb >= a.L) break;
+#pragma unroll
+    for (int m = 0; m < kBlk; ++m) row(tb + (kK - 1) + m, win[2 * (kK - 1) + m]);
+#pragma unroll
+    for (int tt = 0; tt < kBlk; ++tt) {
+      const int64_t t = tb + tt;
+      if (t >= a.L) break;
+      if (do_f) {
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = bfv[i];
+#pragma unroll
+          for (int k = 0; k < kK; ++k) s = fmaf(wf[i][k], win[tt + k][i], s);
+          o[i] = a.act ? silu_f32(s) : s;
+        }
+        store4(a.out_f + (b * a.L + t) * a.C + c0, o);
+      }
+      if (do_r) {
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = brv[i];
+#pragma unroll
+          for (int k = 0; k < kK; ++k) s = fmaf(wr[i][k], win[tt + 2 * (kK - 1) - k][i], s);
+          o[i] = a.act ? silu_f32(s) : s;
+        }
+        store4(a.out_r + (b * a.L + t) * a.C + c0, o);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 2 * (kK - 1); ++m) copy4(win[m], win[kBlk + m]);
+  }
+
+  // the cache for the next block: the last 3 rows of (cache ++ sequence)
+  if (first_tile && a.cache_out) {
+#pragma unroll
+    for (int m = 0; m < kK - 1; ++m) {
+      const int64_t t = a.L - (kK - 1) + m;
+      float v[4];
+      if (t >= 0) {
+        row(t, v);
+      } else {
+        // fewer than 3 tokens in the block: part of the new cache is the old one (index L + m < 3)
+        const int64_t j = a.L + m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = j == 0 ? cache[0][i] : (j == 1 ? cache[1][i] : cache[2][i]);
+      }
+      store4(a.cache_out + (b * (kK - 1) + m) * a.C + c0, v);
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_t(const ConvArgs& in, int64_t batch, int64_t L, int64_t C, hipStream_t stream) {
+  Args<T> a{};
+  a.u = static_cast<const T*>(in.u);
+  a.w_f = in.w_f;
+  a.b_f = in.b_f;
+  a.w_r = in.w_r;
+  a.b_r = in.b_r;
+  a.cache_in = static_cast<const T*>(in.cache_in);
+  a.cache_out = static_cast<T*>(in.cache_out);
+  a.out_f = static_cast<T*>(in.out_f);
+  a.out_r = static_cast<T*>(in.out_r);
+  a.L = L;
+  a.C = C;
+  a.act = in.act;
+  const dim3 grid(static_cast<unsigned>((L + kTile - 1) / kTile),
+                  static_cast<unsigned>((C / 4 + kThreads - 1) / kThreads), static_cast<unsigned>(batch));
+  hipLaunchKernelGGL(k_conv<T>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv(const ConvArgs& a, int64_t batch, int64_t L, int64_t C, int io_dtype, hipStream_t stream) {
+  return io_dtype == 1 ? launch_t<bf16_t>(a, batch, L, C, stream) : launch_t<float>(a, batch, L, C, stream);
+}
+
+}  // namespace conv
+}  // namespace bimamba

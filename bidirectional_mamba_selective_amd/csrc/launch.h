@@ -36,6 +36,26 @@ hipError_t launch_chunked(const ScanArgs& a, const Plan& p, void* workspace, hip
 hipError_t launch_block_fused(const ScanArgs& a, int64_t batch, int64_t block_len, int64_t d_inner,
                               int64_t d_state, hipStream_t stream);
 
+namespace conv {
+
+// Short causal / anti-causal depthwise convolution (width 4) with optional SiLU.
+struct ConvArgs {
+  const void* u;
+  const float* w_f;
+  const float* b_f;
+  const float* w_r;
+  const float* b_r;
+  const void* cache_in;  // block decoding: the 3 tokens before the block (null = zeros)
+  void* cache_out;       // block decoding: receives the last 3 tokens (null = not written)
+  void* out_f;           // null = forward direction not computed
+  void* out_r;           // null = reverse direction not computed
+  int act;
+};
+
+hipError_t launch_conv(const ConvArgs& a, int64_t batch, int64_t L, int64_t C, int io_dtype, hipStream_t stream);
+
+}  // namespace conv
+
 namespace ssd {
 
 // Mamba-2 (SSD) scan: bf16 x, dt, B, C, z, out; fp32 A, D, dt_bias per head.

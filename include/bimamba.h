@@ -64,7 +64,8 @@ typedef enum { BIMAMBA_F32 = 0, BIMAMBA_BF16 = 1 } bimamba_dtype;
 enum {
   BIMAMBA_FLAG_NO_GATE = 1u,  /* out = y_fwd + y_rev, no SiLU(z) factor (z may be NULL) */
   BIMAMBA_FLAG_FWD_ONLY = 2u, /* keep only the forward direction, eq. (4)            */
-  BIMAMBA_FLAG_REV_ONLY = 4u  /* keep only the reverse direction, eq. (5)            */
+  BIMAMBA_FLAG_REV_ONLY = 4u, /* keep only the reverse direction, eq. (5)            */
+  BIMAMBA_FLAG_NO_SILU = 16u  /* short convolution only: return the filter output without SiLU */
 };
 
 /* Library version, (major << 16) | (minor << 8) | patch. */
@@ -190,6 +191,40 @@ int bimamba_ssd_fwd_stage(int stage, const void* x, const void* dt, const float*
                           int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
                           int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/* ---- Short causal / anti-causal convolution ------------------------------
+ * Each direction of the mixer runs a depthwise Conv1d of width d_conv = 4
+ * ahead of its scan (Appendix C Table 12: conv_ch = 4096 channels at the 1.3B
+ * shape, one multiply-add per token, channel and tap; Section 4.1 Table 8:
+ * width 4, directions not tied); the reverse layer is the forward layer on
+ * the flipped sequence (Section 3.2).  Per channel c and token t:
+ *   out_f[t,c] = silu(b_f[c] + sum_k w_f[c,k] * u[t-3+k, c])     (causal)
+ *   out_r[t,c] = silu(b_r[c] + sum_k w_r[c,k] * u[t+3-k, c])     (anti-causal)
+ * with u = 0 outside the sequence.  Both directions come from one read of u.
+ * Layouts: u, out_f, out_r [batch, seqlen, channels] (io_dtype); w_f, w_r
+ * [channels, d_conv] fp32; b_f, b_r [channels] fp32 or NULL (= 0).  For tied
+ * weights pass the same pointers twice.  out_f or out_r may be NULL to skip
+ * that direction (not both); its weights may then be NULL too.
+ * Supported: d_conv 4, channels a multiple of 4, io_dtype F32 or BF16 (fp32
+ * arithmetic, round to nearest even for bf16).  u, outputs and caches must be
+ * aligned to 4 elements (8 bytes bf16, 16 bytes fp32), weights and biases to 4
+ * bytes.  flags: 0 or BIMAMBA_FLAG_NO_SILU.  Outputs must not overlap any
+ * input, each other or a cache.  Ownership and asynchrony as above. */
+int bimamba_conv1d_bidir(const void* u, const float* w_f, const float* b_f, const float* w_r, const float* b_r,
+                         void* out_f, void* out_r, int64_t batch, int64_t seqlen, int64_t channels,
+                         int64_t d_conv, int io_dtype, uint32_t flags, hipStream_t stream);
+
+/* The same for one block of block decoding (Section 4.3, block-cache
+ * paragraph): the causal filter reads the 3 tokens before the block from
+ * cache_in ([batch, 3, channels], io_dtype, oldest first; NULL = zeros) and the
+ * anti-causal filter sees zeros past the block's last token.  cache_out
+ * ([batch, 3, channels]; NULL = not written) receives the last 3 tokens of
+ * (cache_in, block), the cache of the next block; it may equal cache_in
+ * (in-place commit) but must not otherwise overlap it. */
+int bimamba_conv1d_block(const void* u, const float* w_f, const float* b_f, const float* w_r, const float* b_r,
+                         const void* cache_in, void* cache_out, void* out_f, void* out_r, int64_t batch,
+                         int64_t block_len, int64_t channels, int64_t d_conv, int io_dtype, uint32_t flags,
+                         hipStream_t stream);
 
 #ifdef __cplusplus
 }

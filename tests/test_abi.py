@@ -21,7 +21,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libbi
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(bimamba_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(bimamba_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -260,3 +260,49 @@ def test_ssd_checks_run_in_order_and_stages_validate():
     for st in range(4):
         assert call_ssd(stage=st) == WS
         assert call_ssd(stage=st, x=None) == INV
+
+
+def call_conv(block=False, **kw):
+    lib = _lib.load()
+    a = dict(u=fake(0), w_f=fake(1), b_f=fake(2), w_r=fake(3), b_r=fake(4), cin=fake(5), cout=fake(6), of=fake(7),
+             orr=fake(8), batch=1, L=100, c=64, k=4, io=_lib.BIMAMBA_BF16, flags=0)
+    a.update(kw)
+    if block:
+        return lib.bimamba_conv1d_block(a["u"], a["w_f"], a["b_f"], a["w_r"], a["b_r"], a["cin"], a["cout"], a["of"],
+                                        a["orr"], a["batch"], a["L"], a["c"], a["k"], a["io"], a["flags"], None)
+    return lib.bimamba_conv1d_bidir(a["u"], a["w_f"], a["b_f"], a["w_r"], a["b_r"], a["of"], a["orr"], a["batch"],
+                                    a["L"], a["c"], a["k"], a["io"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(u=None), INV),
+    (dict(of=None, orr=None), INV),  # no direction requested
+    (dict(w_f=None), INV),  # forward output without its filter
+    (dict(w_r=None), INV),
+    (dict(batch=0), INV),
+    (dict(L=0), INV),
+    (dict(c=0), INV),
+    (dict(k=0), INV),
+    (dict(k=3), UNS),  # only width 4
+    (dict(c=62), UNS),  # channels in groups of 4
+    (dict(io=5), UNS),
+    (dict(batch=70000), UNS),
+    (dict(flags=_lib.FLAG_NO_GATE), INV),
+    (dict(u=fake(0, 4)), INV),  # bf16 rows need 8-byte alignment
+    (dict(io=_lib.BIMAMBA_F32, of=fake(7, 8)), INV),  # fp32 needs 16
+    (dict(w_f=fake(1, 2)), INV),
+    (dict(of=fake(0, 64)), INV),  # output over the input
+    (dict(orr=fake(7, 0)), INV),  # the two outputs overlap
+    (dict(of=fake(3, 0)), INV),  # output over the reverse filter
+])
+def test_conv_rejects(kw, want):
+    assert call_conv(**kw) == want
+
+
+def test_conv_cache_arguments():
+    # block: cache_out over u or an output, or partly over cache_in, is rejected (only rejected calls are made
+    # here: an accepted one would launch)
+    assert call_conv(block=True, cout=fake(0, 8)) == INV
+    assert call_conv(block=True, cout=fake(7, 16)) == INV
+    assert call_conv(block=True, cin=fake(6, 8)) == INV  # partial overlap of the two caches
+    assert call_conv(block=True, of=fake(5, 0)) == INV  # output over cache_in
