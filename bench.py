@@ -316,6 +316,39 @@ def bench_ssd(args, torch, bm, I, dev, stream):
     }
 
 
+def bench_conv(args, torch, bm, I, dev, stream):
+    """The short causal / anti-causal convolution at the 1.3B layer's conv width (4096 channels), L = 65536, bf16:
+    both directions from one read of the input."""
+    L, C = 65536, 4096
+    rng = np.random.default_rng(0)
+    u = torch.from_numpy(I.bf16_bits(rng.standard_normal((1, L, C), dtype=np.float32)).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    w_f, w_r = (torch.from_numpy((0.5 * rng.standard_normal((C, 4))).astype(np.float32)).to(dev) for _ in range(2))
+    b_f, b_r = (torch.from_numpy((0.1 * rng.standard_normal(C)).astype(np.float32)).to(dev) for _ in range(2))
+    out_f, out_r = torch.empty_like(u), torch.empty_like(u)
+
+    def step():
+        bm.bimamba_conv1d_bidir(u, w_f, b_f, w_r, b_r, out_f=out_f, out_r=out_r, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = L * C * 2 * 3  # u read once, both outputs written once
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"conv: {ms:.4f} ms/call, {gbs:.0f} GB/s")
+    return {"workload": "conv_long_64k_bf16", "seq_len": L, "channels": C, "d_conv": 4, "io_dtype": "bf16",
+            "ms_per_call": round(ms, 4), "tokens_per_s": round(L / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "kernel": "k_conv", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -492,6 +525,8 @@ def main():
         del x, dt, z, B, C, out, out_r, rev_set, fwd_set, ws
         torch.cuda.empty_cache()
         line["ssd"] = bench_ssd(args, torch, bm, I, dev, stream)
+        torch.cuda.empty_cache()
+        line["conv"] = bench_conv(args, torch, bm, I, dev, stream)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_channels} channels")
         line["cpu_baseline"] = cpu_baseline(inp, w.seqlen, w.d_inner, min(args.cpu_channels, w.d_inner))

@@ -284,7 +284,8 @@ static int conv_impl(const void* u, const float* w_f, const float* b_f, const fl
   if (batch <= 0 || L <= 0 || C <= 0 || d_conv <= 0) return BIMAMBA_ERR_INVALID_ARGUMENT;
   if (io_dtype != BIMAMBA_F32 && io_dtype != BIMAMBA_BF16) return BIMAMBA_ERR_UNSUPPORTED;
   if (d_conv != 4 || C % 4 != 0) return BIMAMBA_ERR_UNSUPPORTED;
-  if (batch > 65535 || C / 4 / 256 >= 65535 || L > INT32_MAX / 2) return BIMAMBA_ERR_UNSUPPORTED;
+  if (batch > 65535 || L > INT32_MAX / 2 || static_cast<double>((L + 63) / 64) * ((C / 4 + 255) / 256) > 2.0e9)
+    return BIMAMBA_ERR_UNSUPPORTED;
   if (flags & ~static_cast<uint32_t>(BIMAMBA_FLAG_NO_SILU)) return BIMAMBA_ERR_INVALID_ARGUMENT;
   if (!u || (!out_f && !out_r)) return BIMAMBA_ERR_INVALID_ARGUMENT;
   if ((out_f && !w_f) || (out_r && !w_r)) return BIMAMBA_ERR_INVALID_ARGUMENT;

@@ -14,9 +14,9 @@
 //
 // One thread owns 4 channels of a 64-token tile.  It walks the tile in blocks
 // of 8 tokens with a 14-row window in registers (the 3 rows before the block,
-// the block, and 3 rows after it), so every input row is read once (plus a
-// 6-row halo per tile) and both outputs are written once: the kernel is a
-// pure HBM stream.
+// the block, and 3 rows after it), loading the rows of the next block while it
+// computes the current one, so every input row is read once (plus a 6-row halo
+// per tile) and both outputs are written once: the kernel is a pure HBM stream.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,6 +63,36 @@ __device__ __forceinline__ void store4(bf16_t* p, const float v[4]) {
                                             static_cast<uint32_t>(o[2].bits) | (static_cast<uint32_t>(o[3].bits) << 16));
 }
 
+// Raw 4-element row chunks, kept undecoded while a load is in flight.
+template <typename T>
+struct Raw;
+
+template <>
+struct Raw<float> {
+  float4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void zero() { v = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void get(float o[4]) const {
+    o[0] = v.x;
+    o[1] = v.y;
+    o[2] = v.z;
+    o[3] = v.w;
+  }
+};
+
+template <>
+struct Raw<bf16_t> {
+  uint2 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void zero() { v = make_uint2(0, 0); }
+  __device__ __forceinline__ void get(float o[4]) const {
+    o[0] = __uint_as_float(v.x << 16);
+    o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16);
+    o[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+};
+
 __device__ __forceinline__ void copy4(float* dst, const float* src) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) dst[i] = src[i];
@@ -85,10 +115,13 @@ struct Args {
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_conv(Args<T> a) {
-  const int64_t c0 = (static_cast<int64_t>(blockIdx.y) * kThreads + threadIdx.x) * 4;
+  // workgroups walk the channel blocks of a tile first, so that the ones in flight read whole rows
+  const int64_t cblocks = (a.C / 4 + kThreads - 1) / kThreads;
+  const int64_t tile = static_cast<int64_t>(blockIdx.x) / cblocks;
+  const int64_t c0 = ((static_cast<int64_t>(blockIdx.x) - tile * cblocks) * kThreads + threadIdx.x) * 4;
   if (c0 >= a.C) return;  // no barriers below
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTile;
-  const int64_t b = blockIdx.z;
+  const int64_t t0 = tile * kTile;
+  const int64_t b = blockIdx.y;
   const bool do_f = a.out_f != nullptr, do_r = a.out_r != nullptr;
 
   float wf[4][kK], wr[4][kK], bfv[4], brv[4];
@@ -116,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void k_conv(Args<T> a) {
 
   // cache rows are read before anything is written, so cache_out may alias cache_in
   float cache[kK - 1][4];
-  const bool first_tile = blockIdx.x == 0;
+  const bool first_tile = tile == 0;
   if (first_tile && a.cache_out) {
 #pragma unroll
     for (int m = 0; m < kK - 1; ++m) row(m - (kK - 1), cache[m]);
@@ -125,11 +158,23 @@ __global__ __launch_bounds__(kThreads) void k_conv(Args<T> a) {
   float win[kWin][4];  // win[m] = row t_blk - 3 + m
 #pragma unroll
   for (int m = 0; m < 2 * (kK - 1); ++m) row(t0 - (kK - 1) + m, win[m]);
+  // the rows a block adds to the window are loaded one block ahead
+  Raw<T> nxt[kBlk];
+  auto fetch = [&](int64_t tb) {
+#pragma unroll
+    for (int m = 0; m < kBlk; ++m) {
+      const int64_t t = tb + (kK - 1) + m;
+      if (t < a.L) nxt[m].load(a.u + (b * a.L + t) * a.C + c0);
+      else nxt[m].zero();
+    }
+  };
+  fetch(t0);
   for (int blk = 0; blk < kTile / kBlk; ++blk) {
     const int64_t tb = t0 + blk * kBlk;
     if (tb >= a.L) break;
 #pragma unroll
-    for (int m = 0; m < kBlk; ++m) row(tb + (kK - 1) + m, win[2 * (kK - 1) + m]);
+    for (int m = 0; m < kBlk; ++m) nxt[m].get(win[2 * (kK - 1) + m]);
+    if (blk + 1 < kTile / kBlk && tb + kBlk < a.L) fetch(tb + kBlk);
 #pragma unroll
     for (int tt = 0; tt < kBlk; ++tt) {
       const int64_t t = tb + tt;
@@ -195,8 +240,8 @@ hipError_t launch_t(const ConvArgs& in, int64_t batch, int64_t L, int64_t C, hip
   a.L = L;
   a.C = C;
   a.act = in.act;
-  const dim3 grid(static_cast<unsigned>((L + kTile - 1) / kTile),
-                  static_cast<unsigned>((C / 4 + kThreads - 1) / kThreads), static_cast<unsigned>(batch));
+  const int64_t cblocks = (C / 4 + kThreads - 1) / kThreads;
+  const dim3 grid(static_cast<unsigned>((L + kTile - 1) / kTile * cblocks), static_cast<unsigned>(batch));
   hipLaunchKernelGGL(k_conv<T>, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
