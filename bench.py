@@ -38,6 +38,10 @@ VALU_PEAK_TFLOPS = 157.3
 FLOP_PER_ELEMENT_OUTPUT = 18  # per (token, channel, state): mul + exp(8) + mul + 2 fma(4) + 2 fma(4)
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "k_output_long_64k_bf16_traffic.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "bidirectional_mamba_selective_amd", "csrc", "scan_kernels.hip")
+SSD_SOURCE = os.path.join(ROOT, "bidirectional_mamba_selective_amd", "csrc", "ssd_kernels.hip")
+CONV_SOURCE = os.path.join(ROOT, "bidirectional_mamba_selective_amd", "csrc", "conv_kernels.hip")
+SSD_PROFILE = os.path.join(ROOT, "profiles", "k_ssd_long_64k_bf16_traffic.txt")
+CONV_PROFILE = os.path.join(ROOT, "profiles", "k_conv_long_64k_bf16_traffic.txt")
 
 
 def log(msg):
@@ -50,19 +54,20 @@ def algorithmic_bytes(batch, L, D, N, es):
     return batch * L * per_token + D * N * 4 + 2 * D * 4
 
 
-def kernel_source_hash():
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(path=None):
+    return hashlib.sha256(open(path or KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
 
 
-def profiled_traffic(launch_elems):
-    """HBM bytes per output-kernel launch from the committed rocprofv3 counter summary,
-    or None when it is missing or was taken on a different kernel source."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+def profiled_traffic(launch_elems=None, profile=None, source=None, key="hbm_bytes_per_dispatch"):
+    """HBM bytes per launch of a kernel from a committed rocprofv3 counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    profile = profile or PROFILE_TRAFFIC
+    if not os.path.exists(profile):
         return None
-    txt = open(PROFILE_TRAFFIC).read()
+    txt = open(profile).read()
     m_src = re.search(r"source_sha256_16:\s*([0-9a-f]+)", txt)
-    m_b = re.search(r"hbm_bytes_per_dispatch:\s*([0-9.eE+]+)", txt)
-    if not m_src or not m_b or m_src.group(1) != kernel_source_hash():
+    m_b = re.search(re.escape(key) + r":\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != kernel_source_hash(source):
         return None
     return float(m_b.group(1))
 
@@ -309,7 +314,9 @@ def bench_ssd(args, torch, bm, I, dev, stream):
         "kernels_ms": {k: round(v, 4) for k, v in per.items()},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "flop_per_launch": flop[dom]},
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "flop_per_launch": flop[dom],
+                     "traffic": profiled_traffic(profile=SSD_PROFILE, source=SSD_SOURCE,
+                                                 key=f"hbm_bytes_per_dispatch_{dom}")},
         "hbm": {"bytes_per_call": io_bytes, "achieved_gbs": round(io_bytes / (ms * 1e-3) / 1e9, 1),
                 "frac_of_peak": round(io_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "scan_tflops_pages_count": round(pages_flop / (ms * 1e-3) / 1e12, 2),
@@ -346,7 +353,8 @@ def bench_conv(args, torch, bm, I, dev, stream):
     return {"workload": "conv_long_64k_bf16", "seq_len": L, "channels": C, "d_conv": 4, "io_dtype": "bf16",
             "ms_per_call": round(ms, 4), "tokens_per_s": round(L / (ms * 1e-3), 1),
             "roofline": {"bound": "hbm", "kernel": "k_conv", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes}}
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
+                         "traffic": profiled_traffic(profile=CONV_PROFILE, source=CONV_SOURCE)}}
 
 
 def main():
