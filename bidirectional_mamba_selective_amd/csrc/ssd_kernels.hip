@@ -613,7 +613,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_fsweep(Args a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) y[tp][r] += rf[r] * yf[tp][r];
     }
-    __builtin_amdgcn_sched_barrier(0);
     if (kRev) {
       f32x4 yg[2];
       readout(yg, cf, sHg, l);
@@ -623,7 +622,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_fsweep(Args a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) y[tp][r] += (tau_run * rr[r]) * yg[tp][r];
     }
-    __builtin_amdgcn_sched_barrier(0);
     // skip term and gate
     float o[2][4];
     const int i0 = 16 * w + 4 * q4;
@@ -646,7 +644,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_fsweep(Args a) {
         *reinterpret_cast<uint4*>(a.out + (b * a.L + t) * HP + h * P + 8 * (l & 3)) =
             *reinterpret_cast<const uint4*>(yslot + (l >> 2) * P + 8 * (l & 3));
     }
-    __builtin_amdgcn_sched_barrier(0);
     if (kFwd) state_update(H, ex(tok[kS * 64 + 63]), sBT, sXW, w, l);
     if (w == 0 && k + 1 < nrun) token_prep(sTok[(k + 1) & 1], pdt, (sub0 + k + 1) * Q + l < a.L, Ah, bias, l);
     pdt = pdt2;
