@@ -55,12 +55,13 @@ __device__ __forceinline__ void store4(float* p, const float v[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// round to nearest even, two values per v_cvt_pk_bf16_f32
 __device__ __forceinline__ void store4(bf16_t* p, const float v[4]) {
-  bf16_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) from_f32(v[i], &o[i]);
-  *reinterpret_cast<uint2*>(p) = make_uint2(static_cast<uint32_t>(o[0].bits) | (static_cast<uint32_t>(o[1].bits) << 16),
-                                            static_cast<uint32_t>(o[2].bits) | (static_cast<uint32_t>(o[3].bits) << 16));
+  const f32x4 f = {v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, __builtin_convertvector(f, bf16x4));
 }
 
 // Raw 4-element row chunks, kept undecoded while a load is in flight.

@@ -19,12 +19,9 @@ __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(static_cast<uint32_t>(v.bits) << 16); }
 
 __device__ __forceinline__ void from_f32(float v, float* dst) { *dst = v; }
-// Round to nearest even; NaN stays a quiet NaN.
+// Round to nearest even (the hardware conversion, v_cvt_pk_bf16_f32); NaN stays NaN.
 __device__ __forceinline__ void from_f32(float v, bf16_t* dst) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t qnan = (u >> 16) | 0x40u;
-  dst->bits = static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? qnan : rounded);
+  dst->bits = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
