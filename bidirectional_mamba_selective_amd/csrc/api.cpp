@@ -283,7 +283,7 @@ static int conv_impl(const void* u, const float* w_f, const float* b_f, const fl
                      int64_t C, int64_t d_conv, int io_dtype, uint32_t flags, hipStream_t stream, bool block) {
   if (batch <= 0 || L <= 0 || C <= 0 || d_conv <= 0) return BIMAMBA_ERR_INVALID_ARGUMENT;
   if (io_dtype != BIMAMBA_F32 && io_dtype != BIMAMBA_BF16) return BIMAMBA_ERR_UNSUPPORTED;
-  if (d_conv != 4 || C % 4 != 0) return BIMAMBA_ERR_UNSUPPORTED;
+  if (d_conv != 4 || C % 4 != 0 || C > (int64_t{1} << 22)) return BIMAMBA_ERR_UNSUPPORTED;  // a tile's rows fit a buffer
   if (batch > 65535 || L > INT32_MAX / 2 || static_cast<double>((L + 63) / 64) * ((C / 4 + 255) / 256) > 2.0e9)
     return BIMAMBA_ERR_UNSUPPORTED;
   if (flags & ~static_cast<uint32_t>(BIMAMBA_FLAG_NO_SILU)) return BIMAMBA_ERR_INVALID_ARGUMENT;

@@ -64,33 +64,59 @@ __device__ __forceinline__ void store4(bf16_t* p, const float v[4]) {
   *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, __builtin_convertvector(f, bf16x4));
 }
 
+// Buffer resources.  A tile's first row is the base of its resources and the
+// row offset goes into the VGPR offset together with the lane's channels.  The
+// hardware range check of a raw buffer access (offset >= num_records: a load
+// returns 0, a store is dropped) supplies the zero padding past the sequence end
+// and drops the outputs past it, so no access needs a guard.
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor, untyped 32-bit data format
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           kRsrcWord3);
+}
+
 // Raw 4-element row chunks, kept undecoded while a load is in flight.
 template <typename T>
 struct Raw;
 
 template <>
 struct Raw<float> {
-  float4 v;
-  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
-  __device__ __forceinline__ void zero() { v = make_float4(0.f, 0.f, 0.f, 0.f); }
+  u32x4 v;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  }
   __device__ __forceinline__ void get(float o[4]) const {
-    o[0] = v.x;
-    o[1] = v.y;
-    o[2] = v.z;
-    o[3] = v.w;
+    o[0] = __uint_as_float(v.x);
+    o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z);
+    o[3] = __uint_as_float(v.w);
+  }
+  static __device__ __forceinline__ void store(const float o[4], __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 q = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(q, r, off, 0, 0);
   }
 };
 
 template <>
 struct Raw<bf16_t> {
-  uint2 v;
-  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ void zero() { v = make_uint2(0, 0); }
+  u32x2 v;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  }
   __device__ __forceinline__ void get(float o[4]) const {
     o[0] = __uint_as_float(v.x << 16);
     o[1] = __uint_as_float(v.x & 0xffff0000u);
     o[2] = __uint_as_float(v.y << 16);
     o[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+  // round to nearest even, two values per v_cvt_pk_bf16_f32
+  static __device__ __forceinline__ void store(const float o[4], __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const f32x4 f = {o[0], o[1], o[2], o[3]};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4)), r, off, 0,
+                                          0);
   }
 };
 
@@ -111,10 +137,14 @@ struct Args {
   T* out_f;            // [batch, L, C] or null
   T* out_r;
   int64_t L, C;
-  int act;
 };
 
-template <typename T>
+template <bool ACT>
+__device__ __forceinline__ float act_f32(float s) {
+  return ACT ? silu_f32(s) : s;
+}
+
+template <typename T, bool ACT>
 __global__ __launch_bounds__(kThreads) void k_conv(Args<T> a) {
   // workgroups walk the channel blocks of a tile first, so that the ones in flight read whole rows
   const int64_t cblocks = (a.C / 4 + kThreads - 1) / kThreads;
@@ -137,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void k_conv(Args<T> a) {
     brv[i] = (do_r && a.b_r) ? a.b_r[c0 + i] : 0.0f;
   }
 
-  // row t of the (cache ++ sequence ++ zeros) input, channels c0..c0+3
+  // row t of the (cache ++ sequence ++ zeros) input, channels c0..c0+3 (tile edges only)
   auto row = [&](int64_t t, float v[4]) {
     if (t >= 0 && t < a.L) {
       load4(a.u + (b * a.L + t) * a.C + c0, v);
@@ -148,38 +178,43 @@ __global__ __launch_bounds__(kThreads) void k_conv(Args<T> a) {
     }
   };
 
-  // cache rows are read before anything is written, so cache_out may alias cache_in
-  float cache[kK - 1][4];
-  const bool first_tile = tile == 0;
-  if (first_tile && a.cache_out) {
-#pragma unroll
-    for (int m = 0; m < kK - 1; ++m) row(m - (kK - 1), cache[m]);
-  }
+  // this tile's rows t0 .. t0 + 66 (its tokens and the 3 after them) and its output rows t0 .. t0 + 63;
+  // the resources end at the sequence end
+  const uint32_t row_bytes = static_cast<uint32_t>(a.C) * static_cast<uint32_t>(sizeof(T));
+  const int64_t left = a.L - t0;
+  const uint32_t in_rows = static_cast<uint32_t>(left < kTile + kK - 1 ? left : kTile + kK - 1);
+  const uint32_t out_rows = static_cast<uint32_t>(left < kTile ? left : kTile);
+  const int64_t base = (b * a.L + t0) * a.C;
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.u + base, in_rows * row_bytes);
+  const __amdgpu_buffer_rsrc_t rf = make_rsrc(do_f ? a.out_f + base : nullptr, do_f ? out_rows * row_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(do_r ? a.out_r + base : nullptr, do_r ? out_rows * row_bytes : 0u);
+  const uint32_t lane_off = static_cast<uint32_t>(c0) * static_cast<uint32_t>(sizeof(T));
 
   float win[kWin][4];  // win[m] = row t_blk - 3 + m
 #pragma unroll
-  for (int m = 0; m < 2 * (kK - 1); ++m) row(t0 - (kK - 1) + m, win[m]);
+  for (int m = 0; m < kK - 1; ++m) row(t0 - (kK - 1) + m, win[m]);
+  {
+    Raw<T> q[kK - 1];
+#pragma unroll
+    for (int m = 0; m < kK - 1; ++m) q[m].load(ru, lane_off + m * row_bytes);
+#pragma unroll
+    for (int m = 0; m < kK - 1; ++m) q[m].get(win[kK - 1 + m]);
+  }
   // the rows a block adds to the window are loaded one block ahead
   Raw<T> nxt[kBlk];
-  auto fetch = [&](int64_t tb) {
+  auto fetch = [&](int blk) {
 #pragma unroll
-    for (int m = 0; m < kBlk; ++m) {
-      const int64_t t = tb + (kK - 1) + m;
-      if (t < a.L) nxt[m].load(a.u + (b * a.L + t) * a.C + c0);
-      else nxt[m].zero();
-    }
+    for (int m = 0; m < kBlk; ++m) nxt[m].load(ru, lane_off + (blk * kBlk + (kK - 1) + m) * row_bytes);
   };
-  fetch(t0);
+  fetch(0);
   for (int blk = 0; blk < kTile / kBlk; ++blk) {
-    const int64_t tb = t0 + blk * kBlk;
-    if (tb >= a.L) break;
+    if (t0 + blk * kBlk >= a.L) break;
 #pragma unroll
     for (int m = 0; m < kBlk; ++m) nxt[m].get(win[2 * (kK - 1) + m]);
-    if (blk + 1 < kTile / kBlk && tb + kBlk < a.L) fetch(tb + kBlk);
+    if (blk + 1 < kTile / kBlk) fetch(blk + 1);
 #pragma unroll
     for (int tt = 0; tt < kBlk; ++tt) {
-      const int64_t t = tb + tt;
-      if (t >= a.L) break;
+      const uint32_t off = lane_off + (blk * kBlk + tt) * row_bytes;
       if (do_f) {
         float o[4];
 #pragma unroll
@@ -187,9 +222,9 @@ __global__ __launch_bounds__(kThreads) void k_conv(Args<T> a) {
           float s = bfv[i];
 #pragma unroll
           for (int k = 0; k < kK; ++k) s = fmaf(wf[i][k], win[tt + k][i], s);
-          o[i] = a.act ? silu_f32(s) : s;
+          o[i] = act_f32<ACT>(s);
         }
-        store4(a.out_f + (b * a.L + t) * a.C + c0, o);
+        Raw<T>::store(o, rf, off);
       }
       if (do_r) {
         float o[4];
@@ -198,35 +233,28 @@ __global__ __launch_bounds__(kThreads) void k_conv(Args<T> a) {
           float s = brv[i];
 #pragma unroll
           for (int k = 0; k < kK; ++k) s = fmaf(wr[i][k], win[tt + 2 * (kK - 1) - k][i], s);
-          o[i] = a.act ? silu_f32(s) : s;
+          o[i] = act_f32<ACT>(s);
         }
-        store4(a.out_r + (b * a.L + t) * a.C + c0, o);
+        Raw<T>::store(o, rr, off);
       }
     }
 #pragma unroll
     for (int m = 0; m < 2 * (kK - 1); ++m) copy4(win[m], win[kBlk + m]);
   }
 
-  // the cache for the next block: the last 3 rows of (cache ++ sequence)
-  if (first_tile && a.cache_out) {
+  // The cache for the next block: the last 3 rows of (cache ++ sequence).  Only this thread touches
+  // these channels of the caches, and it reads all three rows before it writes any, so cache_out
+  // may alias cache_in.
+  if (tile == 0 && a.cache_out) {
+    float v[kK - 1][4];
 #pragma unroll
-    for (int m = 0; m < kK - 1; ++m) {
-      const int64_t t = a.L - (kK - 1) + m;
-      float v[4];
-      if (t >= 0) {
-        row(t, v);
-      } else {
-        // fewer than 3 tokens in the block: part of the new cache is the old one (index L + m < 3)
-        const int64_t j = a.L + m;
+    for (int m = 0; m < kK - 1; ++m) row(a.L - (kK - 1) + m, v[m]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = j == 0 ? cache[0][i] : (j == 1 ? cache[1][i] : cache[2][i]);
-      }
-      store4(a.cache_out + (b * (kK - 1) + m) * a.C + c0, v);
-    }
+    for (int m = 0; m < kK - 1; ++m) store4(a.cache_out + (b * (kK - 1) + m) * a.C + c0, v[m]);
   }
 }
 
-template <typename T>
+template <typename T, bool ACT>
 hipError_t launch_t(const ConvArgs& in, int64_t batch, int64_t L, int64_t C, hipStream_t stream) {
   Args<T> a{};
   a.u = static_cast<const T*>(in.u);
@@ -240,17 +268,21 @@ hipError_t launch_t(const ConvArgs& in, int64_t batch, int64_t L, int64_t C, hip
   a.out_r = static_cast<T*>(in.out_r);
   a.L = L;
   a.C = C;
-  a.act = in.act;
   const int64_t cblocks = (C / 4 + kThreads - 1) / kThreads;
   const dim3 grid(static_cast<unsigned>((L + kTile - 1) / kTile * cblocks), static_cast<unsigned>(batch));
-  hipLaunchKernelGGL(k_conv<T>, grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((k_conv<T, ACT>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_act(const ConvArgs& in, int64_t batch, int64_t L, int64_t C, hipStream_t stream) {
+  return in.act ? launch_t<T, true>(in, batch, L, C, stream) : launch_t<T, false>(in, batch, L, C, stream);
 }
 
 }  // namespace
 
 hipError_t launch_conv(const ConvArgs& a, int64_t batch, int64_t L, int64_t C, int io_dtype, hipStream_t stream) {
-  return io_dtype == 1 ? launch_t<bf16_t>(a, batch, L, C, stream) : launch_t<float>(a, batch, L, C, stream);
+  return io_dtype == 1 ? launch_act<bf16_t>(a, batch, L, C, stream) : launch_act<float>(a, batch, L, C, stream);
 }
 
 }  // namespace conv

@@ -205,7 +205,8 @@ int bimamba_ssd_fwd_stage(int stage, const void* x, const void* dt, const float*
  * [channels, d_conv] fp32; b_f, b_r [channels] fp32 or NULL (= 0).  For tied
  * weights pass the same pointers twice.  out_f or out_r may be NULL to skip
  * that direction (not both); its weights may then be NULL too.
- * Supported: d_conv 4, channels a multiple of 4, io_dtype F32 or BF16 (fp32
+ * Supported: d_conv 4, channels a multiple of 4 and at most 4194304 (2^22),
+ * batch at most 65535, io_dtype F32 or BF16 (fp32
  * arithmetic, round to nearest even for bf16).  u, outputs and caches must be
  * aligned to 4 elements (8 bytes bf16, 16 bytes fp32), weights and biases to 4
  * bytes.  flags: 0 or BIMAMBA_FLAG_NO_SILU.  Outputs must not overlap any

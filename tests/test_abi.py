@@ -285,6 +285,7 @@ def call_conv(block=False, **kw):
     (dict(k=0), INV),
     (dict(k=3), UNS),  # only width 4
     (dict(c=62), UNS),  # channels in groups of 4
+    (dict(c=(1 << 22) + 4), UNS),  # a tile's rows must fit one buffer resource
     (dict(io=5), UNS),
     (dict(batch=70000), UNS),
     (dict(flags=_lib.FLAG_NO_GATE), INV),
