@@ -70,6 +70,8 @@ __device__ __forceinline__ void store4(bf16_t* p, const float v[4]) {
 // returns 0, a store is dropped) supplies the zero padding past the sequence end
 // and drops the outputs past it, so no access needs a guard.
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor, untyped 32-bit data format
+// u and both outputs are streamed through once: non-temporal (the nt bit of the cache-policy field)
+constexpr int kStream = 2;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -86,7 +88,7 @@ template <>
 struct Raw<float> {
   u32x4 v;
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream);
   }
   __device__ __forceinline__ void get(float o[4]) const {
     o[0] = __uint_as_float(v.x);
@@ -96,7 +98,7 @@ struct Raw<float> {
   }
   static __device__ __forceinline__ void store(const float o[4], __amdgpu_buffer_rsrc_t r, uint32_t off) {
     const u32x4 q = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
-    __builtin_amdgcn_raw_buffer_store_b128(q, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(q, r, off, 0, kStream);
   }
 };
 
@@ -104,7 +106,7 @@ template <>
 struct Raw<bf16_t> {
   u32x2 v;
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStream);
   }
   __device__ __forceinline__ void get(float o[4]) const {
     o[0] = __uint_as_float(v.x << 16);
@@ -116,7 +118,7 @@ struct Raw<bf16_t> {
   static __device__ __forceinline__ void store(const float o[4], __amdgpu_buffer_rsrc_t r, uint32_t off) {
     const f32x4 f = {o[0], o[1], o[2], o[3]};
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4)), r, off, 0,
-                                          0);
+                                          kStream);
   }
 };
 

@@ -436,6 +436,7 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
                                                    __amdgpu_buffer_rsrc_t a2_rsrc, float qstep, float sj,
                                                    bool last, bool keep_hf) {
   constexpr bool kRev = (DIRS & 2) != 0;
+  constexpr bool kSum = DIRS == 3;
   // the forward chain runs for the forward readout or for the cached forward state
   const bool fwd_chain = (DIRS & 1) != 0 || keep_hf;
   const uint32_t voff4 = static_cast<uint32_t>(lane) * 4u;
@@ -473,10 +474,12 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
       a[k] = GEO ? a[k] * w[k] : fast_exp2(w[k] * a2);
       bb[k] = u[k] * bn[k];
     }
+    float hk[kSum ? SUB : 1];  // with both readouts: the forward state after token k
 #pragma unroll
     for (int k = 0; k < SUB; ++k) {
       if (fwd_chain) hf = fmaf(a[k], hf, bb[k]);
-      if (DIRS & 1) y[k] = fmaf(bn[SUB + k], hf, y[k]);
+      if (kSum) hk[kSum ? k : 0] = hf;
+      else if (DIRS & 1) y[k] = fmaf(bn[SUB + k], hf, y[k]);
     }
     if (kRev) {
       q = GEO ? q * qstep : fast_exp2(a2 * sj);
@@ -485,7 +488,8 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
 #pragma unroll
       for (int k = SUB - 1; k >= 0; --k) {
         hr = fmaf(a[k], hr, bb[k]);
-        y[k] = fmaf(bn[SUB + k], hr, y[k]);
+        // both readouts share one product with C_t[n]: C . h_fwd + C . h_rev = C . (h_fwd + h_rev)
+        y[k] = fmaf(bn[SUB + k], kSum ? hr + hk[kSum ? k : 0] : hr, y[k]);
       }
     }
     if (fwd_chain) sHf[n][lane] = hf;
