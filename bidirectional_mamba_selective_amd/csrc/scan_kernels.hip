@@ -619,19 +619,24 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
 // k_block: one short block of block-cache decoding in a single kernel (the
 // forward direction from the cached state, the reverse direction from zero at
 // the block's last token; the new cache is the forward state after the block).
-// grid (d_inner / 64, batch); a workgroup owns 64 channels (lane = channel) and
-// its wavefronts split the states, kSpw states each.  The block is padded to GM
-// tokens (GM in {16, 32, 64}); padding tokens have delta = 0 and no input, so
-// they leave every state unchanged and are never stored.
-//   1. all wavefronts: delta and delta*x of the block's tokens into LDS, B and C
-//      (fp32) into LDS;
-//   2. each wavefront, per state it owns: abar and delta*x*B for every token
-//      (kept in registers), the forward chain from h_in with its readout, then
-//      the reverse chain with its readout, into a per-wavefront partial y;
-//   3. the partials meet in LDS (the buffer of step 1, reused) and are summed in
-//      a fixed wavefront order (deterministic); skip term, gate, store.
-// With a few hundred wavefronts per call the block step costs one launch
-// instead of the chunked path's six.
+// grid (d_inner / 16, batch), block 256 (four wavefronts).  A workgroup owns 16
+// channels and every state of them: lane l of wavefront w runs channel
+// 16 blockIdx.x + l / 4 and state 4 w + l % 4, so the 16 x 16 recurrences of a
+// workgroup run side by side, one per lane, and a block step fills the chip
+// (d_inner / 16 workgroups).  The block is padded to GM tokens (GM in {16, 32,
+// 64}); padding tokens have delta = 0 and no input, so they leave every state
+// unchanged and are never stored.
+//   1. every global load of the kernel is issued at once, from clamped in-bounds
+//      addresses: the lane's A[d,n] and cached state, and per (token, channel)
+//      dt, x, z, and B, C; delta, delta*x, the skip term D*x and the gate SiLU(z)
+//      go to LDS, B and C (fp32) too;
+//   2. each lane: abar and delta*x*B per token in registers, the forward chain
+//      from the cache (its state per token kept), the new cache, then the
+//      reverse chain, and C_t[n] (h_fwd + h_rev) per token; the four states of a
+//      channel in a wavefront are summed across the lane quad (DPP), the four
+//      wavefronts' sums meet in LDS and are added in a fixed order
+//      (deterministic);
+//   3. skip term, gate, store.
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ float ld_any(const T* p);
@@ -652,119 +657,148 @@ __device__ __forceinline__ void st_any<bf16_t>(bf16_t* p, float v) {
 
 template <int GM>
 struct BlockSmem {
-  static constexpr int kSpw = GM <= 32 ? 1 : 2;        // states per wavefront
-  static constexpr int kMaxWaves = 16 / kSpw;          // d_state <= 16
-  union {
-    struct {
-      float dl[GM][64];
-      float u[GM][64];
-    } in;
-    float y[kMaxWaves][GM][64];
-  } s;
-  float b[16][GM];
-  float c[16][GM];
+  static constexpr int kRow = GM + 4;  // B and C rows padded: the four states a wavefront reads sit in different banks
+  float dl[GM][16];
+  float u[GM][16];
+  float sx[GM][16];  // skip * x
+  float g[GM][16];   // SiLU(z), or 1 without the gate
+  __attribute__((aligned(16))) float b[16][kRow];
+  __attribute__((aligned(16))) float c[16][kRow];
+  float part[4][GM][16];
 };
 
+// sum over the lane quad (the four states of a channel): lanes (0+1) + (2+3) in every quad
+__device__ __forceinline__ float quad_sum(float v) {
+  constexpr int kXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // quad_perm [1, 0, 3, 2]
+  constexpr int kXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);  // quad_perm [2, 3, 0, 1]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kXor1, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kXor2, 0xf, 0xf, false));
+  return v;
+}
+
 template <typename T, int GM>
-__global__ __launch_bounds__(GM <= 32 ? 1024 : 512) void k_block(
-    const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ z, const float* __restrict__ A,
-    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dv,
-    const float* __restrict__ dt_bias, const float* h_in, float* h_out, T* __restrict__ out, int G, int D, int N,
-    int flags) {
+__global__ __launch_bounds__(256) void k_block(const T* __restrict__ x, const T* __restrict__ dt,
+                                               const T* __restrict__ z, const float* __restrict__ A,
+                                               const T* __restrict__ Bm, const T* __restrict__ Cm,
+                                               const float* __restrict__ Dv, const float* __restrict__ dt_bias,
+                                               const float* h_in, float* h_out, T* __restrict__ out, int G, int D,
+                                               int N, int flags) {
   using S = BlockSmem<GM>;
+  constexpr int kTpt = GM / 16;  // (token, channel) pairs and B, C elements per thread
   __shared__ S sm;
-  const int nw = static_cast<int>(blockDim.x) / 64;
-  const int wv = threadIdx.x / 64;
-  const int lane = threadIdx.x % 64;
-  const int d = blockIdx.x * 64 + lane;
+  const int tid = threadIdx.x;
+  const int wv = tid / 64;
+  const int lane = tid % 64;
+  const int cl = lane >> 2;           // channel of this lane's recurrence, within the workgroup
+  const int n = wv * 4 + (lane & 3);  // its state
+  const int d = blockIdx.x * 16 + cl;
   const int b = blockIdx.y;
   const size_t row = static_cast<size_t>(b) * G;  // first token row of this batch element
   const bool gate = (flags & kNoGate) == 0;
   const bool fwd = (flags & kRevOnly) == 0;
   const bool rev = (flags & kFwdOnly) == 0;
 
-  // 1. delta, delta*x; B, C
-  const float bias = dt_bias ? dt_bias[d] : 0.0f;
-  for (int t = wv; t < GM; t += nw) {
-    float dl = 0.0f, u = 0.0f;
-    if (t < G) {
-      const size_t o = (row + t) * D + d;
-      dl = softplus_f32(ld_any(dt + o) + bias);
-      u = dl * ld_any(x + o);
-    }
-    sm.s.in.dl[t][lane] = dl;
-    sm.s.in.u[t][lane] = u;
+  // 1. All loads first, unconditionally from clamped addresses (a load under a branch is waited for
+  //    at the branch's end); the values are selected afterwards.  Stand-ins for absent tensors: A for
+  //    h_in, D and dt_bias, x for z (their values are not used).
+  const int nc = min(n, N - 1);
+  const float av = A[static_cast<size_t>(d) * N + nc];
+  const size_t hs = h_in ? (static_cast<size_t>(b) * D + d) * N + nc : static_cast<size_t>(d) * N + nc;
+  const float hv = (h_in ? h_in : A)[hs];  // read before any write: h_out may alias h_in
+  const int c1 = tid & 15;                 // channel of this thread's (token, channel) pairs
+  const int d1 = blockIdx.x * 16 + c1;
+  const float dvv = (Dv ? Dv : A)[d1];
+  const float bsv = (dt_bias ? dt_bias : A)[d1];
+  const T* zbase = gate ? z : x;
+  float xv[kTpt], dv[kTpt], zv[kTpt], bv[kTpt], cv[kTpt];
+#pragma unroll
+  for (int k = 0; k < kTpt; ++k) {
+    const int t = tid / 16 + 16 * k;
+    const size_t o = (row + min(t, G - 1)) * D + d1;
+    xv[k] = ld_any(x + o);
+    dv[k] = ld_any(dt + o);
+    zv[k] = ld_any(zbase + o);
+    const int i = tid + 256 * k;  // B, C element (state i / GM, token i % GM)
+    const size_t ob = (row + min(i % GM, G - 1)) * N + min(i / GM, N - 1);
+    bv[k] = ld_any(Bm + ob);
+    cv[k] = ld_any(Cm + ob);
   }
-  for (int i = threadIdx.x; i < N * GM; i += blockDim.x) {
-    const int n = i / GM;
-    const int t = i - n * GM;
-    float bv = 0.0f, cv = 0.0f;
-    if (t < G) {
-      bv = ld_any(Bm + (row + t) * N + n);
-      cv = ld_any(Cm + (row + t) * N + n);
-    }
-    sm.b[n][t] = bv;
-    sm.c[n][t] = cv;
+  const float bias = dt_bias ? bsv : 0.0f;
+  const float skip = Dv ? ((fwd && rev) ? 2.0f : 1.0f) * dvv : 0.0f;
+#pragma unroll
+  for (int k = 0; k < kTpt; ++k) {
+    const int t = tid / 16 + 16 * k;
+    const bool live = t < G;
+    const float dl = live ? softplus_f32(dv[k] + bias) : 0.0f;
+    const float xl = live ? xv[k] : 0.0f;
+    sm.dl[t][c1] = dl;
+    sm.u[t][c1] = dl * xl;
+    sm.sx[t][c1] = skip * xl;
+    sm.g[t][c1] = (live && gate) ? silu_f32(zv[k]) : 1.0f;
+    const int i = tid + 256 * k;
+    const bool ok = i / GM < N && i % GM < G;
+    sm.b[i / GM][i % GM] = ok ? bv[k] : 0.0f;
+    sm.c[i / GM][i % GM] = ok ? cv[k] : 0.0f;
   }
   __syncthreads();
 
-  // 2. the states of this wavefront
-  float y[GM];
+  // 2. this lane's recurrence (states n >= N have B = C = 0: they stay 0 and add nothing)
+  const float a2 = n < N ? av * kLog2e : 0.0f;
+  float a[GM], bb[GM], y[GM];
 #pragma unroll
-  for (int t = 0; t < GM; ++t) y[t] = 0.0f;
+  for (int t4 = 0; t4 < GM / 4; ++t4) {
+    const float4 bq = *reinterpret_cast<const float4*>(&sm.b[n][4 * t4]);
+    const float bq4[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
-  for (int q = 0; q < S::kSpw; ++q) {
-    const int n = wv * S::kSpw + q;
-    if (n < N) {
-      const float a2 = A[static_cast<size_t>(d) * N + n] * kLog2e;
-      float a[GM];
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * t4 + i;
+      a[t] = fast_exp2(sm.dl[t][cl] * a2);
+      bb[t] = sm.u[t][cl] * bq4[i];
+    }
+  }
+  float hf = (n < N && h_in) ? hv : 0.0f;
 #pragma unroll
-      for (int t = 0; t < GM; ++t) a[t] = fast_exp2(sm.s.in.dl[t][lane] * a2);
-      const size_t hs = (static_cast<size_t>(b) * D + d) * N + n;
-      float hf = h_in ? h_in[hs] : 0.0f;
+  for (int t = 0; t < GM; ++t) {
+    hf = fmaf(a[t], hf, bb[t]);
+    y[t] = fwd ? hf : 0.0f;
+  }
+  if (h_out && n < N) h_out[(static_cast<size_t>(b) * D + d) * N + n] = hf;  // padding leaves hf unchanged
+  float hr = 0.0f;
 #pragma unroll
-      for (int t = 0; t < GM; ++t) {
-        hf = fmaf(a[t], hf, sm.s.in.u[t][lane] * sm.b[n][t]);
-        if (fwd) y[t] = fmaf(sm.c[n][t], hf, y[t]);
-      }
-      if (h_out) h_out[hs] = hf;  // padding tokens leave hf unchanged
+  for (int t4 = GM / 4 - 1; t4 >= 0; --t4) {
+    const float4 cq = *reinterpret_cast<const float4*>(&sm.c[n][4 * t4]);
+    const float cq4[4] = {cq.x, cq.y, cq.z, cq.w};
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      const int t = 4 * t4 + i;
       if (rev) {
-        // delta*x*B is formed again from LDS rather than kept for every token in
-        // registers (the barrier keeps the compiler from reusing the first reads)
-        asm volatile("" ::: "memory");
-        float hr = 0.0f;
-#pragma unroll
-        for (int t = GM - 1; t >= 0; --t) {
-          hr = fmaf(a[t], hr, sm.s.in.u[t][lane] * sm.b[n][t]);
-          y[t] = fmaf(sm.c[n][t], hr, y[t]);
-        }
+        hr = fmaf(a[t], hr, bb[t]);
+        y[t] += hr;
       }
+      y[t] = quad_sum(y[t] * cq4[i]);
     }
   }
-
-  // 3. partials through LDS (reusing the step-1 buffer), fixed summation order
-  __syncthreads();  // every wavefront is done reading delta and delta*x
+  if ((lane & 3) == 0) {
 #pragma unroll
-  for (int t = 0; t < GM; ++t) sm.s.y[wv][t][lane] = y[t];
+    for (int t = 0; t < GM; ++t) sm.part[wv][t][cl] = y[t];
+  }
   __syncthreads();
-  const float ndir = (fwd && rev) ? 2.0f : 1.0f;
-  const float skip = Dv ? ndir * Dv[d] : 0.0f;
-  for (int t = wv; t < G; t += nw) {
-    float acc = 0.0f;
-    for (int w = 0; w < nw; ++w) acc += sm.s.y[w][t][lane];
-    const size_t o = (row + t) * D + d;
-    acc = fmaf(skip, ld_any(x + o), acc);
-    if (gate) acc *= silu_f32(ld_any(z + o));
-    st_any(out + o, acc);
+
+  // 3. the four wavefronts' sums in a fixed order; skip term, gate, store
+#pragma unroll
+  for (int k = 0; k < kTpt; ++k) {
+    const int t = tid / 16 + 16 * k;
+    if (t < G) {
+      const float acc = ((sm.part[0][t][c1] + sm.part[1][t][c1]) + sm.part[2][t][c1]) + sm.part[3][t][c1];
+      st_any(out + (row + t) * D + d1, (acc + sm.sx[t][c1]) * sm.g[t][c1]);
+    }
   }
 }
 
 template <typename T, int GM>
 static void launch_block_gm(const ScanArgs& a, int batch, int G, int D, int N, hipStream_t stream) {
-  using S = BlockSmem<GM>;
-  const int nw = (N + S::kSpw - 1) / S::kSpw;
-  const dim3 grid(static_cast<unsigned>(D / 64), static_cast<unsigned>(batch));
-  hipLaunchKernelGGL((k_block<T, GM>), grid, dim3(64 * nw), 0, stream, static_cast<const T*>(a.x),
+  const dim3 grid(static_cast<unsigned>(D / 16), static_cast<unsigned>(batch));
+  hipLaunchKernelGGL((k_block<T, GM>), grid, dim3(256), 0, stream, static_cast<const T*>(a.x),
                      static_cast<const T*>(a.dt), static_cast<const T*>(a.z), a.A, static_cast<const T*>(a.B),
                      static_cast<const T*>(a.C), a.D, a.dt_bias, a.h_in, a.h_out, static_cast<T*>(a.out), G, D, N,
                      static_cast<int>(a.flags));
