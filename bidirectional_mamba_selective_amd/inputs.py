@@ -182,3 +182,24 @@ def make_ssd_inputs(w: SSDWorkload, seed: int = 1):
     act = make_ssd_activations(w.batch, w.seqlen, w.nheads, w.headdim, w.d_state, w.io_dtype, seed=seed)
     act.update(A=A, D=D, dt_bias=dt_bias)
     return act
+
+
+def device_normals(shapes: dict, seed: int, io_dtype: str, device="cuda", scales: dict | None = None):
+    """Seeded N(0, scale^2) tensors drawn on the device with torch's generator (one stream per
+    call, tensors in the order given), each drawn in fp32, scaled and rounded once (round to
+    nearest even) to io_dtype.  The same distributions as `normal`, for tensors of several GiB
+    that would take minutes to draw on the host."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dtype = torch.bfloat16 if io_dtype == "bf16" else torch.float32
+    out = {}
+    for name, shape in shapes.items():
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        s = (scales or {}).get(name, 1.0)
+        if s != 1.0:
+            t.mul_(s)
+        out[name] = t.to(dtype)
+        del t
+    return out
