@@ -229,3 +229,24 @@ def test_staged_entry_point_matches_fused():
                                dev["dt_bias"], out=out, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(out, fused)
+
+
+@pytest.mark.parametrize("shift", [-60.0, 60.0])
+@pytest.mark.parametrize("G", [32, 100])
+def test_block_delta_limits(shift, G):
+    """The block step with dt_bias shifted far down (the cached state passes through unchanged) and
+    far up (the state forgets the cache), on the single-kernel and the chunked path (fp32 I/O)."""
+    import torch
+
+    inp = _case(2, G, 128, 16, "f32", seed=G + 7)
+    inp["dt_bias"] = (inp["dt_bias"] + np.float32(shift)).astype(np.float32)
+    h0 = np.random.default_rng(G + 7).standard_normal((2, 128, 16)).astype(np.float32)
+    dev = upload(inp, "f32")
+    h_in = f32_dev(h0)
+    h_out = torch.empty_like(h_in)
+    out = to_host64(_block_call(dev, dev, h_in, h_out))
+    want, want_h = oracle.scan_block(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                                     inp["dt_bias"], h0)
+    e_out, e_h = rel_err(out, want), rel_err(to_host64(h_out), want_h)
+    say(f"block G={G} dt_bias{shift:+.0f}: out {e_out:.3e} h_out {e_h:.3e}")
+    assert e_out <= 1e-4 and e_h <= 1e-5

@@ -168,3 +168,14 @@ def test_long_64k_general_A():
     inp = case(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype, a_jitter=0.2)
     chan = np.arange(17, w.d_inner, 211)
     check_variants(inp, w.io_dtype, variants=VARIANTS[1:2], chan=chan, tag="long_64k_jitterA")
+
+
+@pytest.mark.parametrize("shift", [-60.0, -20.0, 20.0, 60.0])
+@pytest.mark.parametrize("a_jitter", [0.0, 0.2])
+def test_delta_limits(shift, a_jitter):
+    """dt_bias shifted far down (delta -> 0: abar -> 1 and almost no input; at -60 the output is
+    2 D x SiLU(z) to within e^-60) and far up (delta ~ dt + bias: abar -> 0, the state is the
+    current input, powers of abar underflow) in fp32, both A paths, against the oracle."""
+    inp = case(2, 300, 128, 16, "f32", seed=int(abs(shift)) + 3, a_jitter=a_jitter)
+    inp["dt_bias"] = (inp["dt_bias"] + np.float32(shift)).astype(np.float32)
+    check_variants(inp, "f32", variants=VARIANTS[:2], tag=f"delta_shift{shift:+.0f}")
