@@ -32,7 +32,7 @@ struct ScanArgs {
 hipError_t launch_chunked(const ScanArgs& a, const Plan& p, void* workspace, hipStream_t stream, int stage = -1);
 
 // Single-kernel block step for block_len <= kBlockFusedMax: one workgroup per
-// (64 channels, batch element), its wavefronts splitting the states; no workspace.
+// (16 channels, batch element), one lane per (channel, state) recurrence; no workspace.
 hipError_t launch_block_fused(const ScanArgs& a, int64_t batch, int64_t block_len, int64_t d_inner,
                               int64_t d_state, hipStream_t stream);
 

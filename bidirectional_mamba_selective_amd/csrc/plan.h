@@ -16,7 +16,7 @@ constexpr int64_t kLanes = 64;
 // SIMD on a 256-CU part).
 constexpr int64_t kTargetWaves = 4096;
 // Longest block the single-kernel block path handles (it needs no workspace).
-constexpr int64_t kBlockFusedMax = 64;
+constexpr int64_t kBlockFusedMax = 128;
 
 struct Plan {
   int64_t batch, seqlen, d_inner, d_state;

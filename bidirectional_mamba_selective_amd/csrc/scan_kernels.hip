@@ -624,8 +624,8 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
 // 16 blockIdx.x + l / 4 and state 4 w + l % 4, so the 16 x 16 recurrences of a
 // workgroup run side by side, one per lane, and a block step fills the chip
 // (d_inner / 16 workgroups).  The block is padded to GM tokens (GM in {16, 32,
-// 64}); padding tokens have delta = 0 and no input, so they leave every state
-// unchanged and are never stored.
+// 64, 128}); padding tokens have delta = 0 and no input, so they leave every
+// state unchanged and are never stored.
 //   1. every global load of the kernel is issued at once, from clamped in-bounds
 //      addresses: the lane's A[d,n] and cached state, and per (token, channel)
 //      dt, x, z, and B, C; delta, delta*x, the skip term D*x and the gate SiLU(z)
@@ -744,38 +744,73 @@ __global__ __launch_bounds__(256) void k_block(const T* __restrict__ x, const T*
 
   // 2. this lane's recurrence (states n >= N have B = C = 0: they stay 0 and add nothing)
   const float a2 = n < N ? av * kLog2e : 0.0f;
-  float a[GM], bb[GM], y[GM];
-#pragma unroll
-  for (int t4 = 0; t4 < GM / 4; ++t4) {
-    const float4 bq = *reinterpret_cast<const float4*>(&sm.b[n][4 * t4]);
-    const float bq4[4] = {bq.x, bq.y, bq.z, bq.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * t4 + i;
-      a[t] = fast_exp2(sm.dl[t][cl] * a2);
-      bb[t] = sm.u[t][cl] * bq4[i];
-    }
-  }
+  float y[GM];
   float hf = (n < N && h_in) ? hv : 0.0f;
+  if constexpr (GM <= 64) {
+    float a[GM], bb[GM];
 #pragma unroll
-  for (int t = 0; t < GM; ++t) {
-    hf = fmaf(a[t], hf, bb[t]);
-    y[t] = fwd ? hf : 0.0f;
-  }
-  if (h_out && n < N) h_out[(static_cast<size_t>(b) * D + d) * N + n] = hf;  // padding leaves hf unchanged
-  float hr = 0.0f;
+    for (int t4 = 0; t4 < GM / 4; ++t4) {
+      const float4 bq = *reinterpret_cast<const float4*>(&sm.b[n][4 * t4]);
+      const float bq4[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
-  for (int t4 = GM / 4 - 1; t4 >= 0; --t4) {
-    const float4 cq = *reinterpret_cast<const float4*>(&sm.c[n][4 * t4]);
-    const float cq4[4] = {cq.x, cq.y, cq.z, cq.w};
-#pragma unroll
-    for (int i = 3; i >= 0; --i) {
-      const int t = 4 * t4 + i;
-      if (rev) {
-        hr = fmaf(a[t], hr, bb[t]);
-        y[t] += hr;
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * t4 + i;
+        a[t] = fast_exp2(sm.dl[t][cl] * a2);
+        bb[t] = sm.u[t][cl] * bq4[i];
       }
-      y[t] = quad_sum(y[t] * cq4[i]);
+    }
+#pragma unroll
+    for (int t = 0; t < GM; ++t) {
+      hf = fmaf(a[t], hf, bb[t]);
+      y[t] = fwd ? hf : 0.0f;
+    }
+    if (h_out && n < N) h_out[(static_cast<size_t>(b) * D + d) * N + n] = hf;  // padding leaves hf unchanged
+    float hr = 0.0f;
+#pragma unroll
+    for (int t4 = GM / 4 - 1; t4 >= 0; --t4) {
+      const float4 cq = *reinterpret_cast<const float4*>(&sm.c[n][4 * t4]);
+      const float cq4[4] = {cq.x, cq.y, cq.z, cq.w};
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        const int t = 4 * t4 + i;
+        if (rev) {
+          hr = fmaf(a[t], hr, bb[t]);
+          y[t] += hr;
+        }
+        y[t] = quad_sum(y[t] * cq4[i]);
+      }
+    }
+  } else {
+    // Longer blocks: abar and delta*x*B are formed again in the reverse pass (from the same LDS
+    // values, so bit for bit the same) instead of being kept for every token next to y.
+#pragma unroll
+    for (int t4 = 0; t4 < GM / 4; ++t4) {
+      const float4 bq = *reinterpret_cast<const float4*>(&sm.b[n][4 * t4]);
+      const float bq4[4] = {bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * t4 + i;
+        hf = fmaf(fast_exp2(sm.dl[t][cl] * a2), hf, sm.u[t][cl] * bq4[i]);
+        y[t] = fwd ? hf : 0.0f;
+      }
+    }
+    if (h_out && n < N) h_out[(static_cast<size_t>(b) * D + d) * N + n] = hf;  // padding leaves hf unchanged
+    float hr = 0.0f;
+#pragma unroll
+    for (int t4 = GM / 4 - 1; t4 >= 0; --t4) {
+      const float4 bq = *reinterpret_cast<const float4*>(&sm.b[n][4 * t4]);
+      const float4 cq = *reinterpret_cast<const float4*>(&sm.c[n][4 * t4]);
+      const float bq4[4] = {bq.x, bq.y, bq.z, bq.w};
+      const float cq4[4] = {cq.x, cq.y, cq.z, cq.w};
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        const int t = 4 * t4 + i;
+        if (rev) {
+          hr = fmaf(fast_exp2(sm.dl[t][cl] * a2), hr, sm.u[t][cl] * bq4[i]);
+          y[t] += hr;
+        }
+        y[t] = quad_sum(y[t] * cq4[i]);
+      }
     }
   }
   if ((lane & 3) == 0) {
@@ -810,8 +845,10 @@ static hipError_t launch_block_typed(const ScanArgs& a, int batch, int G, int D,
     launch_block_gm<T, 16>(a, batch, G, D, N, stream);
   } else if (G <= 32) {
     launch_block_gm<T, 32>(a, batch, G, D, N, stream);
-  } else {
+  } else if (G <= 64) {
     launch_block_gm<T, 64>(a, batch, G, D, N, stream);
+  } else {
+    launch_block_gm<T, 128>(a, batch, G, D, N, stream);
   }
   return hipGetLastError();
 }

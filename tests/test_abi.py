@@ -152,16 +152,16 @@ def test_scan_block_rejects(kw, want):
 
 def test_block_workspace_only_past_the_single_kernel_limit():
     f = _lib.bimamba_scan_block_workspace_bytes
-    # blocks of up to 64 tokens run as one kernel and need no workspace
-    assert [f(1, g, 4096, 16) for g in (1, 16, 32, 64)] == [0, 0, 0, 0]
-    assert f(1, 65, 4096, 16) > 0 and f(2, 100, 64, 16) > 0
+    # blocks of up to 128 tokens run as one kernel and need no workspace
+    assert [f(1, g, 4096, 16) for g in (1, 16, 32, 64, 65, 128)] == [0] * 6
+    assert f(1, 129, 4096, 16) > 0 and f(2, 200, 64, 16) > 0
     assert f(1, 100, 100, 16) == 0  # unsupported shape
 
 
 def test_scan_block_allows_in_place_state():
     # a block past the single-kernel limit: the call then stops at the workspace size check
-    assert call_block(L=100, h_out=fake(10), wsb=0) == WS  # h_out == h_in is accepted
-    assert call_block(L=100, h_in=None, h_out=None, wsb=0) == WS
+    assert call_block(L=200, h_out=fake(10), wsb=0) == WS  # h_out == h_in is accepted
+    assert call_block(L=200, h_in=None, h_out=None, wsb=0) == WS
 
 
 def call_untied(**kw):

@@ -52,7 +52,7 @@ def _slice(dev, b0, b1):
     return {k: dev[k][:, b0:b1].contiguous() for k in ("x", "dt", "z", "B", "C")}
 
 
-@pytest.mark.parametrize("G", [1, 5, 16, 32, 64, 100])
+@pytest.mark.parametrize("G", [1, 5, 16, 32, 64, 100, 128, 129, 200])
 @pytest.mark.parametrize("flags", [0, NO_GATE, FWD_ONLY, REV_ONLY | NO_GATE])
 def test_block_small(G, flags):
     """One block with a random cached state; out and h_out against oracle.scan_block (fp32 I/O)."""
@@ -98,11 +98,11 @@ def test_block_state_counts(N, G, jitter):
     assert e_out <= 1e-4 and e_h <= 1e-5
 
 
-@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("G", [32, 64, 128, 200])
 def test_block_reruns_then_commit(G):
     """Block-diffusion decoding: the active block is denoised k = 4 times from the same cached state
-    (fresh x, z each time; the cache is not written), then committed once (cache updated). Blocks of 32
-    and 64 tokens take the single-kernel path, 128 the chunked one; bf16 I/O at d_inner 256."""
+    (fresh x, z each time; the cache is not written), then committed once (cache updated). Blocks of up
+    to 128 tokens take the single-kernel path, 200 the chunked one; bf16 I/O at d_inner 256."""
     import torch
 
     from bidirectional_mamba_selective_amd import bimamba_scan_block
@@ -232,7 +232,7 @@ def test_staged_entry_point_matches_fused():
 
 
 @pytest.mark.parametrize("shift", [-60.0, 60.0])
-@pytest.mark.parametrize("G", [32, 100])
+@pytest.mark.parametrize("G", [32, 100, 200])
 def test_block_delta_limits(shift, G):
     """The block step with dt_bias shifted far down (the cached state passes through unchanged) and
     far up (the state forgets the cache), on the single-kernel and the chunked path (fp32 I/O)."""
