@@ -12,6 +12,12 @@ Besides the headline tokens/s the line carries:
                 its duration measured live with HIP events on the stream the
                 library launches on (staged entry point, same arguments);
   hbm           algorithmic bytes of the whole call / step time vs 8 TB/s;
+  general_A, untied, ssd, conv
+                the same shape off the geometric A path, with untied directions,
+                the Mamba-2 heads and the short convolution (each with its own
+                roofline where it has one);
+  other_configs the batched workload (fresh x, z per call) and the block-variant
+                sweep (--no-configs skips them);
   cpu_baseline  the fp64 oracle timed on this host on a bounded channel sample.
 """
 from __future__ import annotations
@@ -239,7 +245,41 @@ def bench_block(args, w, torch, bm, I, dev):
         "workspace_bytes": need,
         "us_per_block_call_graph": call_us,
     }
-    print(json.dumps(line), flush=True)
+    return line
+
+
+def bench_batched(args, torch, bm, I, dev, stream, calls=16):
+    """The batched workload as a denoising loop: `calls` calls with fresh x, z per call (drawn on the
+    device outside the timed region, seed 1000 + call) and dt, B, C, A, D, dt_bias held fixed; each call
+    timed with HIP events on the library's stream."""
+    w = I.WORKLOADS["batched_8k_bf16"]
+    log(f"batched workload {w.name}: batch {w.batch} L {w.seqlen} d_inner {w.d_inner} d_state {w.d_state}, "
+        f"{calls} calls with fresh x, z")
+    shp = (w.batch, w.seqlen, w.d_inner)
+    fixed = I.device_normals({"dt": shp, "B": (w.batch, w.seqlen, w.d_state), "C": (w.batch, w.seqlen, w.d_state)},
+                             seed=1, io_dtype=w.io_dtype, device=dev, scales={"dt": 0.5})
+    A, Dv, bias = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+                   for a in I.make_params(w.d_inner, w.d_state))
+    need = bm.bimamba_scan_fwd_workspace_bytes(w.batch, w.seqlen, w.d_inner, w.d_state)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty(shp, dtype=torch.bfloat16, device=dev)
+    ms = []
+    for s in range(calls + 2):
+        xz = I.device_normals({"x": shp, "z": shp}, seed=1000 + s, io_dtype=w.io_dtype, device=dev)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        bm.bimamba_scan_fwd(xz["x"], fixed["dt"], A, fixed["B"], fixed["C"], Dv, xz["z"], bias, out=out, workspace=ws,
+                            stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if s >= 2:  # the first two calls warm up
+            ms.append(e0.elapsed_time(e1))
+    m = float(np.mean(ms))
+    log(f"batched: {m:.4f} ms per call (mean of {calls})")
+    return {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "d_inner": w.d_inner, "d_state": w.d_state,
+            "calls": calls, "ms_per_call": round(m, 4), "tokens_per_s": round(w.batch * w.seqlen / (m * 1e-3), 1),
+            "note": "fresh x, z per call drawn on the device outside the timed region; per-call HIP events"}
 
 
 # matrix-core products per (64-token run, head) of the two SSD sweeps, and per run of the tiling kernel
@@ -366,6 +406,8 @@ def main():
     ap.add_argument("--cpu-channels", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ssd", action="store_true", help="skip the Mamba-2 (SSD) heads measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the batched and block-variant workloads reported beside the headline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
     args = ap.parse_args()
@@ -386,7 +428,8 @@ def main():
     torch.cuda.set_device(dev)
     bm.load()
     if w.block_len:
-        return bench_block(args, w, torch, bm, I, dev)
+        print(json.dumps(bench_block(args, w, torch, bm, I, dev)), flush=True)
+        return
 
     log(f"workload {w.name}: batch {w.batch} L {w.seqlen} d_inner {w.d_inner} d_state {w.d_state} {w.io_dtype}")
     t0 = time.perf_counter()
@@ -535,6 +578,15 @@ def main():
         line["ssd"] = bench_ssd(args, torch, bm, I, dev, stream)
         torch.cuda.empty_cache()
         line["conv"] = bench_conv(args, torch, bm, I, dev, stream)
+    if not args.no_configs and w.name == "long_64k_bf16":
+        torch.cuda.empty_cache()
+        other = {"batched_8k_bf16": bench_batched(args, torch, bm, I, dev, stream)}
+        torch.cuda.empty_cache()
+        bl = bench_block(argparse.Namespace(steps=3, warmup=1), I.WORKLOADS["block_32k_bf16"], torch, bm, I, dev)
+        other["block_32k_bf16"] = {k: bl[k] for k in ("value", "unit", "ms_per_step", "us_per_block_graph",
+                                                       "us_per_block_eager", "us_per_block_call_graph")}
+        other["block_32k_bf16"]["metric"] = bl["metric"]
+        line["other_configs"] = other
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_channels} channels")
         line["cpu_baseline"] = cpu_baseline(inp, w.seqlen, w.d_inner, min(args.cpu_channels, w.d_inner))
