@@ -126,6 +126,15 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _nbytes(t):
+    """Bytes of a caller-provided workspace tensor (any dtype; it must be contiguous); 0 for None."""
+    if t is None:
+        return 0
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return t.numel() * t.element_size()
+
+
 def _io_dtype(x):
     torch = _torch()
     if x.dtype == torch.bfloat16:
@@ -186,7 +195,7 @@ def bimamba_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, fla
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = lib.bimamba_scan_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
-                              _ptr(out), nb, L, nd, ns, _io_dtype(x), flags, _ptr(workspace), workspace.numel(),
+                              _ptr(out), nb, L, nd, ns, _io_dtype(x), flags, _ptr(workspace), _nbytes(workspace),
                               _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_scan_fwd")
@@ -211,7 +220,7 @@ def bimamba_scan_fwd_untied(fwd, rev, out_f=None, out_r=None, flags: int = 0, wo
     ptrs = [_ptr(f[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")] + [_ptr(out_f)]
     ptrs += [_ptr(r[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")] + [_ptr(out_r)]
     st = lib.bimamba_scan_fwd_untied(*ptrs, nb, L, nd, ns, _io_dtype(f["x"]), flags, _ptr(workspace),
-                                     workspace.numel(), _stream(stream, f["x"].device))
+                                     _nbytes(workspace), _stream(stream, f["x"].device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_scan_fwd_untied")
     return out_f, out_r
@@ -226,7 +235,7 @@ def bimamba_scan_fwd_stage(stage: int, x, dt, A, B, C, D=None, z=None, dt_bias=N
         raise ValueError("the staged entry point needs a caller-kept workspace")
     st = load().bimamba_scan_fwd_stage(int(stage), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                        _ptr(dt_bias), _ptr(out), nb, L, nd, ns, _io_dtype(x), flags, _ptr(workspace),
-                                       workspace.numel(), _stream(stream, x.device))
+                                       _nbytes(workspace), _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, f"bimamba_scan_fwd_stage({stage})")
     return out
@@ -244,7 +253,7 @@ def bimamba_scan_block(x, dt, A, B, C, D=None, z=None, dt_bias=None, h_in=None, 
     need = int(lib.bimamba_scan_block_workspace_bytes(nb, L, nd, ns))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    wbytes = 0 if workspace is None else workspace.numel()
+    wbytes = _nbytes(workspace)
     st = lib.bimamba_scan_block(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
                                 _ptr(h_in), _ptr(h_out), _ptr(out), nb, L, nd, ns, _io_dtype(x), flags,
                                 _ptr(workspace), wbytes, _stream(stream, x.device))
@@ -294,7 +303,7 @@ def bimamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, flag
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = lib.bimamba_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
-                             _ptr(out), nb, L, nh, hp, ns, _io_dtype(x), flags, _ptr(workspace), workspace.numel(),
+                             _ptr(out), nb, L, nh, hp, ns, _io_dtype(x), flags, _ptr(workspace), _nbytes(workspace),
                              _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_ssd_fwd")
@@ -309,7 +318,7 @@ def bimamba_ssd_fwd_stage(stage: int, x, dt, A, B, C, D=None, z=None, dt_bias=No
         raise ValueError("the staged entry point needs a caller-kept workspace")
     st = load().bimamba_ssd_fwd_stage(int(stage), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                       _ptr(dt_bias), _ptr(out), nb, L, nh, hp, ns, _io_dtype(x), flags,
-                                      _ptr(workspace), workspace.numel(), _stream(stream, x.device))
+                                      _ptr(workspace), _nbytes(workspace), _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, f"bimamba_ssd_fwd_stage({stage})")
     return out

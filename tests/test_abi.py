@@ -307,3 +307,13 @@ def test_conv_cache_arguments():
     assert call_conv(block=True, cout=fake(7, 16)) == INV
     assert call_conv(block=True, cin=fake(6, 8)) == INV  # partial overlap of the two caches
     assert call_conv(block=True, of=fake(5, 0)) == INV  # output over cache_in
+
+
+def test_binding_counts_workspace_bytes():
+    import torch
+
+    assert _lib._nbytes(None) == 0
+    assert _lib._nbytes(torch.empty(10, dtype=torch.uint8)) == 10
+    assert _lib._nbytes(torch.empty(10, dtype=torch.float32)) == 40  # any dtype: bytes, not elements
+    with pytest.raises(ValueError):
+        _lib._nbytes(torch.empty(4, 4, dtype=torch.uint8).t())
