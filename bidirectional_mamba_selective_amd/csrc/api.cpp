@@ -193,6 +193,19 @@ int bimamba_scan_block(const void* x, const void* dt, const float* A, const void
   const size_t es = io_dtype == BIMAMBA_BF16 ? 2 : 4;
   const size_t out_bytes = static_cast<size_t>(batch) * block_len * d_inner * es;
   if (h_out && overlap(range_of(h_out, st_bytes), range_of(out, out_bytes))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (h_in && overlap(range_of(h_in, st_bytes), range_of(out, out_bytes))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (h_out) {
+    // the new cache is written while other workgroups still read the block's inputs
+    const Range ho = range_of(h_out, st_bytes);
+    const size_t act = static_cast<size_t>(batch) * block_len * d_inner * es;
+    const size_t bc = static_cast<size_t>(batch) * block_len * d_state * es;
+    if (overlap(ho, range_of(x, act)) || overlap(ho, range_of(dt, act)) || (z && overlap(ho, range_of(z, act))) ||
+        overlap(ho, range_of(B, bc)) || overlap(ho, range_of(C, bc)) ||
+        overlap(ho, range_of(A, static_cast<size_t>(d_inner) * d_state * 4)) ||
+        (D && overlap(ho, range_of(D, static_cast<size_t>(d_inner) * 4))) ||
+        (dt_bias && overlap(ho, range_of(dt_bias, static_cast<size_t>(d_inner) * 4))))
+      return BIMAMBA_ERR_INVALID_ARGUMENT;
+  }
   bimamba::ScanArgs a{x, dt, A, B, C, D, z, dt_bias, out, h_in, h_out, io_dtype, flags};
   if (block_len <= bimamba::kBlockFusedMax) {
     // single-kernel path: the workspace is not used (it may be NULL)

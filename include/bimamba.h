@@ -143,8 +143,9 @@ size_t bimamba_scan_block_workspace_bytes(int64_t batch, int64_t block_len, int6
  *   h_out: [batch, d_inner, d_state] fp32, receives the forward state after the
  *          block's last token (the cache for the next block); NULL means do not
  *          write.  h_out may equal h_in (in-place commit) but must not
- *          otherwise overlap it.  The flags select the directions summed into
- *          out; h_out is the forward state in every case.
+ *          otherwise overlap it, nor any input or out; h_in must not overlap
+ *          out.  The flags select the directions summed into out; h_out is the
+ *          forward state in every case.
  * workspace may be NULL when bimamba_scan_block_workspace_bytes returns 0. */
 int bimamba_scan_block(const void* x, const void* dt, const float* A, const void* B, const void* C,
                        const float* D, const void* z, const float* dt_bias,

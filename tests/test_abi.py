@@ -142,6 +142,10 @@ def test_scan_fwd_checks_run_in_order():
     (dict(h_in=fake(10, 8)), INV),  # misaligned state
     (dict(h_out=fake(10, 256)), INV),  # partial overlap with h_in
     (dict(h_out=fake(8, 0)), INV),  # h_out overlaps out
+    (dict(h_in=fake(8, 0), h_out=None), INV),  # h_in overlaps out
+    (dict(h_out=fake(0, 0)), INV),  # h_out over x
+    (dict(h_out=fake(3, 0)), INV),  # h_out over B
+    (dict(h_out=fake(2, 0)), INV),  # h_out over A
     (dict(x=None), INV),
     (dict(L=0), INV),
     (dict(n=20), UNS),
