@@ -28,7 +28,8 @@ width implies):
   G_t[h]        = abar[t, h] * G_{t+1}[h] + Delta[t, h] * x_t[h, :] (outer) B_t
   y_dir[t, h, p] = sum_n C_t[n] * state_t[h, p, n] + D[h] * x_t[h, p]
   out           = (y_fwd + y_rev) * z * sigmoid(z)
-with H, G of shape [headdim, d_state] per head, H_{-1} = G_L = 0.
+with H, G of shape [headdim, d_state] per head, H_{-1} = G_L = 0 (for one block
+of block-cache decoding, H_{-1} is the cached state; see ssd_scan_block).
 
 Shapes: x, z, out are [batch, L, nheads * headdim] with channel c = h *
 headdim + p; dt is [batch, L, nheads]; B, C are [batch, L, d_state]; A, D and
@@ -41,7 +42,7 @@ import numpy as np
 
 from .scan import silu, softplus
 
-__all__ = ["ssd_discretise", "ssd_forward_scan", "ssd_reverse_scan", "ssd_scan_fwd"]
+__all__ = ["ssd_discretise", "ssd_forward_scan", "ssd_reverse_scan", "ssd_scan_fwd", "ssd_scan_block"]
 
 
 def _f64(a):
@@ -116,6 +117,20 @@ def ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, *, gate=True, fwd
     gate=False drops the SiLU factor; fwd/rev select the directions kept.
     D=None and dt_bias=None mean zero.  The head count is len(A).
     """
+    return ssd_scan_block(x, dt, A, B, C, D, z, dt_bias, None, gate=gate, fwd=fwd, rev=rev)[0]
+
+
+def ssd_scan_block(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, *, gate=True, fwd=True, rev=True):
+    """One block of block-cache decoding with Mamba-2 heads: (out, h_next).
+
+    Section 4.3 (block-cache paragraph): the left-to-right state is cached from
+    the blocks before and carried into this one, while the right-to-left state
+    stays inside the active block.  So the forward recurrence starts from h0
+    ([batch, nheads, headdim, d_state]; zeros when None), the reverse one from
+    zero after the block's last token, and h_next is the forward state after
+    the block's last token (the cache of the next block) whatever directions
+    out keeps.  With h0 = None this is the full-sequence scan.
+    """
     if gate and z is None:
         raise ValueError("z is required when the gate is applied")
     A = _f64(A)
@@ -124,14 +139,15 @@ def ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, *, gate=True, fwd
     delta = ssd_discretise(dt, dt_bias)
     if delta.shape[-1] != nh:
         raise ValueError("dt must hold one value per (token, head)")
+    y_f, h_next = ssd_forward_scan(delta, xh, A, B, C, h0)
     out = np.zeros_like(xh)
-    for keep, scan in ((fwd, ssd_forward_scan), (rev, ssd_reverse_scan)):
+    for keep, y in ((fwd, y_f), (rev, ssd_reverse_scan(delta, xh, A, B, C)[0] if rev else None)):
         if not keep:
             continue
-        out = out + scan(delta, xh, A, B, C)[0]
+        out = out + y
         if D is not None:
             out = out + _f64(D)[None, None, :, None] * xh
     out = out.reshape(_f64(x).shape)
     if gate:
         out = out * silu(z)
-    return out
+    return out, h_next

@@ -214,6 +214,38 @@ def pin_ssd_linearity(impl):
     return err < 1e-12, f"rel err {err:.3e}"
 
 
+def pin_ssd_block_chaining(impl):
+    """S9: block-cache decoding (Section 4.3, block-cache paragraph).  Chaining blocks through the cached
+    forward state reproduces the full forward scan; each block's reverse output is the reverse scan of
+    that block alone; the cache equals the closed-form forward state at the block's end (whatever
+    directions the output keeps)."""
+    rng = np.random.default_rng(590)
+    nb, L, nh, hp, ns, G = 2, 40, 2, 3, 4, 8
+    case = rand_case(rng, nb, L, nh, hp, ns)
+    full_f = call(impl, case, fwd=True, rev=False, gate=False)
+    dl = _softplus(case["dt"] + case["dt_bias"][None, None, :])
+    xh = case["x"].reshape(nb, L, nh, hp)
+    h = None
+    worst = 0.0
+    for b0 in range(0, L, G):
+        sl = {k: (case[k][:, b0:b0 + G] if k in ("x", "dt", "z", "B", "C") else case[k]) for k in case}
+        args = [sl[k] for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")]
+        out_f, h_next = impl.ssd_scan_block(*args, h, gate=False, fwd=True, rev=False)
+        worst = max(worst, _rel(out_f, full_f[:, b0:b0 + G]))
+        out_r, h_r = impl.ssd_scan_block(*args, h, gate=False, fwd=False, rev=True)
+        worst = max(worst, _rel(out_r, call(impl, sl, fwd=False, rev=True, gate=False)))
+        worst = max(worst, _rel(h_r, h_next))
+        te = b0 + G - 1
+        want = np.zeros((nb, nh, hp, ns))
+        for s_ in range(te + 1):
+            seg = dl[:, s_ + 1:te + 1, :].sum(axis=1)  # [nb, nh]
+            term = (dl[:, s_, :, None] * xh[:, s_])[:, :, :, None] * case["B"][:, s_, None, None, :]
+            want += np.exp(case["A"][None] * seg)[:, :, None, None] * term
+        worst = max(worst, _rel(h_next, want))
+        h = h_next
+    return worst < 1e-12, f"max rel err {worst:.3e}"
+
+
 ALL_SSD_PINS = [
     pin_ssd_brute_force,
     pin_ssd_is_tied_s6,
@@ -223,4 +255,5 @@ ALL_SSD_PINS = [
     pin_ssd_head_independence,
     pin_ssd_states,
     pin_ssd_linearity,
+    pin_ssd_block_chaining,
 ]

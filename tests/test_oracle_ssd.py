@@ -57,6 +57,29 @@ def _discretise_heads_reversed(dt, dt_bias):
 
 
 _orig_discretise = ossd.ssd_discretise
+_orig_block = ossd.ssd_scan_block
+
+
+def _block_reverse_from_cache(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, **kw):
+    """The block's reverse recurrence wrongly starts from the cached forward state."""
+    if h0 is None or not kw.get("rev", True):
+        return _orig_block(x, dt, A, B, C, D, z, dt_bias, h0, **kw)
+    out, h_next = _orig_block(x, dt, A, B, C, D, z, dt_bias, h0, **kw)
+    nh = len(A)
+    xh = ossd._heads(x, nh)
+    delta = ossd.ssd_discretise(dt, dt_bias)
+    extra = ossd.ssd_reverse_scan(delta, xh, A, B, C, h0)[0] - ossd.ssd_reverse_scan(delta, xh, A, B, C)[0]
+    extra = extra.reshape(np.shape(x))
+    if kw.get("gate", True):
+        extra = extra * ossd.silu(z)
+    return out + extra, h_next
+
+
+def _block_cache_is_reverse_state(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None, **kw):
+    """The cache handed to the next block is the reverse state after token 0."""
+    out, _ = _orig_block(x, dt, A, B, C, D, z, dt_bias, h0, **kw)
+    delta = ossd.ssd_discretise(dt, dt_bias)
+    return out, ossd.ssd_reverse_scan(delta, ossd._heads(x, len(A)), A, B, C)[1]
 
 
 MUTANTS = {
@@ -67,6 +90,8 @@ MUTANTS = {
     "channels laid out head-minor": [("_heads", _heads_channel_major)],
     "dt_bias ignored": [("ssd_discretise", _discretise_no_bias)],
     "step sizes of the heads reversed": [("ssd_discretise", _discretise_heads_reversed)],
+    "block reverse starts from the cache": [("ssd_scan_block", _block_reverse_from_cache)],
+    "block cache is the reverse state": [("ssd_scan_block", _block_cache_is_reverse_state)],
 }
 
 
