@@ -41,6 +41,8 @@ EXPORTED = (
     "bimamba_ssd_fwd_workspace_bytes",
     "bimamba_ssd_fwd",
     "bimamba_ssd_fwd_stage",
+    "bimamba_ssd_block_workspace_bytes",
+    "bimamba_ssd_block",
     "bimamba_conv1d_bidir",
     "bimamba_conv1d_block",
 )
@@ -89,6 +91,10 @@ def load() -> ctypes.CDLL:
     lib.bimamba_ssd_fwd_stage.restype = ctypes.c_int
     lib.bimamba_ssd_fwd_stage.argtypes = [ctypes.c_int] + [vp] * 9 + [i64] * 5 + [ctypes.c_int, ctypes.c_uint32, vp,
                                                                                     sz, vp]
+    lib.bimamba_ssd_block_workspace_bytes.restype = sz
+    lib.bimamba_ssd_block_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.bimamba_ssd_block.restype = ctypes.c_int
+    lib.bimamba_ssd_block.argtypes = [vp] * 11 + [i64] * 5 + [ctypes.c_int, ctypes.c_uint32, vp, sz, vp]
     lib.bimamba_conv1d_bidir.restype = ctypes.c_int
     lib.bimamba_conv1d_bidir.argtypes = [vp] * 7 + [i64] * 4 + [ctypes.c_int, ctypes.c_uint32, vp]
     lib.bimamba_conv1d_block.restype = ctypes.c_int
@@ -321,6 +327,30 @@ def bimamba_ssd_fwd_stage(stage: int, x, dt, A, B, C, D=None, z=None, dt_bias=No
                                       _ptr(workspace), _nbytes(workspace), _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, f"bimamba_ssd_fwd_stage({stage})")
+    return out
+
+
+def bimamba_ssd_block_workspace_bytes(batch: int, block_len: int, nheads: int, headdim: int, d_state: int) -> int:
+    return int(load().bimamba_ssd_block_workspace_bytes(batch, block_len, nheads, headdim, d_state))
+
+
+def bimamba_ssd_block(x, dt, A, B, C, D=None, z=None, dt_bias=None, h_in=None, h_out=None, out=None,
+                      flags: int = 0, workspace=None, stream=None):
+    """One block of block-cache decoding with Mamba-2 heads; returns out.  h_in / h_out are fp32
+    [batch, nheads, headdim, d_state] (h_out may be h_in): the cached forward state before and after the block."""
+    torch = _torch()
+    nb, L, nh, hp, ns, out = _ssd_common(x, dt, A, B, C, D, z, dt_bias, out)
+    _check(h_in, "h_in", (nb, nh, hp, ns), torch.float32, x.device)
+    _check(h_out, "h_out", (nb, nh, hp, ns), torch.float32, x.device)
+    lib = load()
+    need = int(lib.bimamba_ssd_block_workspace_bytes(nb, L, nh, hp, ns))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib.bimamba_ssd_block(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                               _ptr(h_in), _ptr(h_out), _ptr(out), nb, L, nh, hp, ns, _io_dtype(x), flags,
+                               _ptr(workspace), _nbytes(workspace), _stream(stream, x.device))
+    if st != BIMAMBA_OK:
+        raise BimambaError(st, "bimamba_ssd_block")
     return out
 
 

@@ -236,9 +236,9 @@ static int ssd_check_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
 }
 
 static int ssd_impl(int stage, const void* x, const void* dt, const float* A, const void* B, const void* C,
-                    const float* D, const void* z, const float* dt_bias, void* out, int64_t batch, int64_t seqlen,
-                    int64_t nheads, int64_t headdim, int64_t d_state, int io_dtype, uint32_t flags, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream) {
+                    const float* D, const void* z, const float* dt_bias, const float* h_in, float* h_out, void* out,
+                    int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state, int io_dtype,
+                    uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (stage < -1 || stage > 3) return BIMAMBA_ERR_INVALID_ARGUMENT;
   int s = ssd_check_shape(batch, seqlen, nheads, headdim, d_state, io_dtype);
   if (s != BIMAMBA_OK) return s;
@@ -258,11 +258,28 @@ static int ssd_impl(int stage, const void* x, const void* dt, const float* A, co
       overlap(o, range_of(C, bc)) || (z && overlap(o, range_of(z, act))) || overlap(o, range_of(A, par)) ||
       (D && overlap(o, range_of(D, par))) || (dt_bias && overlap(o, range_of(dt_bias, par))))
     return BIMAMBA_ERR_INVALID_ARGUMENT;
+  // block decoding: the cached forward state in and out ([batch, nheads, headdim, d_state] fp32)
+  const size_t stb = static_cast<size_t>(batch) * nheads * headdim * d_state * 4;
+  if ((h_in && !aligned(h_in, 4)) || (h_out && !aligned(h_out, 4))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (h_out && (flags & BIMAMBA_FLAG_REV_ONLY)) return BIMAMBA_ERR_INVALID_ARGUMENT;  // no forward state computed
+  if (h_in && h_out && h_in != h_out && overlap(range_of(h_in, stb), range_of(h_out, stb)))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (h_in && overlap(range_of(h_in, stb), o)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (h_out) {
+    const Range ho = range_of(h_out, stb);
+    if (overlap(ho, o) || overlap(ho, range_of(x, act)) || overlap(ho, range_of(dt, dtb)) ||
+        overlap(ho, range_of(B, bc)) || overlap(ho, range_of(C, bc)) || (z && overlap(ho, range_of(z, act))) ||
+        overlap(ho, range_of(A, par)) || (D && overlap(ho, range_of(D, par))) ||
+        (dt_bias && overlap(ho, range_of(dt_bias, par))))
+      return BIMAMBA_ERR_INVALID_ARGUMENT;
+  }
   const bimamba::ssd::SsdPlan p = bimamba::ssd::make_ssd_plan(batch, seqlen, nheads);
   if (workspace_bytes < p.total) return BIMAMBA_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned(workspace, 256)) return BIMAMBA_ERR_INVALID_ARGUMENT;
-  if (overlap(range_of(workspace, p.total), o)) return BIMAMBA_ERR_INVALID_ARGUMENT;
-  const bimamba::ssd::SsdArgs a{x, dt, A, B, C, D, z, dt_bias, out, flags};
+  const Range wr = range_of(workspace, p.total);
+  if (overlap(wr, o) || (h_in && overlap(wr, range_of(h_in, stb))) || (h_out && overlap(wr, range_of(h_out, stb))))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const bimamba::ssd::SsdArgs a{x, dt, A, B, C, D, z, dt_bias, out, flags, h_in, h_out};
   return map_hip(bimamba::ssd::launch_ssd(a, p, workspace, stream, stage));
 }
 
@@ -276,8 +293,8 @@ int bimamba_ssd_fwd(const void* x, const void* dt, const float* A, const void* B
                     const void* z, const float* dt_bias, void* out, int64_t batch, int64_t seqlen, int64_t nheads,
                     int64_t headdim, int64_t d_state, int io_dtype, uint32_t flags, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
-  return ssd_impl(-1, x, dt, A, B, C, D, z, dt_bias, out, batch, seqlen, nheads, headdim, d_state, io_dtype, flags,
-                  workspace, workspace_bytes, stream);
+  return ssd_impl(-1, x, dt, A, B, C, D, z, dt_bias, nullptr, nullptr, out, batch, seqlen, nheads, headdim, d_state,
+                  io_dtype, flags, workspace, workspace_bytes, stream);
 }
 
 int bimamba_ssd_fwd_stage(int stage, const void* x, const void* dt, const float* A, const void* B, const void* C,
@@ -285,8 +302,21 @@ int bimamba_ssd_fwd_stage(int stage, const void* x, const void* dt, const float*
                           int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state, int io_dtype,
                           uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (stage < 0) return BIMAMBA_ERR_INVALID_ARGUMENT;
-  return ssd_impl(stage, x, dt, A, B, C, D, z, dt_bias, out, batch, seqlen, nheads, headdim, d_state, io_dtype,
-                  flags, workspace, workspace_bytes, stream);
+  return ssd_impl(stage, x, dt, A, B, C, D, z, dt_bias, nullptr, nullptr, out, batch, seqlen, nheads, headdim,
+                  d_state, io_dtype, flags, workspace, workspace_bytes, stream);
+}
+
+size_t bimamba_ssd_block_workspace_bytes(int64_t batch, int64_t block_len, int64_t nheads, int64_t headdim,
+                                         int64_t d_state) {
+  return bimamba_ssd_fwd_workspace_bytes(batch, block_len, nheads, headdim, d_state);
+}
+
+int bimamba_ssd_block(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                      const void* z, const float* dt_bias, const float* h_in, float* h_out, void* out,
+                      int64_t batch, int64_t block_len, int64_t nheads, int64_t headdim, int64_t d_state,
+                      int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return ssd_impl(-1, x, dt, A, B, C, D, z, dt_bias, h_in, h_out, out, batch, block_len, nheads, headdim, d_state,
+                  io_dtype, flags, workspace, workspace_bytes, stream);
 }
 
 // ---- Short causal / anti-causal convolution ----

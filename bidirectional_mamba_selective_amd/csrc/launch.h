@@ -70,10 +70,13 @@ struct SsdArgs {
   const float* dt_bias;
   void* out;
   uint32_t flags;
+  const float* h_in;  // block decoding: forward state entering the sequence (null = zeros)
+  float* h_out;       // block decoding: receives the forward state after it (null = not written)
 };
 
 // Staged chunked scan: stage 0 tiles B and C, 1 chunk summaries, 2 carry,
-// 3 output; stage < 0 launches all four.
+// 3 output; stage < 0 launches all four.  h_in / h_out enter and leave
+// through the carry stage.
 hipError_t launch_ssd(const SsdArgs& a, const SsdPlan& p, void* workspace, hipStream_t stream, int stage = -1);
 
 }  // namespace ssd

@@ -110,6 +110,8 @@ struct Args {
   float* Pc;      // [batch, nchunk, H]
   float* tau;     // [batch, nchunk, H, rpc]: product of abar over the chunk's tokens right of each run
   int gate;
+  const float* h_in;  // [batch, H, P, N] forward state entering the sequence, or null (zeros)
+  float* h_out;       // [batch, H, P, N] forward state after the sequence, or null
 };
 
 // (batch, chunk, head) of a workgroup.  Workgroups are dispatched round-robin
@@ -485,23 +487,31 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_rsweep(Args a) {
 
 // ---------------------------------------------------------------------------
 // k_ssd_carry: chunk-local states -> states entering each chunk (in place).
-// One thread per (batch, head, state element); sequential over chunks.
+// One thread per (batch, head, state element); sequential over chunks.  In
+// block decoding the forward chain starts from the cached state h_in and its
+// value after the last chunk is the new cache h_out (both [batch, H, P, N]);
+// each thread reads and writes only its own element, so h_out may be h_in.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_ssd_carry(float* S, const float* Pc, int64_t batch, int64_t H,
-                                                   int64_t nchunk, int dirs) {
+                                                   int64_t nchunk, int dirs, const float* h_in, float* h_out) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t e = gid % kSF, bh = gid / kSF;
   if (bh >= batch * H) return;
   const int64_t b = bh / H, h = bh % H;
   if (dirs & 1) {
-    float acc = 0.0f;
+    // element e of the tile layout [nb][tp][lane][r] is state n of channel p
+    const int64_t r = e % 4, ln = (e / 4) % 64, tp = (e / 256) % 2, nb = e / 512;
+    const int64_t n = 16 * nb + 4 * (ln / 16) + r, p = 16 * tp + ln % 16;
+    const int64_t hidx = ((b * H + h) * P + p) * N + n;
+    float acc = h_in ? h_in[hidx] : 0.0f;
     for (int64_t c = 0; c < nchunk; ++c) {
       const int64_t item = (b * nchunk + c) * H + h;
-      float* p = S + (item * 2 + 0) * kSF + e;
-      const float t = *p;
-      *p = acc;
+      float* p_s = S + (item * 2 + 0) * kSF + e;
+      const float t = *p_s;
+      *p_s = acc;
       acc = Pc[item] * acc + t;
     }
+    if (h_out) h_out[hidx] = acc;
   }
   if (dirs & 2) {
     float acc = 0.0f;
@@ -661,7 +671,7 @@ hipError_t launch_dirs(const Args& a, int64_t batch, hipStream_t stream, int sta
   if (stage < 0 || stage == 2) {
     const int64_t threads = batch * a.H * kSF;
     hipLaunchKernelGGL(k_ssd_carry, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream, a.S,
-                       a.Pc, batch, a.H, a.nchunk, DIRS);
+                       a.Pc, batch, a.H, a.nchunk, DIRS, a.h_in, a.h_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -699,6 +709,8 @@ hipError_t launch_ssd(const SsdArgs& in, const SsdPlan& p, void* workspace, hipS
   a.Pc = reinterpret_cast<float*>(ws + p.off_p);
   a.tau = reinterpret_cast<float*>(ws + p.off_tau);
   a.gate = (in.flags & kNoGate) ? 0 : 1;
+  a.h_in = in.h_in;
+  a.h_out = in.h_out;
   if (stage < 0 || stage == 0) {
     hipLaunchKernelGGL(k_ssd_stage, dim3(static_cast<unsigned>(p.nsub), static_cast<unsigned>(p.batch)),
                        dim3(kThreads), 0, stream, a.B, a.C, a.g, a.cp, a.bt, p.seqlen, p.nsub);

@@ -193,6 +193,31 @@ int bimamba_ssd_fwd_stage(int stage, const void* x, const void* dt, const float*
                           int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* Bytes of device workspace bimamba_ssd_block needs (the same as a full call
+ * over block_len tokens). */
+size_t bimamba_ssd_block_workspace_bytes(int64_t batch, int64_t block_len, int64_t nheads, int64_t headdim,
+                                         int64_t d_state);
+
+/* One block of block-cache decoding with Mamba-2 heads (Section 4.3,
+ * block-cache paragraph): the forward direction resumes from the cached state
+ * h_in, the reverse direction starts from zero after the block's last token
+ * and never looks past the block.  x, dt, z, B, C, out hold the block's
+ * block_len tokens; everything else is as in bimamba_ssd_fwd.
+ *   h_in : [batch, nheads, headdim, d_state] fp32 (state n of channel
+ *          h*headdim + p at ((b*nheads + h)*headdim + p)*d_state + n), the
+ *          forward state before the block; NULL means zeros.
+ *   h_out: the same layout, receives the forward state after the block's last
+ *          token (the cache of the next block); NULL means do not write.  It
+ *          may equal h_in (in-place commit) but must not otherwise overlap it,
+ *          nor any input, out or the workspace; h_in must not overlap out or
+ *          the workspace.  With BIMAMBA_FLAG_REV_ONLY the forward state is not
+ *          computed and h_out must be NULL (INVALID_ARGUMENT otherwise).
+ * h_in and h_out are 4-byte aligned. */
+int bimamba_ssd_block(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
+                      const void* z, const float* dt_bias, const float* h_in, float* h_out, void* out,
+                      int64_t batch, int64_t block_len, int64_t nheads, int64_t headdim, int64_t d_state,
+                      int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---- Short causal / anti-causal convolution ------------------------------
  * Each direction of the mixer runs a depthwise Conv1d of width d_conv = 4
  * ahead of its scan (Appendix C Table 12: conv_ch = 4096 channels at the 1.3B

@@ -14,4 +14,4 @@ from .scan import (  # noqa: F401
     softplus,
 )
 from .conv import conv_anticausal, conv_bidir, conv_block, conv_causal  # noqa: F401
-from .ssd import ssd_discretise, ssd_forward_scan, ssd_reverse_scan, ssd_scan_fwd  # noqa: F401
+from .ssd import ssd_discretise, ssd_forward_scan, ssd_reverse_scan, ssd_scan_block, ssd_scan_fwd  # noqa: F401

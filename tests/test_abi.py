@@ -321,3 +321,39 @@ def test_binding_counts_workspace_bytes():
     assert _lib._nbytes(torch.empty(10, dtype=torch.float32)) == 40  # any dtype: bytes, not elements
     with pytest.raises(ValueError):
         _lib._nbytes(torch.empty(4, 4, dtype=torch.uint8).t())
+
+
+def call_ssd_block(**kw):
+    lib = _lib.load()
+    a = dict(x=fake(0), dt=fake(1), A=fake(2), B=fake(3), C=fake(4), D=fake(5), z=fake(6), dt_bias=fake(7),
+             h_in=fake(10), h_out=fake(11), out=fake(8), batch=1, L=32, h=4, p=32, n=128, io=_lib.BIMAMBA_BF16,
+             flags=0, ws=fake(9), wsb=0)
+    a.update(kw)
+    return lib.bimamba_ssd_block(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["dt_bias"], a["h_in"],
+                                 a["h_out"], a["out"], a["batch"], a["L"], a["h"], a["p"], a["n"], a["io"], a["flags"],
+                                 a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), INV),
+    (dict(L=0), INV),
+    (dict(n=64), UNS),
+    (dict(h_in=fake(10, 2)), INV),  # misaligned state
+    (dict(h_out=fake(10, 256)), INV),  # partial overlap with h_in
+    (dict(h_out=fake(8, 0)), INV),  # h_out over out
+    (dict(h_out=fake(0, 0)), INV),  # h_out over x
+    (dict(h_out=fake(3, 0)), INV),  # h_out over B
+    (dict(h_in=fake(8, 0), h_out=None), INV),  # h_in over out
+    (dict(flags=_lib.FLAG_REV_ONLY), INV),  # no forward state to cache
+    (dict(wsb=0), WS),
+    (dict(h_out=fake(10), wsb=0), WS),  # in-place commit accepted (stops at the workspace check)
+    (dict(h_in=None, h_out=None, wsb=0), WS),
+    (dict(flags=_lib.FLAG_REV_ONLY, h_out=None, wsb=0), WS),
+])
+def test_ssd_block_rejects(kw, want):
+    assert call_ssd_block(**kw) == want
+
+
+def test_ssd_block_workspace_is_the_full_call_workspace():
+    assert _lib.bimamba_ssd_block_workspace_bytes(2, 100, 8, 32, 128) == \
+        _lib.bimamba_ssd_fwd_workspace_bytes(2, 100, 8, 32, 128) > 0
