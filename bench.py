@@ -347,6 +347,8 @@ def bench_ssd(args, torch, bm, I, dev, stream):
     io_bytes = (tokens * (nc * 2 * (2 + 1 + 3) + w.nheads * 2 * 2 + 2 * w.d_state * 2)
                 + runs * (2 * tile + SSD_Q * SSD_Q * 4) * 2 + runs * 2 * tile)
     pages_flop = 2 * 2 * nc * w.d_state * tokens  # the paper's count: 2 d_inner d_state per token and direction
+    del x, dt, z, B, C, out, ws
+    block_us = ssd_block_latency(torch, bm, I, dev, w, A, Dv, bias)
     return {
         "workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "nheads": w.nheads, "headdim": w.headdim,
         "d_state": w.d_state, "io_dtype": "bf16", "state_dtype": "f32",
@@ -360,7 +362,52 @@ def bench_ssd(args, torch, bm, I, dev, stream):
         "hbm": {"bytes_per_call": io_bytes, "achieved_gbs": round(io_bytes / (ms * 1e-3) / 1e9, 1),
                 "frac_of_peak": round(io_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "scan_tflops_pages_count": round(pages_flop / (ms * 1e-3) / 1e12, 2),
+        "block_step_us": block_us,
     }
+
+
+def ssd_block_latency(torch, bm, I, dev, w, A, Dv, bias):
+    """Block-cache decoding with the 120 heads: one bimamba_ssd_block step re-run 100 times from the same
+    cache (h_out = NULL), captured as a graph and replayed; us per step at 32 and 64 tokens."""
+    res = {}
+    h = torch.zeros(1, w.nheads, w.headdim, w.d_state, dtype=torch.float32, device=dev)
+    for G in (32, 64):
+        act = I.make_ssd_activations(1, G, w.nheads, w.headdim, w.d_state, "bf16", seed=9)
+        bl = {k: torch.from_numpy(I.bf16_bits(act[k]).view(np.int16)).view(torch.bfloat16).to(dev)
+              for k in ("x", "dt", "z", "B", "C")}
+        o = torch.empty_like(bl["x"])
+        ws = torch.empty(bm.bimamba_ssd_block_workspace_bytes(1, G, w.nheads, w.headdim, w.d_state),
+                         dtype=torch.uint8, device=dev)
+
+        def one(s_):
+            bm.bimamba_ssd_block(bl["x"], bl["dt"], A, bl["B"], bl["C"], Dv, bl["z"], bias, h_in=h, h_out=None,
+                                 out=o, workspace=ws, stream=s_)
+
+        gs = torch.cuda.Stream(dev)
+        gs.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(gs):
+            one(gs)
+        torch.cuda.synchronize()
+        ref = o.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g, stream=gs):
+                for _ in range(100):
+                    one(gs)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            o.zero_()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+            if not torch.equal(o, ref):
+                raise SystemExit(f"ssd block G={G}: graph replay differs from the eager call")
+        res[str(G)] = round(float(np.median(ts)) * 1e6 / 100, 2)
+        log(f"ssd block step G={G}: {res[str(G)]} us per step (graph of 100 re-runs)")
+    return res
 
 
 def bench_conv(args, torch, bm, I, dev, stream):
