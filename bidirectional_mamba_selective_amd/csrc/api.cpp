@@ -235,11 +235,14 @@ static int ssd_check_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
   return BIMAMBA_OK;
 }
 
+// ssd_impl's stage value for the single-kernel block step (blocks of at most one run)
+constexpr int kSsdBlockFused = -2;
+
 static int ssd_impl(int stage, const void* x, const void* dt, const float* A, const void* B, const void* C,
                     const float* D, const void* z, const float* dt_bias, const float* h_in, float* h_out, void* out,
                     int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state, int io_dtype,
                     uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (stage < -1 || stage > 3) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if ((stage < -1 || stage > 3) && stage != kSsdBlockFused) return BIMAMBA_ERR_INVALID_ARGUMENT;
   int s = ssd_check_shape(batch, seqlen, nheads, headdim, d_state, io_dtype);
   if (s != BIMAMBA_OK) return s;
   if (flags & ~kKnownFlags) return BIMAMBA_ERR_INVALID_ARGUMENT;
@@ -273,13 +276,17 @@ static int ssd_impl(int stage, const void* x, const void* dt, const float* A, co
         (dt_bias && overlap(ho, range_of(dt_bias, par))))
       return BIMAMBA_ERR_INVALID_ARGUMENT;
   }
+  const bimamba::ssd::SsdArgs a{x, dt, A, B, C, D, z, dt_bias, out, flags, h_in, h_out};
+  if (stage == kSsdBlockFused) {
+    // a block of at most one run: one kernel, no workspace
+    return map_hip(bimamba::ssd::launch_ssd_block(a, batch, seqlen, nheads, stream));
+  }
   const bimamba::ssd::SsdPlan p = bimamba::ssd::make_ssd_plan(batch, seqlen, nheads);
   if (workspace_bytes < p.total) return BIMAMBA_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned(workspace, 256)) return BIMAMBA_ERR_INVALID_ARGUMENT;
   const Range wr = range_of(workspace, p.total);
   if (overlap(wr, o) || (h_in && overlap(wr, range_of(h_in, stb))) || (h_out && overlap(wr, range_of(h_out, stb))))
     return BIMAMBA_ERR_INVALID_ARGUMENT;
-  const bimamba::ssd::SsdArgs a{x, dt, A, B, C, D, z, dt_bias, out, flags, h_in, h_out};
   return map_hip(bimamba::ssd::launch_ssd(a, p, workspace, stream, stage));
 }
 
@@ -308,6 +315,7 @@ int bimamba_ssd_fwd_stage(int stage, const void* x, const void* dt, const float*
 
 size_t bimamba_ssd_block_workspace_bytes(int64_t batch, int64_t block_len, int64_t nheads, int64_t headdim,
                                          int64_t d_state) {
+  if (block_len <= bimamba::ssd::kQ) return 0;  // single-kernel path
   return bimamba_ssd_fwd_workspace_bytes(batch, block_len, nheads, headdim, d_state);
 }
 
@@ -315,8 +323,8 @@ int bimamba_ssd_block(const void* x, const void* dt, const float* A, const void*
                       const void* z, const float* dt_bias, const float* h_in, float* h_out, void* out,
                       int64_t batch, int64_t block_len, int64_t nheads, int64_t headdim, int64_t d_state,
                       int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return ssd_impl(-1, x, dt, A, B, C, D, z, dt_bias, h_in, h_out, out, batch, block_len, nheads, headdim, d_state,
-                  io_dtype, flags, workspace, workspace_bytes, stream);
+  return ssd_impl(block_len <= bimamba::ssd::kQ ? kSsdBlockFused : -1, x, dt, A, B, C, D, z, dt_bias, h_in, h_out,
+                  out, batch, block_len, nheads, headdim, d_state, io_dtype, flags, workspace, workspace_bytes, stream);
 }
 
 // ---- Short causal / anti-causal convolution ----

@@ -79,6 +79,9 @@ struct SsdArgs {
 // through the carry stage.
 hipError_t launch_ssd(const SsdArgs& a, const SsdPlan& p, void* workspace, hipStream_t stream, int stage = -1);
 
+// One block-cache decoding step of at most kQ tokens in a single kernel (no workspace).
+hipError_t launch_ssd_block(const SsdArgs& a, int64_t batch, int64_t block_len, int64_t nheads, hipStream_t stream);
+
 }  // namespace ssd
 
 }  // namespace bimamba

@@ -660,6 +660,186 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_fsweep(Args a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_ssd_block: one block of block-cache decoding of at most Q tokens (one run)
+// for one (batch, head) per workgroup, in a single kernel.  The run's C B^T,
+// B^T and per-token terms are formed here instead of by the tiling kernel; out
+// = the intra-run products of both directions (the reverse direction starts
+// from zero after the block), the readout of the cached forward state, the
+// skip term and the gate; the new cache = the cached state decayed over the
+// block plus the block's own update.  Wavefront w owns output rows 16w..16w+15
+// and state row blocks 2w, 2w + 1, as in the sweeps.  The cache is read and
+// written in the caller's layout [batch, H, P, N]; each element is read and
+// written by the same lane, so h_out may be h_in.
+// ---------------------------------------------------------------------------
+template <int DIRS>
+__global__ __launch_bounds__(kThreads, 2) void k_ssd_block(Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sBs[Q * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sCs[Q * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sBT[N * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sXT[P * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sXW[P * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sHs[P * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sZ[4 * 16 * P];
+  __shared__ __attribute__((aligned(16))) uint16_t sY[4 * 16 * P];
+  __shared__ __attribute__((aligned(16))) float sTok[kTokRows * 64];
+  constexpr bool kFwd = DIRS & 1, kRev = DIRS & 2;
+  constexpr float kDiag = (kFwd && kRev) ? 2.0f : 1.0f;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q4 = l >> 4, l16 = l & 15;
+  const int64_t h = blockIdx.x % a.H, b = blockIdx.x / a.H;
+  const float Ah = a.A[h];
+  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const float Dfac = a.D ? a.D[h] * kDiag : 0.0f;
+  const int64_t HP = a.H * P;
+  uint16_t* zslot = sZ + w * 16 * P;
+  uint16_t* yslot = sY + w * 16 * P;
+
+  // 1. the block's B and C rows (zero past its end), the head's x, z and step sizes, and the cache
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ci = tid + kThreads * i;
+    const int j = ci >> 4, cc = ci & 15;
+    uint4 vb = make_uint4(0, 0, 0, 0), vc = make_uint4(0, 0, 0, 0);
+    if (j < a.L) {
+      vb = *reinterpret_cast<const uint4*>(a.B + (b * a.L + j) * N + 8 * cc);
+      vc = *reinterpret_cast<const uint4*>(a.C + (b * a.L + j) * N + 8 * cc);
+    }
+    *reinterpret_cast<uint4*>(sBs + sw256(j, cc)) = vb;
+    *reinterpret_cast<uint4*>(sCs + sw256(j, cc)) = vc;
+  }
+  const uint4 px = load_act(a.x, a, b, 0, h, tid);
+  if (a.gate) *reinterpret_cast<uint4*>(zslot + (l >> 2) * P + 8 * (l & 3)) = load_act(a.z, a, b, 0, h, 64 * w + l);
+  State H;
+  state_zero(H);
+  if (kFwd && a.h_in) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = 16 * (2 * w + i) + 4 * q4 + r, p = 16 * tp + l16;
+          H.t[i][tp][r] = a.h_in[((b * a.H + h) * P + p) * N + n];
+        }
+  }
+  if (w == 0) token_prep(sTok, load_dt(a, b, 0, h, l), l < a.L, Ah, bias, l);
+  __syncthreads();
+
+  // 2. B^T rows (the state update's operand), this wavefront's rows of C B^T, x tiles, the cache as bf16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ci = tid + kThreads * i;
+    const int n = ci >> 3, jc = ci & 7;
+    uint32_t w2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j0 = 8 * jc + 2 * e;
+      w2[e] = static_cast<uint32_t>(sBs[sw256(j0, n >> 3) + (n & 7)]) |
+              (static_cast<uint32_t>(sBs[sw256(j0 + 1, n >> 3) + (n & 7)]) << 16);
+    }
+    *reinterpret_cast<uint4*>(sBT + sw128(n, jc)) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+  }
+  bf16x8 cf[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) cf[k] = lds8(sCs, sw256(16 * w + l16, 4 * k + q4));
+  f32x4 gcur[4];
+#pragma unroll
+  for (int tj = 0; tj < 4; ++tj) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = mfma(lds8(sBs, sw256(16 * tj + l16, 4 * k + q4)), cf[k], acc);
+    gcur[tj] = acc;
+  }
+  const float* tok = sTok;
+  put_xt(sXT, px, tid, nullptr, 1.0f);
+  if (kFwd) put_xt(sXW, px, tid, tok + kWf * 64, 1.0f);
+  if (kFwd) state_to_lds(H, sHs, w, l);
+  __syncthreads();
+
+  // 3. out.  W = mask o (C B^T) o delta_j for rows i = 16w + l16 as the A operand, k-slots permuted as in
+  // the reverse sweep: slot e < 4 -> j = 32k2 + 4q4 + e, slot e >= 4 -> j = 32k2 + 16 + 4q4 + e - 4
+  const int i = 16 * w + l16;
+  const float si = tok[kS * 64 + i], ei = tok[kE * 64 + i];
+#pragma unroll
+  for (int tj = 0; tj < 4; ++tj) {
+    const int j0 = 16 * tj + 4 * q4;
+    const f32x4 sj = *reinterpret_cast<const f32x4*>(tok + kS * 64 + j0);
+    const f32x4 ej = *reinterpret_cast<const f32x4*>(tok + kE * 64 + j0);
+    const f32x4 dj = *reinterpret_cast<const f32x4*>(tok + kDl * 64 + j0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + r;
+      float m;
+      if (j < i) m = kFwd ? ex(si - sj[r]) : 0.0f;
+      else if (j > i) m = kRev ? ex(ej[r] - ei) : 0.0f;
+      else m = kDiag;
+      gcur[tj][r] *= m * dj[r];
+    }
+  }
+  f32x4 y[2] = {zero4(), zero4()};
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    bf16x8 wa;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      wa[r] = static_cast<__bf16>(gcur[2 * k2][r]);
+      wa[4 + r] = static_cast<__bf16>(gcur[2 * k2 + 1][r]);
+    }
+    const int jlo = 32 * k2 + 4 * q4;
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+      const int p = 16 * tp + l16;
+      const uint2 lo = *reinterpret_cast<const uint2*>(sXT + sw128(p, jlo >> 3) + (jlo & 7));
+      const uint2 hi = *reinterpret_cast<const uint2*>(sXT + sw128(p, (jlo + 16) >> 3) + (jlo & 7));
+      y[tp] = mfma(wa, __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), y[tp]);
+    }
+  }
+  if (kFwd) {
+    f32x4 yf[2];
+    readout(yf, cf, sHs, l);
+    const f32x4 rf = *reinterpret_cast<const f32x4*>(tok + kRf * 64 + 16 * w + 4 * q4);
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[tp][r] += rf[r] * yf[tp][r];
+  }
+  float o[2][4];
+  const int i0 = 16 * w + 4 * q4;
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp) {
+    const int p = 16 * tp + l16;
+    const uint2 xv = *reinterpret_cast<const uint2*>(sXT + sw128(p, i0 >> 3) + (i0 & 7));
+    const float xs[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xffff0000u),
+                         __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xffff0000u)};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      o[tp][r] = y[tp][r] + Dfac * xs[r];
+      if (a.gate) o[tp][r] *= silu_f32(bf(zslot[(4 * q4 + r) * P + p]));
+    }
+  }
+  tile_rows_to_lds(yslot, o, l);
+  {
+    const int64_t t = 16 * w + (l >> 2);
+    if (t < a.L)
+      *reinterpret_cast<uint4*>(a.out + (b * a.L + t) * HP + h * P + 8 * (l & 3)) =
+          *reinterpret_cast<const uint4*>(yslot + (l >> 2) * P + 8 * (l & 3));
+  }
+
+  // 4. the new cache: the cached state decayed over the block plus the block's update
+  if (kFwd && a.h_out) {
+    state_update(H, ex(tok[kS * 64 + 63]), sBT, sXW, w, l);
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = 16 * (2 * w + i2) + 4 * q4 + r, p = 16 * tp + l16;
+          a.h_out[((b * a.H + h) * P + p) * N + n] = H.t[i2][tp][r];
+        }
+  }
+}
+
 template <int DIRS>
 hipError_t launch_dirs(const Args& a, int64_t batch, hipStream_t stream, int stage) {
   const unsigned groups = static_cast<unsigned>(batch * a.nchunk * a.H);
@@ -684,6 +864,33 @@ hipError_t launch_dirs(const Args& a, int64_t batch, hipStream_t stream, int sta
 }
 
 }  // namespace
+
+hipError_t launch_ssd_block(const SsdArgs& in, int64_t batch, int64_t block_len, int64_t nheads, hipStream_t stream) {
+  Args a{};
+  a.x = static_cast<const uint16_t*>(in.x);
+  a.dt = static_cast<const uint16_t*>(in.dt);
+  a.A = in.A;
+  a.B = static_cast<const uint16_t*>(in.B);
+  a.C = static_cast<const uint16_t*>(in.C);
+  a.D = in.D;
+  a.z = static_cast<const uint16_t*>(in.z);
+  a.dt_bias = in.dt_bias;
+  a.out = static_cast<uint16_t*>(in.out);
+  a.L = block_len;
+  a.H = nheads;
+  a.gate = (in.flags & kNoGate) ? 0 : 1;
+  a.h_in = in.h_in;
+  a.h_out = in.h_out;
+  const dim3 grid(static_cast<unsigned>(batch * nheads));
+  if (in.flags & kFwdOnly) {
+    hipLaunchKernelGGL(k_ssd_block<1>, grid, dim3(kThreads), 0, stream, a);
+  } else if (in.flags & kRevOnly) {
+    hipLaunchKernelGGL(k_ssd_block<2>, grid, dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(k_ssd_block<3>, grid, dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_ssd(const SsdArgs& in, const SsdPlan& p, void* workspace, hipStream_t stream, int stage) {
   char* ws = static_cast<char*>(workspace);

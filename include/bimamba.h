@@ -193,8 +193,9 @@ int bimamba_ssd_fwd_stage(int stage, const void* x, const void* dt, const float*
                           int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
-/* Bytes of device workspace bimamba_ssd_block needs (the same as a full call
- * over block_len tokens). */
+/* Bytes of device workspace bimamba_ssd_block needs: 0 for blocks of at most
+ * 64 tokens (one kernel), otherwise the same as a full call over block_len
+ * tokens. */
 size_t bimamba_ssd_block_workspace_bytes(int64_t batch, int64_t block_len, int64_t nheads, int64_t headdim,
                                          int64_t d_state);
 
@@ -212,7 +213,8 @@ size_t bimamba_ssd_block_workspace_bytes(int64_t batch, int64_t block_len, int64
  *          nor any input, out or the workspace; h_in must not overlap out or
  *          the workspace.  With BIMAMBA_FLAG_REV_ONLY the forward state is not
  *          computed and h_out must be NULL (INVALID_ARGUMENT otherwise).
- * h_in and h_out are 4-byte aligned. */
+ * h_in and h_out are 4-byte aligned.  workspace may be NULL when
+ * bimamba_ssd_block_workspace_bytes returns 0. */
 int bimamba_ssd_block(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
                       const void* z, const float* dt_bias, const float* h_in, float* h_out, void* out,
                       int64_t batch, int64_t block_len, int64_t nheads, int64_t headdim, int64_t d_state,

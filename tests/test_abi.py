@@ -326,8 +326,8 @@ def test_binding_counts_workspace_bytes():
 def call_ssd_block(**kw):
     lib = _lib.load()
     a = dict(x=fake(0), dt=fake(1), A=fake(2), B=fake(3), C=fake(4), D=fake(5), z=fake(6), dt_bias=fake(7),
-             h_in=fake(10), h_out=fake(11), out=fake(8), batch=1, L=32, h=4, p=32, n=128, io=_lib.BIMAMBA_BF16,
-             flags=0, ws=fake(9), wsb=0)
+             h_in=fake(10), h_out=fake(11), out=fake(8), batch=1, L=100, h=4, p=32, n=128, io=_lib.BIMAMBA_BF16,
+             flags=0, ws=fake(9), wsb=0)  # past one run: a valid call stops at the workspace check
     a.update(kw)
     return lib.bimamba_ssd_block(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["dt_bias"], a["h_in"],
                                  a["h_out"], a["out"], a["batch"], a["L"], a["h"], a["p"], a["n"], a["io"], a["flags"],
@@ -354,6 +354,8 @@ def test_ssd_block_rejects(kw, want):
     assert call_ssd_block(**kw) == want
 
 
-def test_ssd_block_workspace_is_the_full_call_workspace():
+def test_ssd_block_workspace():
+    # blocks of at most one 64-token run take the single-kernel path and need no workspace
+    assert [_lib.bimamba_ssd_block_workspace_bytes(2, g, 8, 32, 128) for g in (1, 32, 64)] == [0, 0, 0]
     assert _lib.bimamba_ssd_block_workspace_bytes(2, 100, 8, 32, 128) == \
         _lib.bimamba_ssd_fwd_workspace_bytes(2, 100, 8, 32, 128) > 0

@@ -165,15 +165,17 @@ def test_ssd_block_step(G, flags):
     assert e_out <= TOL and e_h <= CACHE_TOL
 
 
-def test_ssd_block_chain_and_reruns():
-    """Block decoding over 6 blocks of 64 tokens with the cache committed in place; before each commit the
-    block is re-run twice without h_out (the cache must not change).  Every block's output and the cache at
-    every boundary against the oracle; the chained forward-only outputs also equal the full forward scan."""
+@pytest.mark.parametrize("G", [64, 96])
+def test_ssd_block_chain_and_reruns(G):
+    """Block decoding over 6 blocks with the cache committed in place (64-token blocks take the
+    single-kernel path, 96 the chunked one); before each commit the block is re-run twice without h_out
+    (the cache must not change).  Every block's output and the cache at every boundary against the
+    oracle; the chained forward-only outputs also equal the full forward scan."""
     import oracle
     from bidirectional_mamba_selective_amd import bimamba_ssd_block
 
     torch = torch_mod()
-    nb, nh, G, nblk = 1, 4, 64, 6
+    nb, nh, nblk = 1, 4, 6
     L = G * nblk
     inp = _inputs(nb, L, nh, seed=77)
     dev = _upload(inp)
@@ -201,6 +203,6 @@ def test_ssd_block_chain_and_reruns():
         e_out = rel_err(to_host64(out), want)
         e_h = rel_err(to_host64(h), want_h)
         e_f = rel_err(to_host64(out_f), full_f[:, sl])
-        say(f"ssd block chain {k}: out {e_out:.3e} cache {e_h:.3e} forward vs full scan {e_f:.3e}")
+        say(f"ssd block chain G={G} {k}: out {e_out:.3e} cache {e_h:.3e} forward vs full scan {e_f:.3e}")
         assert e_out <= TOL and e_h <= CACHE_TOL and e_f <= TOL
         h_host = want_h
