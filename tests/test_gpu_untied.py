@@ -102,3 +102,43 @@ def test_untied_layer_2k_subset():
     ef, er = rel_err(got_f[:, :, chan], want_f), rel_err(got_r[:, :, chan], want_r)
     say(f"untied layer 2k subset: out_f {ef:.3e} out_r {er:.3e}")
     assert ef <= tol_for("bf16") and er <= tol_for("bf16")
+
+
+@pytest.mark.parametrize("G", [32, 200])
+def test_untied_block_decoding_from_two_block_calls(G):
+    """Block-cache decoding with untied directions is two block calls: the forward layer's set with
+    FWD_ONLY and the cache, the reverse layer's set with REV_ONLY and no cache.  Over 4 chained blocks
+    (32 tokens: single kernel; 200: chunked path), out_f, out_r and the cache against the oracle's block
+    step of each set, and the chained forward outputs against the untied full-sequence forward output."""
+    import torch
+
+    from bidirectional_mamba_selective_amd import bimamba_scan_block
+    from tests.gpu_util import f32_dev
+
+    D, N, nblk = 128, 16, 4
+    f = _set(1, G * nblk, D, N, "f32", seed=31, a_jitter=0.0, param_seed=3)
+    r = _set(1, G * nblk, D, N, "f32", seed=32, a_jitter=0.2, param_seed=4)
+    df, dr = upload(f, "f32"), upload(r, "f32")
+    h = torch.zeros(1, D, N, device="cuda")
+    h_host = None
+    full_f, _ = oracle.scan_fwd_untied(f, r)
+    for k in range(nblk):
+        sl = slice(k * G, (k + 1) * G)
+        bf = {key: df[key][:, sl].contiguous() for key in ("x", "dt", "z", "B", "C")}
+        br = {key: dr[key][:, sl].contiguous() for key in ("x", "dt", "z", "B", "C")}
+        out_f = bimamba_scan_block(bf["x"], bf["dt"], df["A"], bf["B"], bf["C"], df["D"], bf["z"], df["dt_bias"],
+                                   h_in=h, h_out=h, flags=2)  # FWD_ONLY, committed in place
+        out_r = bimamba_scan_block(br["x"], br["dt"], dr["A"], br["B"], br["C"], dr["D"], br["z"], dr["dt_bias"],
+                                   flags=4)  # REV_ONLY
+        torch.cuda.synchronize()
+        hf = {key: f[key][:, sl] for key in ("x", "dt", "z", "B", "C")}
+        hr = {key: r[key][:, sl] for key in ("x", "dt", "z", "B", "C")}
+        want_f, want_h = oracle.scan_block(hf["x"], hf["dt"], f["A"], hf["B"], hf["C"], f["D"], hf["z"], f["dt_bias"],
+                                           h_host, fwd=True, rev=False)
+        want_r, _ = oracle.scan_block(hr["x"], hr["dt"], r["A"], hr["B"], hr["C"], r["D"], hr["z"], r["dt_bias"],
+                                      None, fwd=False, rev=True)
+        ef, er, eh = rel_err(to_host64(out_f), want_f), rel_err(to_host64(out_r), want_r), rel_err(to_host64(h), want_h)
+        ec = rel_err(to_host64(out_f), full_f[:, sl])
+        say(f"untied block G={G} {k}: out_f {ef:.3e} out_r {er:.3e} cache {eh:.3e} vs full forward {ec:.3e}")
+        assert ef <= tol_for("f32") and er <= tol_for("f32") and eh <= 1e-5 and ec <= tol_for("f32")
+        h_host = want_h
