@@ -254,6 +254,9 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
                                                 float* __restrict__ R, float* __restrict__ SIG) {
   constexpr int SUB = static_cast<int>(kSub);
   static_assert(NM * SUB <= 64 * 4, "one float4 of B per lane");
+  // the boundary states feed only an output pass that runs both chains left to right; a
+  // reverse-only pass walks right to left and carries its state across tiles instead
+  constexpr bool kStoreR = DS == 3;
   __shared__ float sR[(DS & 2) ? NM : 1][64];
   __shared__ float sS[(DS & 1) ? NM : 1][64];
   __shared__ __align__(16) float sB[GEO ? NM : 1][SUB];  // this tile's B, one row per state (GEO)
@@ -314,12 +317,12 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
       float w[SUB];
 #pragma unroll
       for (int k = 0; k < SUB; ++k) w[k] = fast_exp2(dl[k] * a20);
-      summary_tile_states<SUB, true, DS>(N, lane, w, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, j > 0);
+      summary_tile_states<SUB, true, DS>(N, lane, w, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, kStoreR && j > 0);
     } else {
-      summary_tile_states<SUB, false, DS>(N, lane, dl, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, j > 0);
+      summary_tile_states<SUB, false, DS>(N, lane, dl, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, kStoreR && j > 0);
     }
     sigma += tile_sum;
-    if ((DS & 2) && j > 0) __builtin_nontemporal_store(sigma, &SIG[jb * D + d]);
+    if (kStoreR && j > 0) __builtin_nontemporal_store(sigma, &SIG[jb * D + d]);
   }
   for (int n = 0; n < N; ++n) {
     const size_t o = (cbase * N + n) * D + d;
@@ -497,6 +500,46 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
 }
 
 // ---------------------------------------------------------------------------
+// k_output state loop of the right-to-left walk (reverse readout only): the
+// reverse state of each state index is carried across the chunk's tiles in sH,
+// starting from the chunk's carry from the right, so no boundary state is read.
+// ---------------------------------------------------------------------------
+template <int SUB, bool GEO>
+__device__ __forceinline__ void output_tile_states_rwalk(int N, int D, int lane, const float (&w)[SUB],
+                                                         const float (&u)[SUB], float (&y)[SUB],
+                                                         const float* __restrict__ bt, float (*sH)[64],
+                                                         __amdgpu_buffer_rsrc_t a2_rsrc) {
+  const uint32_t voff4 = static_cast<uint32_t>(lane) * 4u;
+  const uint32_t nstride4 = static_cast<uint32_t>(D) * 4u;
+  float a[SUB];
+#pragma unroll
+  for (int k = 0; k < SUB; ++k) a[k] = 1.0f;
+  float a2_next = GEO ? 0.0f : IO<float>::load(a2_rsrc, voff4, 0);
+#pragma unroll 1
+  for (int n = 0; n < N; ++n) {
+    const sfloat* bn = scalar_ptr(bt + static_cast<size_t>(n) * 2 * SUB);
+    float a2 = 0.0f;
+    if (!GEO) {
+      a2 = a2_next;
+      a2_next = IO<float>::load(a2_rsrc, voff4, static_cast<uint32_t>(min(n + 1, N - 1)) * nstride4);
+    }
+    float hr = sH[n][lane];
+    float bb[SUB];
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) {
+      a[k] = GEO ? a[k] * w[k] : fast_exp2(w[k] * a2);
+      bb[k] = u[k] * bn[k];
+    }
+#pragma unroll
+    for (int k = SUB - 1; k >= 0; --k) {
+      hr = fmaf(a[k], hr, bb[k]);
+      y[k] = fmaf(bn[SUB + k], hr, y[k]);
+    }
+    sH[n][lane] = hr;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_output: grid (d_inner / 64, nchunk, batch), block 64 (one wavefront).
 // x, dt and z tiles are brought into LDS one tile ahead with direct-to-LDS
 // loads, so the HBM stream of tile j+1 overlaps the state loop of tile j (all
@@ -513,7 +556,10 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
                                                const float* __restrict__ R, const float* __restrict__ SIG,
                                                const float* __restrict__ A2T, float* __restrict__ h_out) {
   constexpr int SUB = static_cast<int>(kSub);
-  __shared__ float sHf[NM][64];  // per-lane forward state, indexed by a runtime state index
+  // DIRS bit 2: reverse readout only, tiles walked right to left with the reverse state carried
+  constexpr bool kRW = (DIRS & 4) != 0;
+  constexpr int DR = DIRS & 3;  // the readouts
+  __shared__ float sHf[NM][64];  // per-lane carried state (forward, or reverse for kRW), by state index
   __shared__ __align__(16) T sX[SUB][64];
   __shared__ __align__(16) T sDT[SUB][64];
   __shared__ __align__(16) T sZ[SUB][64];
@@ -533,10 +579,10 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
   for (int n = 0; n < N; ++n) geo_lane = geo_lane && (Arow[n] == static_cast<float>(n + 1) * a0);
   // Each wavefront runs in exactly one of the two instantiations (general / geometric A).
   if (wave_geometric(geo_lane) != GEO) return;
-  for (int n = 0; n < N; ++n) sHf[n][lane] = Cf[(cbase * N + n) * D + d];
+  for (int n = 0; n < N; ++n) sHf[n][lane] = (kRW ? Cr : Cf)[(cbase * N + n) * D + d];
   const float a20 = a0 * kLog2e;
   const float bias = dt_bias ? dt_bias[d] : 0.0f;
-  constexpr float ndir = (DIRS == 3) ? 2.0f : 1.0f;
+  constexpr float ndir = (DR == 3) ? 2.0f : 1.0f;
   const float skip = Dv ? ndir * Dv[d] : 0.0f;
   const uint32_t voff = static_cast<uint32_t>(lane) * IO<T>::kBytes;
   const uint32_t row_bytes = static_cast<uint32_t>(D) * IO<T>::kBytes;
@@ -546,16 +592,19 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
 
   const int nsub_c = (te - t0 + SUB - 1) / SUB;
   {
-    const size_t tile = (row + t0) * D + col0;
-    const int nv = min(SUB, te - t0);
+    const int tf = t0 + (kRW ? nsub_c - 1 : 0) * SUB;  // the first tile of the walk
+    const size_t tile = (row + tf) * D + col0;
+    const int nv = min(SUB, te - tf);
     lds_load_tile<T>(x + tile, nv, row_bytes, sX, lane);
     lds_load_tile<T>(dt + tile, nv, row_bytes, sDT, lane);
     if (gate) lds_load_tile<T>(z + tile, nv, row_bytes, sZ, lane);
   }
-  for (int j = 0; j < nsub_c; ++j) {
+  for (int jj = 0; jj < nsub_c; ++jj) {
+    const int j = kRW ? nsub_c - 1 - jj : jj;
     const int ts = t0 + j * SUB;
     const int nvalid = min(SUB, te - ts);
-    const bool last = (j == nsub_c - 1);
+    const bool last = (jj == nsub_c - 1);  // the last tile of the walk: nothing to prefetch
+    const int ts1 = ts + (kRW ? -SUB : SUB);  // the next tile of the walk
     const size_t jb = cbase * nsub + j;
     const size_t tile = (row + ts) * D + col0;
     const size_t tile_bytes = static_cast<size_t>(nvalid) * row_bytes;
@@ -569,12 +618,14 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
     }
     wait_lds_all();  // the reads are done before the buffers are refilled
     if (!last) {
-      const size_t tile1 = tile + static_cast<size_t>(SUB) * D;
-      const int nv1 = min(SUB, te - (ts + SUB));
+      const size_t tile1 = (row + ts1) * D + col0;
+      const int nv1 = min(SUB, te - ts1);
       lds_load_tile<T>(x + tile1, nv1, row_bytes, sX, lane);
       lds_load_tile<T>(dt + tile1, nv1, row_bytes, sDT, lane);
     }
-    const float sj = last ? 0.0f : __builtin_nontemporal_load(&SIG[jb * D + d]);
+    // the left-to-right walk's reverse chain enters each tile from its stored boundary state
+    const bool chunk_end = (j == nsub_c - 1);
+    const float sj = (kRW || chunk_end || !(DR & 2)) ? 0.0f : __builtin_nontemporal_load(&SIG[jb * D + d]);
     const float* bt = bct + (static_cast<size_t>(b) * ntile + static_cast<size_t>(c) * nsub + j) * N * 2 * SUB;
     const __amdgpu_buffer_rsrc_t rj_rsrc = make_rsrc(R + jb * N * D + col0, state_bytes);
     float dl[SUB], u[SUB], y[SUB];
@@ -584,15 +635,24 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
       u[k] = dl[k] * xr[k];
       y[k] = skip * xr[k];
     }
-    if (GEO) {
+    if (kRW) {
+      if (GEO) {
+        float w[SUB];
+#pragma unroll
+        for (int k = 0; k < SUB; ++k) w[k] = fast_exp2(dl[k] * a20);
+        output_tile_states_rwalk<SUB, true>(N, D, lane, w, u, y, bt, sHf, a2_rsrc);
+      } else {
+        output_tile_states_rwalk<SUB, false>(N, D, lane, dl, u, y, bt, sHf, a2_rsrc);
+      }
+    } else if (GEO) {
       float w[SUB];
 #pragma unroll
       for (int k = 0; k < SUB; ++k) w[k] = fast_exp2(dl[k] * a20);
-      output_tile_states<SUB, DIRS, true>(N, D, lane, w, u, y, bt, sHf, rj_rsrc, cr_rsrc, a2_rsrc,
-                                          fast_exp2(a20 * sj), sj, last, h_out != nullptr);
+      output_tile_states<SUB, DR, true>(N, D, lane, w, u, y, bt, sHf, rj_rsrc, cr_rsrc, a2_rsrc,
+                                        fast_exp2(a20 * sj), sj, chunk_end, h_out != nullptr);
     } else {
-      output_tile_states<SUB, DIRS, false>(N, D, lane, dl, u, y, bt, sHf, rj_rsrc, cr_rsrc, a2_rsrc, 1.0f, sj,
-                                           last, h_out != nullptr);
+      output_tile_states<SUB, DR, false>(N, D, lane, dl, u, y, bt, sHf, rj_rsrc, cr_rsrc, a2_rsrc, 1.0f, sj,
+                                         chunk_end, h_out != nullptr);
     }
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + tile, tile_bytes);
     if (gate) {
@@ -601,16 +661,13 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
 #pragma unroll
       for (int k = 0; k < SUB; ++k) zr[k] = lds_val<T>(sZ, k, lane);
       wait_lds_all();
-      if (!last) {
-        const size_t tile1 = tile + static_cast<size_t>(SUB) * D;
-        lds_load_tile<T>(z + tile1, min(SUB, te - (ts + SUB)), row_bytes, sZ, lane);
-      }
+      if (!last) lds_load_tile<T>(z + (row + ts1) * D + col0, min(SUB, te - ts1), row_bytes, sZ, lane);
 #pragma unroll
       for (int k = 0; k < SUB; ++k) y[k] *= silu_f32(zr[k]);
     }
     store_col<T, SUB>(y, ro, voff, row_bytes, nvalid);
   }
-  if (h_out != nullptr && c == nchunk - 1) {
+  if (!kRW && h_out != nullptr && c == nchunk - 1) {
     for (int n = 0; n < N; ++n) h_out[(static_cast<size_t>(b) * D + d) * N + n] = sHf[n][lane];
   }
 }
@@ -942,8 +999,12 @@ static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipSt
   if (a.flags & kFwdOnly) {
     launch_output<T, NM, 1>(grid, stream, x, dt, z, a, bct, out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf,
                             Cr, R, SIG, A2T);
-  } else if (a.flags & kRevOnly) {
+  } else if ((a.flags & kRevOnly) && a.h_out != nullptr) {
+    // the cached forward state needs the forward chain: left to right, reverse from the boundary states
     launch_output<T, NM, 2>(grid, stream, x, dt, z, a, bct, out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf,
+                            Cr, R, SIG, A2T);
+  } else if (a.flags & kRevOnly) {
+    launch_output<T, NM, 6>(grid, stream, x, dt, z, a, bct, out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf,
                             Cr, R, SIG, A2T);
   } else {
     launch_output<T, NM, 3>(grid, stream, x, dt, z, a, bct, out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf,
