@@ -587,7 +587,7 @@ def main():
     traffic = profiled_traffic(elems) if w.name == "long_64k_bf16" else None
     roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / VALU_PEAK_TFLOPS, 4), "traffic": traffic,
-                "kernel": "k_output (output pass, both A instantiations; the geometric one does the work here)",
+                "kernel": "k_output (output pass; the workload's A takes its geometric body)",
                 "kernel_ms": round(per["k_output"], 4)}
     hbm_gbs = abytes / (ms_step * 1e-3) / 1e9
     line = {

@@ -243,23 +243,22 @@ __device__ __forceinline__ void summary_tile_states(int N, int lane, const float
 
 // ---------------------------------------------------------------------------
 // k_summary: grid (d_inner / 64, nchunk, batch), block 64.  DS as above; P is
-// always written (both carries compose with it).
+// always written (both carries compose with it).  Each wavefront tests its
+// channels' A rows and runs the geometric or the general body (a
+// wavefront-uniform branch: one launch serves both kinds of channels).
 // ---------------------------------------------------------------------------
 template <typename T, int NM, bool GEO, int DS>
-__global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T* __restrict__ dt,
-                                                const float* __restrict__ A, const float* __restrict__ bct,
-                                                const float* __restrict__ dt_bias, int L, int D, int N, int chunk,
-                                                int nchunk, int nsub, int ntile, float* __restrict__ Sf,
-                                                float* __restrict__ Sr, float* __restrict__ P,
-                                                float* __restrict__ R, float* __restrict__ SIG) {
+__device__ __forceinline__ void summary_body(const T* __restrict__ x, const T* __restrict__ dt,
+                                             const float* __restrict__ Arow, const float* __restrict__ bct,
+                                             const float* __restrict__ dt_bias, int L, int D, int N, int chunk,
+                                             int nchunk, int nsub, int ntile, float* __restrict__ Sf,
+                                             float* __restrict__ Sr, float* __restrict__ P, float* __restrict__ R,
+                                             float* __restrict__ SIG, float (*sR)[64], float (*sS)[64],
+                                             float (*sB)[kSub]) {
   constexpr int SUB = static_cast<int>(kSub);
-  static_assert(NM * SUB <= 64 * 4, "one float4 of B per lane");
   // the boundary states feed only an output pass that runs both chains left to right; a
   // reverse-only pass walks right to left and carries its state across tiles instead
   constexpr bool kStoreR = DS == 3;
-  __shared__ float sR[(DS & 2) ? NM : 1][64];
-  __shared__ float sS[(DS & 1) ? NM : 1][64];
-  __shared__ __align__(16) float sB[GEO ? NM : 1][SUB];  // this tile's B, one row per state (GEO)
   const int lane = threadIdx.x;
   const int d = blockIdx.x * 64 + lane;
   const int c = blockIdx.y;
@@ -268,13 +267,7 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
   const int te = min(L, t0 + chunk);
   const size_t row = static_cast<size_t>(b) * L;
   const size_t cbase = static_cast<size_t>(b) * nchunk + c;
-
-  const float* __restrict__ Arow = A + static_cast<size_t>(d) * N;
   const float a0 = Arow[0];
-  bool geo_lane = true;
-  for (int n = 0; n < N; ++n) geo_lane = geo_lane && (Arow[n] == static_cast<float>(n + 1) * a0);
-  // Each wavefront runs in exactly one of the two instantiations (general / geometric A).
-  if (wave_geometric(geo_lane) != GEO) return;
   for (int n = 0; n < N; ++n) {
     if (DS & 2) sR[(DS & 2) ? n : 0][lane] = 0.0f;
     if (DS & 1) sS[(DS & 1) ? n : 0][lane] = 0.0f;
@@ -301,7 +294,7 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
       const int n = min(lane / (SUB / 4), N - 1);
       const int part = lane % (SUB / 4);
       const float4 v = *reinterpret_cast<const float4*>(bt + static_cast<size_t>(n) * 2 * SUB + part * 4);
-      if (lane < NM * (SUB / 4)) *reinterpret_cast<float4*>(&sB[GEO ? lane / (SUB / 4) : 0][part * 4]) = v;
+      if (lane < NM * (SUB / 4)) *reinterpret_cast<float4*>(&sB[lane / (SUB / 4)][part * 4]) = v;
     }
     float dl[SUB], u[SUB];
     tile_delta<SUB>(dr, bias, nvalid, dl);
@@ -332,6 +325,31 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
   }
 }
 
+template <typename T, int NM, int DS>
+__global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T* __restrict__ dt,
+                                                const float* __restrict__ A, const float* __restrict__ bct,
+                                                const float* __restrict__ dt_bias, int L, int D, int N, int chunk,
+                                                int nchunk, int nsub, int ntile, float* __restrict__ Sf,
+                                                float* __restrict__ Sr, float* __restrict__ P,
+                                                float* __restrict__ R, float* __restrict__ SIG) {
+  static_assert(NM * static_cast<int>(kSub) <= 64 * 4, "one float4 of B per lane");
+  __shared__ float sR[(DS & 2) ? NM : 1][64];
+  __shared__ float sS[(DS & 1) ? NM : 1][64];
+  __shared__ __align__(16) float sB[NM][kSub];  // the tile's B, one row per state (geometric body)
+  const int d = blockIdx.x * 64 + threadIdx.x;
+  const float* __restrict__ Arow = A + static_cast<size_t>(d) * N;
+  const float a0 = Arow[0];
+  bool geo_lane = true;
+  for (int n = 0; n < N; ++n) geo_lane = geo_lane && (Arow[n] == static_cast<float>(n + 1) * a0);
+  if (wave_geometric(geo_lane)) {
+    summary_body<T, NM, true, DS>(x, dt, Arow, bct, dt_bias, L, D, N, chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG,
+                                  sR, sS, sB);
+  } else {
+    summary_body<T, NM, false, DS>(x, dt, Arow, bct, dt_bias, L, D, N, chunk, nchunk, nsub, ntile, Sf, Sr, P, R,
+                                   SIG, sR, sS, sB);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // k_carry: one thread per (b, n, d); sequential over chunks in both directions.
 // The two directions run in one loop (two independent chains), and the inputs
@@ -345,7 +363,7 @@ __global__ __launch_bounds__(256) void k_carry(const float* __restrict__ Sf, con
                                                float* __restrict__ Cr, const float* __restrict__ h_in,
                                                const float* __restrict__ A, float* __restrict__ A2T, int batch,
                                                int nchunk, int N, int D) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const size_t total = static_cast<size_t>(batch) * N * D;
   if (idx >= total) return;
@@ -546,23 +564,20 @@ __device__ __forceinline__ void output_tile_states_rwalk(int N, int D, int lane,
 // wavefronts run the same loop in step; without this they would all wait for
 // memory at the same time and then all compute).
 // ---------------------------------------------------------------------------
-template <typename T, int NM, int DIRS, bool GEO>
-__global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T* __restrict__ dt,
-                                               const T* __restrict__ z, const float* __restrict__ A,
-                                               const float* __restrict__ bct, const float* __restrict__ Dv,
-                                               const float* __restrict__ dt_bias, T* __restrict__ out, int L, int D,
-                                               int N, int chunk, int nchunk, int nsub, int ntile, int gate,
-                                               const float* __restrict__ Cf, const float* __restrict__ Cr,
-                                               const float* __restrict__ R, const float* __restrict__ SIG,
-                                               const float* __restrict__ A2T, float* __restrict__ h_out) {
+template <typename T, int DIRS, bool GEO>
+__device__ __forceinline__ void output_body(const T* __restrict__ x, const T* __restrict__ dt,
+                                            const T* __restrict__ z, float a0, const float* __restrict__ bct,
+                                            const float* __restrict__ Dv, const float* __restrict__ dt_bias,
+                                            T* __restrict__ out, int L, int D, int N, int chunk, int nchunk, int nsub,
+                                            int ntile, int gate, const float* __restrict__ Cf,
+                                            const float* __restrict__ Cr, const float* __restrict__ R,
+                                            const float* __restrict__ SIG, const float* __restrict__ A2T,
+                                            float* __restrict__ h_out, float (*sHf)[64], T (*sX)[64], T (*sDT)[64],
+                                            T (*sZ)[64]) {
   constexpr int SUB = static_cast<int>(kSub);
   // DIRS bit 2: reverse readout only, tiles walked right to left with the reverse state carried
   constexpr bool kRW = (DIRS & 4) != 0;
   constexpr int DR = DIRS & 3;  // the readouts
-  __shared__ float sHf[NM][64];  // per-lane carried state (forward, or reverse for kRW), by state index
-  __shared__ __align__(16) T sX[SUB][64];
-  __shared__ __align__(16) T sDT[SUB][64];
-  __shared__ __align__(16) T sZ[SUB][64];
   const int lane = threadIdx.x;
   const int d = blockIdx.x * 64 + lane;
   const size_t col0 = static_cast<size_t>(blockIdx.x) * 64;
@@ -572,13 +587,6 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
   const int te = min(L, t0 + chunk);
   const size_t row = static_cast<size_t>(b) * L;
   const size_t cbase = static_cast<size_t>(b) * nchunk + c;
-
-  const float* __restrict__ Arow = A + static_cast<size_t>(d) * N;
-  const float a0 = Arow[0];
-  bool geo_lane = true;
-  for (int n = 0; n < N; ++n) geo_lane = geo_lane && (Arow[n] == static_cast<float>(n + 1) * a0);
-  // Each wavefront runs in exactly one of the two instantiations (general / geometric A).
-  if (wave_geometric(geo_lane) != GEO) return;
   for (int n = 0; n < N; ++n) sHf[n][lane] = (kRW ? Cr : Cf)[(cbase * N + n) * D + d];
   const float a20 = a0 * kLog2e;
   const float bias = dt_bias ? dt_bias[d] : 0.0f;
@@ -669,6 +677,33 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
   }
   if (!kRW && h_out != nullptr && c == nchunk - 1) {
     for (int n = 0; n < N; ++n) h_out[(static_cast<size_t>(b) * D + d) * N + n] = sHf[n][lane];
+  }
+}
+
+template <typename T, int NM, int DIRS>
+__global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T* __restrict__ dt,
+                                               const T* __restrict__ z, const float* __restrict__ A,
+                                               const float* __restrict__ bct, const float* __restrict__ Dv,
+                                               const float* __restrict__ dt_bias, T* __restrict__ out, int L, int D,
+                                               int N, int chunk, int nchunk, int nsub, int ntile, int gate,
+                                               const float* __restrict__ Cf, const float* __restrict__ Cr,
+                                               const float* __restrict__ R, const float* __restrict__ SIG,
+                                               const float* __restrict__ A2T, float* __restrict__ h_out) {
+  __shared__ float sHf[NM][64];  // per-lane carried state (forward, or reverse for a right-to-left walk)
+  __shared__ __align__(16) T sX[kSub][64];
+  __shared__ __align__(16) T sDT[kSub][64];
+  __shared__ __align__(16) T sZ[kSub][64];
+  const int d = blockIdx.x * 64 + threadIdx.x;
+  const float* __restrict__ Arow = A + static_cast<size_t>(d) * N;
+  const float a0 = Arow[0];
+  bool geo_lane = true;
+  for (int n = 0; n < N; ++n) geo_lane = geo_lane && (Arow[n] == static_cast<float>(n + 1) * a0);
+  if (wave_geometric(geo_lane)) {
+    output_body<T, DIRS, true>(x, dt, z, a0, bct, Dv, dt_bias, out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf, Cr,
+                               R, SIG, A2T, h_out, sHf, sX, sDT, sZ);
+  } else {
+    output_body<T, DIRS, false>(x, dt, z, a0, bct, Dv, dt_bias, out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf,
+                                Cr, R, SIG, A2T, h_out, sHf, sX, sDT, sZ);
   }
 }
 
@@ -926,20 +961,16 @@ static void launch_output(dim3 grid, hipStream_t stream, const T* x, const T* dt
                           const float* bct, T* out, int L, int D, int N, int chunk, int nchunk, int nsub, int ntile,
                           int gate, const float* Cf, const float* Cr, const float* R, const float* SIG,
                           const float* A2T) {
-  hipLaunchKernelGGL((k_output<T, NM, DIRS, true>), grid, dim3(64), 0, stream, x, dt, z, a.A, bct, a.D, a.dt_bias,
-                     out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf, Cr, R, SIG, A2T, a.h_out);
-  hipLaunchKernelGGL((k_output<T, NM, DIRS, false>), grid, dim3(64), 0, stream, x, dt, z, a.A, bct, a.D, a.dt_bias,
-                     out, L, D, N, chunk, nchunk, nsub, ntile, gate, Cf, Cr, R, SIG, A2T, a.h_out);
+  hipLaunchKernelGGL((k_output<T, NM, DIRS>), grid, dim3(64), 0, stream, x, dt, z, a.A, bct, a.D, a.dt_bias, out, L,
+                     D, N, chunk, nchunk, nsub, ntile, gate, Cf, Cr, R, SIG, A2T, a.h_out);
 }
 
 template <typename T, int NM, int DS>
 static void launch_summary(dim3 grid, hipStream_t stream, const T* x, const T* dt, const ScanArgs& a,
                            const float* bct, int L, int D, int N, int chunk, int nchunk, int nsub, int ntile, float* Sf,
                            float* Sr, float* P, float* R, float* SIG) {
-  hipLaunchKernelGGL((k_summary<T, NM, true, DS>), grid, dim3(64), 0, stream, x, dt, a.A, bct, a.dt_bias, L, D, N,
-                     chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG);
-  hipLaunchKernelGGL((k_summary<T, NM, false, DS>), grid, dim3(64), 0, stream, x, dt, a.A, bct, a.dt_bias, L, D, N,
-                     chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG);
+  hipLaunchKernelGGL((k_summary<T, NM, DS>), grid, dim3(64), 0, stream, x, dt, a.A, bct, a.dt_bias, L, D, N, chunk,
+                     nchunk, nsub, ntile, Sf, Sr, P, R, SIG);
 }
 
 template <typename T, int NM>
@@ -966,8 +997,6 @@ static hipError_t launch_typed(const ScanArgs& a, const Plan& p, void* ws, hipSt
   T* out = static_cast<T*>(a.out);
 
   hipError_t e = hipSuccess;
-  // Both A-path instantiations are launched; every wavefront exits from the one
-  // that does not match its channels' A rows.
   if (stage < 0 || stage == 0) {
     const size_t nbc = static_cast<size_t>(p.batch) * ntile * N * kSub;
     hipLaunchKernelGGL((k_stage_bc<T>), dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0, stream, Bm, Cm,
