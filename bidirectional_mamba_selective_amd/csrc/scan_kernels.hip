@@ -711,23 +711,29 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
 // k_block: one short block of block-cache decoding in a single kernel (the
 // forward direction from the cached state, the reverse direction from zero at
 // the block's last token; the new cache is the forward state after the block).
-// grid (d_inner / 16, batch), block 256 (four wavefronts).  A workgroup owns 16
-// channels and every state of them: lane l of wavefront w runs channel
-// 16 blockIdx.x + l / 4 and state 4 w + l % 4, so the 16 x 16 recurrences of a
-// workgroup run side by side, one per lane, and a block step fills the chip
-// (d_inner / 16 workgroups).  The block is padded to GM tokens (GM in {16, 32,
-// 64, 128}); padding tokens have delta = 0 and no input, so they leave every
-// state unchanged and are never stored.
+// grid (d_inner / 16, batch), block 256 HV (HV groups of four wavefronts).  A
+// workgroup owns 16 channels and every state of them: lane l of wavefront w of
+// a group runs channel 16 blockIdx.x + l / 4 and state 4 w + l % 4, so the
+// 16 x 16 recurrences of a workgroup run side by side, one per lane, and a
+// block step fills the chip (d_inner / 16 workgroups).  The block is padded to
+// GM tokens (GM in {16, 32, 64, 128}); padding tokens have delta = 0 and no
+// input, so they leave every state unchanged and are never stored.  With
+// HV = 2 (GM = 128) the two halves of the block run side by side, one per
+// group, so each recurrence walks 64 tokens at a time:
+//   first half: forward chain from the cache   | second half: reverse chain from zero
+//   (both leave their state at the halves' boundary in LDS; barrier)
+//   first half: reverse chain from the second  | second half: forward chain from the
+//   half's boundary state                      | first half's end state; the new cache
+// Each chain is exact: it starts from the state that enters its half.
 //   1. every global load of the kernel is issued at once, from clamped in-bounds
 //      addresses: the lane's A[d,n] and cached state, and per (token, channel)
 //      dt, x, z, and B, C; delta, delta*x, the skip term D*x and the gate SiLU(z)
 //      go to LDS, B and C (fp32) too;
-//   2. each lane: abar and delta*x*B per token in registers, the forward chain
-//      from the cache (its state per token kept), the new cache, then the
-//      reverse chain, and C_t[n] (h_fwd + h_rev) per token; the four states of a
-//      channel in a wavefront are summed across the lane quad (DPP), the four
-//      wavefronts' sums meet in LDS and are added in a fixed order
-//      (deterministic);
+//   2. each lane: abar and delta*x*B per token of its half in registers, the two
+//      chains as above with the state per token kept, and C_t[n] (h_fwd + h_rev)
+//      per token; the four states of a channel in a wavefront are summed across
+//      the lane quad (DPP), the four wavefronts' sums meet in LDS and are added
+//      in a fixed order (deterministic);
 //   3. skip term, gate, store.
 // ---------------------------------------------------------------------------
 template <typename T>
@@ -757,6 +763,7 @@ struct BlockSmem {
   __attribute__((aligned(16))) float b[16][kRow];
   __attribute__((aligned(16))) float c[16][kRow];
   float part[4][GM][16];
+  float edge[GM > 64 ? 2 : 1][GM > 64 ? 16 : 1][16];  // GM = 128: [fwd, rev][state][channel] at the halves' boundary
 };
 
 // sum over the lane quad (the four states of a channel): lanes (0+1) + (2+3) in every quad
@@ -768,18 +775,22 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
-template <typename T, int GM>
-__global__ __launch_bounds__(256) void k_block(const T* __restrict__ x, const T* __restrict__ dt,
-                                               const T* __restrict__ z, const float* __restrict__ A,
-                                               const T* __restrict__ Bm, const T* __restrict__ Cm,
-                                               const float* __restrict__ Dv, const float* __restrict__ dt_bias,
-                                               const float* h_in, float* h_out, T* __restrict__ out, int G, int D,
-                                               int N, int flags) {
+template <typename T, int GM, int HV>
+__global__ __launch_bounds__(256 * HV) void k_block(const T* __restrict__ x, const T* __restrict__ dt,
+                                                    const T* __restrict__ z, const float* __restrict__ A,
+                                                    const T* __restrict__ Bm, const T* __restrict__ Cm,
+                                                    const float* __restrict__ Dv, const float* __restrict__ dt_bias,
+                                                    const float* h_in, float* h_out, T* __restrict__ out, int G,
+                                                    int D, int N, int flags) {
   using S = BlockSmem<GM>;
-  constexpr int kTpt = GM / 16;  // (token, channel) pairs and B, C elements per thread
+  static_assert(HV == 1 || (HV == 2 && GM == 128), "two halves for 128-token blocks only");
+  constexpr int kThreads = 256 * HV;
+  constexpr int GH = GM / HV;             // tokens per half
+  constexpr int kTpt = GM * 16 / kThreads;  // (token, channel) pairs and B, C elements per thread
   __shared__ S sm;
   const int tid = threadIdx.x;
-  const int wv = tid / 64;
+  const int half = HV == 2 ? tid / 256 : 0;  // wavefront-uniform
+  const int wv = (tid % 256) / 64;
   const int lane = tid % 64;
   const int cl = lane >> 2;           // channel of this lane's recurrence, within the workgroup
   const int n = wv * 4 + (lane & 3);  // its state
@@ -796,8 +807,10 @@ __global__ __launch_bounds__(256) void k_block(const T* __restrict__ x, const T*
   const int nc = min(n, N - 1);
   const float av = A[static_cast<size_t>(d) * N + nc];
   const size_t hs = h_in ? (static_cast<size_t>(b) * D + d) * N + nc : static_cast<size_t>(d) * N + nc;
-  const float hv = (h_in ? h_in : A)[hs];  // read before any write: h_out may alias h_in
-  const int c1 = tid & 15;                 // channel of this thread's (token, channel) pairs
+  // read before any write: h_out may alias h_in (the lanes that use it consume it before the barrier
+  // that precedes every write of h_out)
+  const float hv = (h_in ? h_in : A)[hs];
+  const int c1 = tid & 15;  // channel of this thread's (token, channel) pairs
   const int d1 = blockIdx.x * 16 + c1;
   const float dvv = (Dv ? Dv : A)[d1];
   const float bsv = (dt_bias ? dt_bias : A)[d1];
@@ -805,12 +818,12 @@ __global__ __launch_bounds__(256) void k_block(const T* __restrict__ x, const T*
   float xv[kTpt], dv[kTpt], zv[kTpt], bv[kTpt], cv[kTpt];
 #pragma unroll
   for (int k = 0; k < kTpt; ++k) {
-    const int t = tid / 16 + 16 * k;
+    const int t = tid / 16 + (kThreads / 16) * k;
     const size_t o = (row + min(t, G - 1)) * D + d1;
     xv[k] = ld_any(x + o);
     dv[k] = ld_any(dt + o);
     zv[k] = ld_any(zbase + o);
-    const int i = tid + 256 * k;  // B, C element (state i / GM, token i % GM)
+    const int i = tid + kThreads * k;  // B, C element (state i / GM, token i % GM)
     const size_t ob = (row + min(i % GM, G - 1)) * N + min(i / GM, N - 1);
     bv[k] = ld_any(Bm + ob);
     cv[k] = ld_any(Cm + ob);
@@ -819,7 +832,7 @@ __global__ __launch_bounds__(256) void k_block(const T* __restrict__ x, const T*
   const float skip = Dv ? ((fwd && rev) ? 2.0f : 1.0f) * dvv : 0.0f;
 #pragma unroll
   for (int k = 0; k < kTpt; ++k) {
-    const int t = tid / 16 + 16 * k;
+    const int t = tid / 16 + (kThreads / 16) * k;
     const bool live = t < G;
     const float dl = live ? softplus_f32(dv[k] + bias) : 0.0f;
     const float xl = live ? xv[k] : 0.0f;
@@ -827,94 +840,102 @@ __global__ __launch_bounds__(256) void k_block(const T* __restrict__ x, const T*
     sm.u[t][c1] = dl * xl;
     sm.sx[t][c1] = skip * xl;
     sm.g[t][c1] = (live && gate) ? silu_f32(zv[k]) : 1.0f;
-    const int i = tid + 256 * k;
+    const int i = tid + kThreads * k;
     const bool ok = i / GM < N && i % GM < G;
     sm.b[i / GM][i % GM] = ok ? bv[k] : 0.0f;
     sm.c[i / GM][i % GM] = ok ? cv[k] : 0.0f;
   }
   __syncthreads();
 
-  // 2. this lane's recurrence (states n >= N have B = C = 0: they stay 0 and add nothing)
+  // 2. this lane's recurrences over the tokens t0 .. t0 + GH - 1 of its half (states n >= N have
+  //    B = C = 0: they stay 0 and add nothing)
+  const int t0 = half * GH;
   const float a2 = n < N ? av * kLog2e : 0.0f;
-  float y[GM];
-  float hf = (n < N && h_in) ? hv : 0.0f;
-  if constexpr (GM <= 64) {
-    float a[GM], bb[GM];
+  float a[GH], bb[GH], y[GH];
 #pragma unroll
-    for (int t4 = 0; t4 < GM / 4; ++t4) {
-      const float4 bq = *reinterpret_cast<const float4*>(&sm.b[n][4 * t4]);
-      const float bq4[4] = {bq.x, bq.y, bq.z, bq.w};
+  for (int t4 = 0; t4 < GH / 4; ++t4) {
+    const float4 bq = *reinterpret_cast<const float4*>(&sm.b[n][t0 + 4 * t4]);
+    const float bq4[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * t4 + i;
-        a[t] = fast_exp2(sm.dl[t][cl] * a2);
-        bb[t] = sm.u[t][cl] * bq4[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * t4 + i;
+      a[t] = fast_exp2(sm.dl[t0 + t][cl] * a2);
+      bb[t] = sm.u[t0 + t][cl] * bq4[i];
     }
+  }
+  if (half == 0) {
+    // the forward chain from the cache; its state per token is kept in y
+    float hf = (n < N && h_in) ? hv : 0.0f;
 #pragma unroll
-    for (int t = 0; t < GM; ++t) {
+    for (int t = 0; t < GH; ++t) {
       hf = fmaf(a[t], hf, bb[t]);
       y[t] = fwd ? hf : 0.0f;
     }
-    if (h_out && n < N) h_out[(static_cast<size_t>(b) * D + d) * N + n] = hf;  // padding leaves hf unchanged
+    if (HV == 1) {
+      if (h_out && n < N) h_out[(static_cast<size_t>(b) * D + d) * N + n] = hf;  // padding leaves hf unchanged
+    } else {
+      sm.edge[0][HV == 2 ? n : 0][cl] = hf;
+    }
+  } else {
+    // second half: the reverse chain from zero at the block's last token
     float hr = 0.0f;
 #pragma unroll
-    for (int t4 = GM / 4 - 1; t4 >= 0; --t4) {
-      const float4 cq = *reinterpret_cast<const float4*>(&sm.c[n][4 * t4]);
+    for (int t = GH - 1; t >= 0; --t) {
+      hr = fmaf(a[t], hr, bb[t]);
+      y[t] = rev ? hr : 0.0f;
+    }
+    sm.edge[HV == 2 ? 1 : 0][HV == 2 ? n : 0][cl] = hr;
+  }
+  if (HV == 2) __syncthreads();
+  if (half == 0) {
+    // the reverse chain, entering the first half from the second (zero with one half)
+    float hr = HV == 2 ? sm.edge[HV == 2 ? 1 : 0][HV == 2 ? n : 0][cl] : 0.0f;
+#pragma unroll
+    for (int t4 = GH / 4 - 1; t4 >= 0; --t4) {
+      const float4 cq = *reinterpret_cast<const float4*>(&sm.c[n][t0 + 4 * t4]);
       const float cq4[4] = {cq.x, cq.y, cq.z, cq.w};
+      // with two halves, delta*x*B is formed again here rather than held across the barrier
+      const float4 bq = HV == 2 ? *reinterpret_cast<const float4*>(&sm.b[n][t0 + 4 * t4]) : cq;
+      const float bq4[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
       for (int i = 3; i >= 0; --i) {
         const int t = 4 * t4 + i;
         if (rev) {
-          hr = fmaf(a[t], hr, bb[t]);
+          hr = fmaf(a[t], hr, HV == 2 ? sm.u[t0 + t][cl] * bq4[i] : bb[t]);
           y[t] += hr;
         }
         y[t] = quad_sum(y[t] * cq4[i]);
       }
     }
   } else {
-    // Longer blocks: abar and delta*x*B are formed again in the reverse pass (from the same LDS
-    // values, so bit for bit the same) instead of being kept for every token next to y.
+    // second half: the forward chain from the first half's end state; the new cache
+    float hf = sm.edge[0][HV == 2 ? n : 0][cl];
 #pragma unroll
-    for (int t4 = 0; t4 < GM / 4; ++t4) {
-      const float4 bq = *reinterpret_cast<const float4*>(&sm.b[n][4 * t4]);
+    for (int t4 = 0; t4 < GH / 4; ++t4) {
+      const float4 cq = *reinterpret_cast<const float4*>(&sm.c[n][t0 + 4 * t4]);
+      const float cq4[4] = {cq.x, cq.y, cq.z, cq.w};
+      const float4 bq = *reinterpret_cast<const float4*>(&sm.b[n][t0 + 4 * t4]);
       const float bq4[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 4 * t4 + i;
-        hf = fmaf(fast_exp2(sm.dl[t][cl] * a2), hf, sm.u[t][cl] * bq4[i]);
-        y[t] = fwd ? hf : 0.0f;
-      }
-    }
-    if (h_out && n < N) h_out[(static_cast<size_t>(b) * D + d) * N + n] = hf;  // padding leaves hf unchanged
-    float hr = 0.0f;
-#pragma unroll
-    for (int t4 = GM / 4 - 1; t4 >= 0; --t4) {
-      const float4 bq = *reinterpret_cast<const float4*>(&sm.b[n][4 * t4]);
-      const float4 cq = *reinterpret_cast<const float4*>(&sm.c[n][4 * t4]);
-      const float bq4[4] = {bq.x, bq.y, bq.z, bq.w};
-      const float cq4[4] = {cq.x, cq.y, cq.z, cq.w};
-#pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        const int t = 4 * t4 + i;
-        if (rev) {
-          hr = fmaf(fast_exp2(sm.dl[t][cl] * a2), hr, sm.u[t][cl] * bq4[i]);
-          y[t] += hr;
-        }
+        hf = fmaf(a[t], hf, sm.u[t0 + t][cl] * bq4[i]);
+        if (fwd) y[t] += hf;
         y[t] = quad_sum(y[t] * cq4[i]);
       }
     }
+    if (h_out && n < N) h_out[(static_cast<size_t>(b) * D + d) * N + n] = hf;  // padding leaves hf unchanged
   }
   if ((lane & 3) == 0) {
 #pragma unroll
-    for (int t = 0; t < GM; ++t) sm.part[wv][t][cl] = y[t];
+    for (int t = 0; t < GH; ++t) sm.part[wv][t0 + t][cl] = y[t];
   }
   __syncthreads();
 
   // 3. the four wavefronts' sums in a fixed order; skip term, gate, store
 #pragma unroll
   for (int k = 0; k < kTpt; ++k) {
-    const int t = tid / 16 + 16 * k;
+    const int t = tid / 16 + (kThreads / 16) * k;
     if (t < G) {
       const float acc = ((sm.part[0][t][c1] + sm.part[1][t][c1]) + sm.part[2][t][c1]) + sm.part[3][t][c1];
       st_any(out + (row + t) * D + d1, (acc + sm.sx[t][c1]) * sm.g[t][c1]);
@@ -924,8 +945,9 @@ __global__ __launch_bounds__(256) void k_block(const T* __restrict__ x, const T*
 
 template <typename T, int GM>
 static void launch_block_gm(const ScanArgs& a, int batch, int G, int D, int N, hipStream_t stream) {
+  constexpr int HV = GM > 64 ? 2 : 1;
   const dim3 grid(static_cast<unsigned>(D / 16), static_cast<unsigned>(batch));
-  hipLaunchKernelGGL((k_block<T, GM>), grid, dim3(256), 0, stream, static_cast<const T*>(a.x),
+  hipLaunchKernelGGL((k_block<T, GM, HV>), grid, dim3(256 * HV), 0, stream, static_cast<const T*>(a.x),
                      static_cast<const T*>(a.dt), static_cast<const T*>(a.z), a.A, static_cast<const T*>(a.B),
                      static_cast<const T*>(a.C), a.D, a.dt_bias, a.h_in, a.h_out, static_cast<T*>(a.out), G, D, N,
                      static_cast<int>(a.flags));

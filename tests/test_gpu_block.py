@@ -76,7 +76,7 @@ def test_block_small(G, flags):
 
 
 @pytest.mark.parametrize("N", [1, 5, 16])
-@pytest.mark.parametrize("G", [7, 33])
+@pytest.mark.parametrize("G", [7, 33, 100])
 @pytest.mark.parametrize("jitter", [0.0, 0.2])
 def test_block_state_counts(N, G, jitter):
     """Blocks short enough for the single-kernel path, with state counts that leave the last wavefront
