@@ -718,8 +718,8 @@ __global__ __launch_bounds__(64) void k_output(const T* __restrict__ x, const T*
 // block step fills the chip (d_inner / 16 workgroups).  The block is padded to
 // GM tokens (GM in {16, 32, 64, 128}); padding tokens have delta = 0 and no
 // input, so they leave every state unchanged and are never stored.  With
-// HV = 2 (GM = 128) the two halves of the block run side by side, one per
-// group, so each recurrence walks 64 tokens at a time:
+// HV = 2 (GM >= 32) the two halves of the block run side by side, one per
+// group, so each recurrence walks GM / 2 tokens at a time:
 //   first half: forward chain from the cache   | second half: reverse chain from zero
 //   (both leave their state at the halves' boundary in LDS; barrier)
 //   first half: reverse chain from the second  | second half: forward chain from the
@@ -753,7 +753,7 @@ __device__ __forceinline__ void st_any<bf16_t>(bf16_t* p, float v) {
   p->bits = __builtin_bit_cast(unsigned short, h);
 }
 
-template <int GM>
+template <int GM, int HV>
 struct BlockSmem {
   static constexpr int kRow = GM + 4;  // B and C rows padded: the four states a wavefront reads sit in different banks
   float dl[GM][16];
@@ -763,7 +763,7 @@ struct BlockSmem {
   __attribute__((aligned(16))) float b[16][kRow];
   __attribute__((aligned(16))) float c[16][kRow];
   float part[4][GM][16];
-  float edge[GM > 64 ? 2 : 1][GM > 64 ? 16 : 1][16];  // GM = 128: [fwd, rev][state][channel] at the halves' boundary
+  float edge[HV][HV == 2 ? 16 : 1][16];  // two halves: [fwd, rev][state][channel] at the halves' boundary
 };
 
 // sum over the lane quad (the four states of a channel): lanes (0+1) + (2+3) in every quad
@@ -782,8 +782,8 @@ __global__ __launch_bounds__(256 * HV) void k_block(const T* __restrict__ x, con
                                                     const float* __restrict__ Dv, const float* __restrict__ dt_bias,
                                                     const float* h_in, float* h_out, T* __restrict__ out, int G,
                                                     int D, int N, int flags) {
-  using S = BlockSmem<GM>;
-  static_assert(HV == 1 || (HV == 2 && GM == 128), "two halves for 128-token blocks only");
+  using S = BlockSmem<GM, HV>;
+  static_assert(HV == 1 || (HV == 2 && GM >= 32), "halves of at least 16 tokens");
   constexpr int kThreads = 256 * HV;
   constexpr int GH = GM / HV;             // tokens per half
   constexpr int kTpt = GM * 16 / kThreads;  // (token, channel) pairs and B, C elements per thread
@@ -945,7 +945,7 @@ __global__ __launch_bounds__(256 * HV) void k_block(const T* __restrict__ x, con
 
 template <typename T, int GM>
 static void launch_block_gm(const ScanArgs& a, int batch, int G, int D, int N, hipStream_t stream) {
-  constexpr int HV = GM > 64 ? 2 : 1;
+  constexpr int HV = GM >= 32 ? 2 : 1;  // halves of 16 tokens or more
   const dim3 grid(static_cast<unsigned>(D / 16), static_cast<unsigned>(batch));
   hipLaunchKernelGGL((k_block<T, GM, HV>), grid, dim3(256 * HV), 0, stream, static_cast<const T*>(a.x),
                      static_cast<const T*>(a.dt), static_cast<const T*>(a.z), a.A, static_cast<const T*>(a.B),
