@@ -21,8 +21,9 @@
 //              forward recurrence from zero (composed into the chunk's forward
 //              end state with the decay of everything to the tile's right) and
 //              continues the reverse recurrence from the running state, which
-//              it stores at every tile boundary together with the suffix sum
-//              of delta to the chunk end.  Outputs per (chunk, d, n):
+//              (when both directions are kept) it stores at every tile
+//              boundary together with the suffix sum of delta to the chunk
+//              end.  Outputs per (chunk, d, n):
 //              Sf = forward end state from zero, Sr = reverse start state from
 //              zero, P = product of abar over the chunk.
 //   k_carry    composes the affine chunk maps h -> P h + S in both directions:
@@ -32,7 +33,10 @@
 //              abar and delta*x*B once per token and shares them between the
 //              forward recurrence (from the carried state) and the reverse
 //              recurrence (from the exact boundary state), accumulating
-//              C . (h_fwd + h_rev) per token; then skip term, gate, store.
+//              C . (h_fwd + h_rev) per token; then skip term, gate, store.  A
+//              reverse-only pass walks the tiles right to left instead and
+//              carries its reverse state from tile to tile.
+//   k_block    a whole short block of block-cache decoding in one kernel.
 // The transition is diagonal per (d, n), so nothing here is a dense
 // contraction; the kernels are bound by VALU and transcendental issue.
 //
@@ -40,7 +44,8 @@
 // exactly (the S4D-real initialisation has this form), exp(delta A[d,n]) is
 // the (n+1)-th power of r = exp(delta A[d,0]); the kernels then form abar by
 // one multiplication per state instead of one exponential.  The test is exact
-// and per wavefront; any other A takes the general path.
+// and per wavefront; any other A takes the general path.  Both bodies sit in
+// one kernel behind a wavefront-uniform branch, so one launch serves any mix.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -404,7 +409,14 @@ __global__ __launch_bounds__(256) void k_carry(const float* __restrict__ Sf, con
 // itself.  The memory clobber keeps the compiler from moving LDS accesses
 // across a wait.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) through the builtin, so that the compiler's own wait insertion knows that every
+// vector memory operation issued so far is complete (with an opaque asm wait it kept adding waits of
+// its own for loads already waited for: 1-2 % of the output pass); the empty asm keeps memory accesses
+// from moving across it.
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt at their maxima (not waited for)
+  asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ void wait_lds_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Direct-to-LDS load of a [kSub x 64] tile of a token-major [*, D] tensor
