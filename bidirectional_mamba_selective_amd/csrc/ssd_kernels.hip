@@ -76,6 +76,18 @@ __device__ __forceinline__ uint16_t to_bf(float v) { return __builtin_bit_cast(u
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// 16 bytes of a run's output (token 16w + l/4 of the run, channels 8(l%4)..+7 of head h) through a
+// buffer resource whose range ends at the sequence end: rows past it are dropped by the hardware, so
+// the store is issued by every lane without a branch.
+__device__ __forceinline__ void store_run_row(uint16_t* out, int64_t b, int64_t L, int64_t HP, int64_t t0,
+                                              int64_t h, int row, int part, uint4 v) {
+  const int64_t nv = L - t0 < Q ? L - t0 : Q;  // valid tokens of the run
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(out + (b * L + t0) * HP + h * P, static_cast<short>(0),
+                                                               static_cast<int>(nv * HP * 2), 0x00020000);
+  const uint32_t off = static_cast<uint32_t>((row * HP + 8 * part) * 2);
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, off, 0, 0);
+}
+
 // LDS tiles of bf16 rows, in 16-byte chunks of 8 elements.  Chunk c of row r is
 // stored at a swizzled chunk position so that 16 lanes reading the same chunk
 // of 16 consecutive rows hit different banks.
@@ -586,6 +598,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_fsweep(Args a) {
   issue(0);
   if (w == 0) token_prep(sTok[0], pdt, sub0 * Q + l < a.L, Ah, bias, l);
   pdt = pdt2;
+  // a run's output is stored at the start of the next step's computation, just before that step's
+  // loads are issued: the store has a whole step to complete before the wait for those loads
+  uint4 pend = make_uint4(0, 0, 0, 0);
 
   for (int64_t k = 0; k < nrun; ++k) {
     const int64_t t0 = (sub0 + k) * Q;
@@ -606,6 +621,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_fsweep(Args a) {
     const float tau_run = ptau;
     if (kFwd) state_to_lds(H, sHs, w, l);
     __syncthreads();
+    if (k > 0) store_run_row(a.out, b, a.L, HP, t0 - Q, h, 16 * w + (l >> 2), l & 3, pend);
     if (k + 1 < nrun) issue(k + 1);
 
     // ---- compute ----
@@ -648,16 +664,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_fsweep(Args a) {
       }
     }
     tile_rows_to_lds(yslot, o, l);
-    {
-      const int64_t t = t0 + 16 * w + (l >> 2);
-      if (t < a.L)
-        *reinterpret_cast<uint4*>(a.out + (b * a.L + t) * HP + h * P + 8 * (l & 3)) =
-            *reinterpret_cast<const uint4*>(yslot + (l >> 2) * P + 8 * (l & 3));
-    }
+    pend = *reinterpret_cast<const uint4*>(yslot + (l >> 2) * P + 8 * (l & 3));
     if (kFwd) state_update(H, ex(tok[kS * 64 + 63]), sBT, sXW, w, l);
     if (w == 0 && k + 1 < nrun) token_prep(sTok[(k + 1) & 1], pdt, (sub0 + k + 1) * Q + l < a.L, Ah, bias, l);
     pdt = pdt2;
   }
+  store_run_row(a.out, b, a.L, HP, (sub0 + nrun - 1) * Q, h, 16 * w + (l >> 2), l & 3, pend);
 }
 
 // ---------------------------------------------------------------------------
