@@ -96,9 +96,15 @@ struct Raw<float> {
     o[2] = __uint_as_float(v.z);
     o[3] = __uint_as_float(v.w);
   }
-  static __device__ __forceinline__ void store(const float o[4], __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4 q = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+  using Word = u32x4;
+  static __device__ __forceinline__ Word pack(const float o[4]) {
+    return Word{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+  }
+  static __device__ __forceinline__ void store_word(Word q, __amdgpu_buffer_rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b128(q, r, off, 0, kStream);
+  }
+  static __device__ __forceinline__ void store(const float o[4], __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    store_word(pack(o), r, off);
   }
 };
 
@@ -115,10 +121,16 @@ struct Raw<bf16_t> {
     o[3] = __uint_as_float(v.y & 0xffff0000u);
   }
   // round to nearest even, two values per v_cvt_pk_bf16_f32
-  static __device__ __forceinline__ void store(const float o[4], __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  using Word = u32x2;
+  static __device__ __forceinline__ Word pack(const float o[4]) {
     const f32x4 f = {o[0], o[1], o[2], o[3]};
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4)), r, off, 0,
-                                          kStream);
+    return __builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4));
+  }
+  static __device__ __forceinline__ void store_word(Word q, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b64(q, r, off, 0, kStream);
+  }
+  static __device__ __forceinline__ void store(const float o[4], __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    store_word(pack(o), r, off);
   }
 };
 
@@ -209,11 +221,25 @@ __global__ __launch_bounds__(kThreads) void k_conv(Args<T> a) {
     for (int m = 0; m < kBlk; ++m) nxt[m].load(ru, lane_off + (blk * kBlk + (kK - 1) + m) * row_bytes);
   };
   fetch(0);
+  // bf16: a block's outputs are stored during the next block, right after its rows are fetched, so
+  // that the wait for those rows (vector memory completes in order) never waits for the stores
+  constexpr bool kDefer = sizeof(T) == 2;
+  typename Raw<T>::Word pf[kDefer ? kBlk : 1], pr[kDefer ? kBlk : 1];
+  auto flush = [&](int blk) {
+#pragma unroll
+    for (int tt = 0; tt < kBlk; ++tt) {
+      const uint32_t off = lane_off + (blk * kBlk + tt) * row_bytes;
+      if (do_f) Raw<T>::store_word(pf[kDefer ? tt : 0], rf, off);
+      if (do_r) Raw<T>::store_word(pr[kDefer ? tt : 0], rr, off);
+    }
+  };
+  int nblk = 0;  // blocks computed
   for (int blk = 0; blk < kTile / kBlk; ++blk) {
     if (t0 + blk * kBlk >= a.L) break;
 #pragma unroll
     for (int m = 0; m < kBlk; ++m) nxt[m].get(win[2 * (kK - 1) + m]);
     if (blk + 1 < kTile / kBlk) fetch(blk + 1);
+    if (kDefer && blk > 0) flush(blk - 1);
 #pragma unroll
     for (int tt = 0; tt < kBlk; ++tt) {
       const uint32_t off = lane_off + (blk * kBlk + tt) * row_bytes;
@@ -226,7 +252,8 @@ __global__ __launch_bounds__(kThreads) void k_conv(Args<T> a) {
           for (int k = 0; k < kK; ++k) s = fmaf(wf[i][k], win[tt + k][i], s);
           o[i] = act_f32<ACT>(s);
         }
-        Raw<T>::store(o, rf, off);
+        if (kDefer) pf[kDefer ? tt : 0] = Raw<T>::pack(o);
+        else Raw<T>::store(o, rf, off);
       }
       if (do_r) {
         float o[4];
@@ -237,12 +264,15 @@ __global__ __launch_bounds__(kThreads) void k_conv(Args<T> a) {
           for (int k = 0; k < kK; ++k) s = fmaf(wr[i][k], win[tt + 2 * (kK - 1) - k][i], s);
           o[i] = act_f32<ACT>(s);
         }
-        Raw<T>::store(o, rr, off);
+        if (kDefer) pr[kDefer ? tt : 0] = Raw<T>::pack(o);
+        else Raw<T>::store(o, rr, off);
       }
     }
 #pragma unroll
     for (int m = 0; m < 2 * (kK - 1); ++m) copy4(win[m], win[kBlk + m]);
+    ++nblk;
   }
+  if (kDefer && nblk > 0) flush(nblk - 1);
 
   // The cache for the next block: the last 3 rows of (cache ++ sequence).  Only this thread touches
   // these channels of the caches, and it reads all three rows before it writes any, so cache_out
