@@ -207,8 +207,7 @@ template <int SUB, bool GEO, int DS>
 __device__ __forceinline__ void summary_tile_states(int N, int lane, const float (&w)[SUB], const float (&u)[SUB],
                                                     float sigma, float a20, float (*sB)[SUB],
                                                     const float* __restrict__ bt, const float* __restrict__ Arow,
-                                                    float (*sR)[64], float (*sS)[64], float* __restrict__ Rdst,
-                                                    uint32_t r_stride, bool store_r) {
+                                                    float (*sR)[64], float (*sS)[64]) {
   float a[SUB];
 #pragma unroll
   for (int k = 0; k < SUB; ++k) a[k] = 1.0f;
@@ -239,10 +238,7 @@ __device__ __forceinline__ void summary_tile_states(int N, int lane, const float
       q = GEO ? q * qstep : fast_exp2(a2 * sigma);
       sS[n][lane] = fmaf(q, f, sS[n][lane]);
     }
-    if (DS & 2) {
-      sR[n][lane] = r;
-      if (store_r) __builtin_nontemporal_store(r, &Rdst[static_cast<size_t>(n) * r_stride]);
-    }
+    if (DS & 2) sR[n][lane] = r;
   }
 }
 
@@ -301,6 +297,25 @@ __device__ __forceinline__ void summary_body(const T* __restrict__ x, const T* _
       const float4 v = *reinterpret_cast<const float4*>(bt + static_cast<size_t>(n) * 2 * SUB + part * 4);
       if (lane < NM * (SUB / 4)) *reinterpret_cast<float4*>(&sB[lane / (SUB / 4)][part * 4]) = v;
     }
+    // The previous tile's boundary states and suffix sum are stored here, after this tile's loads are
+    // issued: vector memory completes in order, so stores issued before the loads would be waited for
+    // with them.
+    // The stores are issued on every tile, without a branch (on the walk's first tile, and for states
+    // n >= N, they fall outside their resources and are dropped), so the compiler can count them and
+    // wait for the loads alone.
+    if (kStoreR) {
+      const bool have = j < nsub_c - 1;
+      const size_t jp = cbase * nsub + (have ? j : 0);  // the slot of the boundary left of tile j + 1
+      const size_t col0 = static_cast<size_t>(blockIdx.x) * 64;
+      const __amdgpu_buffer_rsrc_t rr =
+          make_rsrc(R + jp * N * D + col0, have ? (static_cast<size_t>(N) * D - col0) * 4 : 0);
+#pragma unroll
+      for (int n = 0; n < NM; ++n)
+        IO<float>::store<kStreamCpol>(sR[(DS & 2) ? n : 0][lane], rr,
+                                      (static_cast<uint32_t>(n) * static_cast<uint32_t>(D) + lane) * 4u, 0);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(SIG + jp * D + col0, have ? 256 : 0);
+      IO<float>::store<kStreamCpol>(sigma, rs, static_cast<uint32_t>(lane) * 4u, 0);
+    }
     float dl[SUB], u[SUB];
     tile_delta<SUB>(dr, bias, nvalid, dl);
     float tile_sum = 0.0f;
@@ -309,18 +324,15 @@ __device__ __forceinline__ void summary_body(const T* __restrict__ x, const T* _
       u[k] = dl[k] * xr[k];
       tile_sum += dl[k];
     }
-    const size_t jb = cbase * nsub + (j - 1);
-    float* Rdst = R + jb * N * D + d;
     if (GEO) {
       float w[SUB];
 #pragma unroll
       for (int k = 0; k < SUB; ++k) w[k] = fast_exp2(dl[k] * a20);
-      summary_tile_states<SUB, true, DS>(N, lane, w, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, kStoreR && j > 0);
+      summary_tile_states<SUB, true, DS>(N, lane, w, u, sigma, a20, sB, bt, Arow, sR, sS);
     } else {
-      summary_tile_states<SUB, false, DS>(N, lane, dl, u, sigma, a20, sB, bt, Arow, sR, sS, Rdst, D, kStoreR && j > 0);
+      summary_tile_states<SUB, false, DS>(N, lane, dl, u, sigma, a20, sB, bt, Arow, sR, sS);
     }
     sigma += tile_sum;
-    if (kStoreR && j > 0) __builtin_nontemporal_store(sigma, &SIG[jb * D + d]);
   }
   for (int n = 0; n < N; ++n) {
     const size_t o = (cbase * N + n) * D + d;
