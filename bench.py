@@ -8,10 +8,17 @@ and output kernels), inputs already resident in HBM.  W untimed steps, then K
 timed steps bracketed by device synchronisations; one JSON line is printed.
 
 Besides the headline tokens/s the line carries:
-  roofline      the output kernel (the dominant one) against the VALU roofline,
-                its duration measured live with HIP events on the stream the
-                library launches on (staged entry point, same arguments);
+  roofline      the output kernel (the dominant one) against the HBM roofline:
+                the call's algorithmic bytes (each input read once, out written
+                once) over that kernel's duration, measured live with HIP events
+                on the stream the library launches on (staged entry point, same
+                arguments), against 8 TB/s; traffic = the kernel's counter bytes;
+  valu          the same kernel's VALU issue: measured instructions per element
+                (committed counters) against the issue rate measured by the
+                microbenchmarks;
   hbm           algorithmic bytes of the whole call / step time vs 8 TB/s;
+  micro         HBM read and copy streams, FMA and v_exp_f32 issue rates, and the
+                empty-kernel launch floor (graph replay) on this box;
   general_A, untied, ssd, conv
                 the same shape off the geometric A path, with untied directions,
                 the Mamba-2 heads and the short convolution (each with its own
@@ -37,12 +44,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "bidir selective-scan tokens/s + achieved HBM GB/s (% peak) at L=65536"
 HBM_PEAK_GBS = 8000.0
-# MI355X published fp32 vector peak; one fp32 FMA = 2 FLOP, one transcendental
-# (v_exp_f32 / v_log_f32 / v_rcp_f32) issues at a quarter of the FMA rate and
-# is counted as the 8 FLOP of the four FMA slots it occupies.
-VALU_PEAK_TFLOPS = 157.3
-FLOP_PER_ELEMENT_OUTPUT = 18  # per (token, channel, state): mul + exp(8) + mul + 2 fma(4) + 2 fma(4)
+NOMINAL_CLOCK_GHZ = 2.4  # MI355X peak engine clock; 256 CUs of 4 SIMDs
+N_SIMD = 1024
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "k_output_long_64k_bf16_traffic.txt")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "k_output_long_64k_bf16_counters.txt")
+MICRO_LIB = os.path.join(ROOT, "bidirectional_mamba_selective_amd", "libbimamba_micro.so")
 KERNEL_SOURCE = os.path.join(ROOT, "bidirectional_mamba_selective_amd", "csrc", "scan_kernels.hip")
 SSD_SOURCE = os.path.join(ROOT, "bidirectional_mamba_selective_amd", "csrc", "ssd_kernels.hip")
 CONV_SOURCE = os.path.join(ROOT, "bidirectional_mamba_selective_amd", "csrc", "conv_kernels.hip")
@@ -78,32 +84,155 @@ def profiled_traffic(launch_elems=None, profile=None, source=None, key="hbm_byte
     return float(m_b.group(1))
 
 
-def cpu_baseline(inp, L, D, nch):
-    """The oracle as it stands on all L tokens of nch channels (exact for those channels:
-    a channel's output depends on that channel and the shared B, C only), scaled to tokens/s of
-    the full channel count.  numpy elementwise work runs on one thread."""
-    import oracle
+def profiled_counters(kernel="k_output"):
+    """VALU instructions per SIMD and lane operations per element of one kernel from the committed SQ
+    counter summary, or None when it is missing or was taken on a different kernel source."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    txt = open(PROFILE_COUNTERS).read()
+    m_src = re.search(r"source_sha256_16:\s*([0-9a-f]+)", txt)
+    if not m_src or m_src.group(1) != kernel_source_hash():
+        return None
+    sec = txt.split(kernel + "<", 1)
+    if len(sec) < 2:
+        return None
+    m = re.search(r"VALU instructions per SIMD:\s*([0-9.eE+]+); lane operations per \(token, channel, state\):"
+                  r"\s*([0-9.]+)", sec[1])
+    return None if not m else {"instructions_per_simd": float(m.group(1)), "lane_ops_per_element": float(m.group(2))}
 
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
-    chan = np.linspace(0, D - 1, nch).astype(np.int64)
-    sub = dict(x=inp["x"][:, :, chan], dt=inp["dt"][:, :, chan], z=inp["z"][:, :, chan], B=inp["B"], C=inp["C"],
-               A=inp["A"][chan], D=inp["D"][chan], dt_bias=inp["dt_bias"][chan])
-    ctx = threadpool_limits(1) if threadpool_limits else None
-    t0 = time.perf_counter()
-    if ctx:
-        with ctx:
-            oracle.scan_fwd(sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], sub["dt_bias"])
-    else:
-        oracle.scan_fwd(sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"], sub["D"], sub["z"], sub["dt_bias"])
-    sec = time.perf_counter() - t0
+
+# The oracle's inputs for the all-cores CPU baseline, set before the worker processes are forked (they
+# inherit them copy-on-write) and cleared afterwards.
+_CPU_SHARED = {}
+
+
+def _oracle_channels(chan):
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    s = _CPU_SHARED
+    with threadpool_limits(1):
+        oracle.scan_fwd(s["x"][:, :, chan], s["dt"][:, :, chan], s["A"][chan], s["B"], s["C"], s["D"][chan],
+                        s["z"][:, :, chan], s["dt_bias"][chan])
+    return len(chan)
+
+
+def cpu_baseline(inp, L, D, nch1, workers):
+    """The oracle as it stands, timed on this host: (1) on one thread over all L tokens of nch1 channels,
+    scaled to the full channel count; (2) over the whole workload (every token and channel), its channels
+    split evenly across `workers` processes, one thread each.  Both are exact for the channels they run: a
+    channel's output depends only on that channel and the shared B, C.  The all-cores figure is the value."""
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
+
     batch = inp["x"].shape[0]
-    tok_s = batch * L / (sec * D / nch)
-    return {"value": tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"all {batch}x{L} tokens of {nch} of {D} channels in {sec:.1f} s on 1 host thread, "
-                      f"scaled by {D}/{nch} to the full channel count"}
+    chan = np.linspace(0, D - 1, nch1).astype(np.int64)
+    _CPU_SHARED.clear()
+    _CPU_SHARED.update(inp)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        _oracle_channels(chan)
+        sec1 = time.perf_counter() - t0
+    tok_s1 = batch * L / (sec1 * D / nch1)
+    shards = np.array_split(np.arange(D, dtype=np.int64), workers)
+    with mp.get_context("fork").Pool(workers) as pool:
+        pool.map(len, [[0]] * workers)  # the workers are up before the clock starts
+        t0 = time.perf_counter()
+        done = sum(pool.map(_oracle_channels, shards, chunksize=1))
+        secn = time.perf_counter() - t0
+    _CPU_SHARED.clear()
+    assert done == D
+    return {"value": round(batch * L / secn, 1), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"the whole workload ({batch}x{L} tokens, {D} channels) in {secn:.1f} s, its channels split "
+                      f"over {workers} processes of one thread each; one thread: {nch1} of {D} channels in "
+                      f"{sec1:.1f} s, scaled by {D}/{nch1} to {tok_s1:.0f} tokens/s",
+            "value_1core": round(tok_s1, 1)}
+
+
+def host_workers():
+    """Worker processes for the all-cores CPU baseline: the host cores this process may run on, at most 16
+    (a GPU machine's CPU share per GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def bench_micro(torch, dev, stream):
+    """Microbenchmarks on this machine, each timed with HIP events on `stream` (median of 5): HBM read-only and
+    copy streams over 4 GiB and 2 GiB, the issue rate of independent fp32 FMAs and of v_exp_f32 at 1 to 8
+    wavefronts per SIMD, and an empty kernel's launch floor replayed from a graph (one 64-lane workgroup,
+    and the block step's grid of 256 workgroups of 512 threads)."""
+    import ctypes
+
+    if not os.path.exists(MICRO_LIB):
+        raise RuntimeError(f"{MICRO_LIB} is missing: build it with `python -m bidirectional_mamba_selective_amd.build`")
+    lib = ctypes.CDLL(MICRO_LIB)
+    vp, sz, ci = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.micro_read.argtypes = [vp, sz, vp, vp]
+    lib.micro_copy.argtypes = [vp, vp, sz, vp]
+    lib.micro_fma.argtypes = [vp, ci, ci, vp]
+    lib.micro_exp.argtypes = [vp, ci, ci, vp]
+    lib.micro_empty.argtypes = [ci, ci, vp]
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(fn, reps=5):
+        ts = []
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if st != 0:
+                raise RuntimeError(f"micro kernel launch failed: {st}")
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts[1:]))
+
+    res = {}
+    src = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    t = timed(lambda: lib.micro_read(ctypes.c_void_p(src.data_ptr()), src.numel(), ctypes.c_void_p(sink.data_ptr()),
+                                     sp))
+    res["hbm_read_gbs"] = round(src.numel() / t / 1e9, 1)
+    half = src.numel() // 2
+    t = timed(lambda: lib.micro_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(src.data_ptr() + half), half,
+                                     sp))
+    res["hbm_copy_gbs"] = round(2 * half / t / 1e9, 1)  # bytes read + bytes written
+    del src
+    fma, ex = {}, {}
+    for w in (1, 2, 4, 8):
+        iters = 4096
+        t = timed(lambda: lib.micro_fma(ctypes.c_void_p(sink.data_ptr()), iters, w, sp))
+        rate = N_SIMD * w * 64 * 8 * iters / t  # lane-FMAs per second
+        fma[str(w)] = round(rate / (256 * NOMINAL_CLOCK_GHZ * 1e9), 1)  # per clock and CU at the nominal clock
+        t = timed(lambda: lib.micro_exp(ctypes.c_void_p(sink.data_ptr()), 1024, w, sp))
+        ex[str(w)] = round(N_SIMD * w * 64 * 8 * 1024 / t / (256 * NOMINAL_CLOCK_GHZ * 1e9), 1)
+    res["fma_lanes_per_clk_per_cu"] = fma
+    res["exp_lanes_per_clk_per_cu"] = ex
+    # clocks per wave64 FMA instruction and SIMD at 4 wavefronts per SIMD (the scan kernels' occupancy)
+    res["fma_clk_per_instruction_4waves"] = round(64 * 4 / fma["4"], 3)
+
+    floor = {}
+    for groups, threads in ((1, 64), (256, 512)):
+        gs = torch.cuda.Stream(dev)
+        gs.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g, stream=gs):
+                for _ in range(200):
+                    lib.micro_empty(groups, threads, ctypes.c_void_p(gs.cuda_stream))
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(4):
+            t0 = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        floor[f"{groups}x{threads}"] = round(float(np.median(ts[1:])) * 1e6 / 200, 2)
+    res["empty_kernel_graph_us"] = floor
+    log(f"micro: read {res['hbm_read_gbs']} GB/s, copy {res['hbm_copy_gbs']} GB/s, fma lanes/clk/CU {fma}, "
+        f"exp {ex}, empty-kernel graph floor {floor} us")
+    return res
 
 
 def up_arr(a, w, torch, I, dev):
@@ -248,7 +377,7 @@ def bench_block(args, w, torch, bm, I, dev):
     return line
 
 
-def bench_batched(args, torch, bm, I, dev, stream, calls=16):
+def bench_batched(args, torch, bm, I, dev, stream, calls=128):
     """The batched workload as a denoising loop: `calls` calls with fresh x, z per call (drawn on the
     device outside the timed region, seed 1000 + call) and dt, B, C, A, D, dt_bias held fixed; each call
     timed with HIP events on the library's stream."""
@@ -276,17 +405,15 @@ def bench_batched(args, torch, bm, I, dev, stream, calls=16):
         if s >= 2:  # the first two calls warm up
             ms.append(e0.elapsed_time(e1))
     m = float(np.mean(ms))
-    log(f"batched: {m:.4f} ms per call (mean of {calls})")
+    tot = float(np.sum(ms))
+    log(f"batched: {calls} calls, {tot:.2f} ms in all, {m:.4f} ms per call")
     return {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "d_inner": w.d_inner, "d_state": w.d_state,
-            "calls": calls, "ms_per_call": round(m, 4), "tokens_per_s": round(w.batch * w.seqlen / (m * 1e-3), 1),
-            "note": "fresh x, z per call drawn on the device outside the timed region; per-call HIP events"}
+            "calls": calls, "ms_all_calls": round(tot, 3), "ms_per_call": round(m, 4),
+            "tokens_per_s": round(calls * w.batch * w.seqlen / (tot * 1e-3), 1),
+            "note": "the workload's 128 denoising calls, fresh x, z per call drawn on the device outside the timed "
+                    "region; per-call HIP events summed"}
 
 
-# matrix-core products per (64-token run, head) of the two SSD sweeps, and per run of the tiling kernel
-SSD_Q, SSD_P, SSD_N = 64, 32, 128
-SSD_FLOP_RSWEEP = 2 * SSD_Q * SSD_Q * SSD_P + 2 * SSD_Q * SSD_N * SSD_P + 2 * (2 * SSD_N * SSD_Q * SSD_P)
-SSD_FLOP_FSWEEP = 2 * (2 * SSD_Q * SSD_N * SSD_P) + 2 * SSD_N * SSD_Q * SSD_P
-SSD_FLOP_STAGE = 2 * SSD_Q * SSD_Q * SSD_N
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -333,20 +460,13 @@ def bench_ssd(args, torch, bm, I, dev, stream):
     per = {n: float(np.mean([evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)]))
            for i, n in enumerate(names)}
     log(f"ssd: {ms:.4f} ms/call; per-kernel ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per.items()))
-    runs = w.batch * ((w.seqlen + SSD_Q - 1) // SSD_Q)
-    flop = {"k_ssd_rsweep": SSD_FLOP_RSWEEP * runs * w.nheads, "k_ssd_fsweep": SSD_FLOP_FSWEEP * runs * w.nheads,
-            "k_ssd_stage": SSD_FLOP_STAGE * runs}
-    dom = max(("k_ssd_rsweep", "k_ssd_fsweep"), key=lambda k: per[k])
-    achieved = flop[dom] / (per[dom] * 1e-3) / 1e12
+    dom = max(per, key=lambda k: per[k])
     tokens = w.batch * w.seqlen
     nc = w.nheads * w.headdim
-    # HBM bytes the call must move: x twice (one per sweep), z once, out written twice and read once (the
-    # reverse sweep's partial output), dt twice, B and C once; per run the tiling kernel writes C and B^T
-    # (bf16) and C B^T (fp32), which the reverse sweep reads once and the forward sweep reads without C B^T
-    tile = SSD_Q * SSD_N * 2
-    io_bytes = (tokens * (nc * 2 * (2 + 1 + 3) + w.nheads * 2 * 2 + 2 * w.d_state * 2)
-                + runs * (2 * tile + SSD_Q * SSD_Q * 4) * 2 + runs * 2 * tile)
+    # algorithmic bytes: x, z read once, out written once, dt, B, C read once (A, D, dt_bias: 3 floats per head)
+    io_bytes = tokens * (3 * nc * 2 + w.nheads * 2 + 2 * w.d_state * 2) + 3 * w.nheads * 4
     pages_flop = 2 * 2 * nc * w.d_state * tokens  # the paper's count: 2 d_inner d_state per token and direction
+    gbs_dom = io_bytes / (per[dom] * 1e-3) / 1e9
     del x, dt, z, B, C, out, ws
     block_us = ssd_block_latency(torch, bm, I, dev, w, A, Dv, bias)
     return {
@@ -354,14 +474,17 @@ def bench_ssd(args, torch, bm, I, dev, stream):
         "d_state": w.d_state, "io_dtype": "bf16", "state_dtype": "f32",
         "ms_per_call": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
         "kernels_ms": {k: round(v, 4) for k, v in per.items()},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "flop_per_launch": flop[dom],
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(gbs_dom, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs_dom / HBM_PEAK_GBS, 4), "bytes_per_launch": io_bytes,
                      "traffic": profiled_traffic(profile=SSD_PROFILE, source=SSD_SOURCE,
-                                                 key=f"hbm_bytes_per_dispatch_{dom}")},
-        "hbm": {"bytes_per_call": io_bytes, "achieved_gbs": round(io_bytes / (ms * 1e-3) / 1e9, 1),
-                "frac_of_peak": round(io_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "scan_tflops_pages_count": round(pages_flop / (ms * 1e-3) / 1e12, 2),
+                                                 key=f"hbm_bytes_per_dispatch_{dom}"),
+                     "note": "the call's algorithmic bytes over the dominant kernel's time"},
+        "hbm": {"algorithmic_bytes": io_bytes, "achieved_gbs": round(io_bytes / (ms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(io_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic": profiled_traffic(profile=SSD_PROFILE, source=SSD_SOURCE, key="hbm_bytes_per_call")},
+        "mfma": {"flop_per_call": pages_flop, "achieved_tflops": round(pages_flop / (ms * 1e-3) / 1e12, 2),
+                 "peak": MFMA_BF16_PEAK_TFLOPS, "frac": round(pages_flop / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                 "note": "the pages' count, 2 d_inner d_state per token and direction, over the whole call"},
         "block_step_us": block_us,
     }
 
@@ -450,13 +573,14 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_64k_bf16")
-    ap.add_argument("--cpu-channels", type=int, default=1536)
+    ap.add_argument("--cpu-channels", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ssd", action="store_true", help="skip the Mamba-2 (SSD) heads measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the batched and block-variant workloads reported beside the headline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
+    ap.add_argument("--no-micro", action="store_true", help="skip the microbenchmarks")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -583,12 +707,29 @@ def main():
     tokens = w.batch * w.seqlen
     abytes = algorithmic_bytes(w.batch, w.seqlen, w.d_inner, w.d_state, es)
     t_out = per["k_output"] * 1e-3
-    achieved = FLOP_PER_ELEMENT_OUTPUT * elems / t_out / 1e12
-    traffic = profiled_traffic(elems) if w.name == "long_64k_bf16" else None
-    roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / VALU_PEAK_TFLOPS, 4), "traffic": traffic,
+    long_shape = w.name == "long_64k_bf16"
+    traffic = profiled_traffic(elems) if long_shape else None
+    gbs_out = abytes / t_out / 1e9
+    roofline = {"bound": "hbm", "achieved": round(gbs_out, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs_out / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "k_output (output pass; the workload's A takes its geometric body)",
-                "kernel_ms": round(per["k_output"], 4)}
+                "kernel_ms": round(per["k_output"], 4), "bytes_per_launch": abytes,
+                "note": "the call's algorithmic bytes (each input read once, out written once) over the output "
+                        "kernel's time"}
+    micro = None if args.no_micro else bench_micro(torch, dev, stream)
+    cnt = profiled_counters() if long_shape else None
+    valu = None
+    if cnt:
+        clk = per["k_output"] * 1e-3 * NOMINAL_CLOCK_GHZ * 1e9 / cnt["instructions_per_simd"]
+        valu = {"kernel": "k_output", "lane_ops_per_element": cnt["lane_ops_per_element"],
+                "instructions_per_simd": cnt["instructions_per_simd"],
+                "clk_per_instruction": round(clk, 3)}
+        if micro:
+            floor = micro["fma_clk_per_instruction_4waves"]
+            valu.update(issue_clk_per_instruction=floor, frac=round(floor / clk, 4))
+        valu["note"] = ("wavefront VALU instructions of one launch per SIMD (committed SQ counters of this kernel "
+                        "source) and the clocks each took at the nominal 2.4 GHz, against independent FMAs issued at "
+                        "4 wavefronts per SIMD (micro)")
     hbm_gbs = abytes / (ms_step * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -606,8 +747,10 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "d_inner": w.d_inner,
                    "d_state": w.d_state, "io_dtype": w.io_dtype, "state_dtype": "f32"},
         "roofline": roofline,
+        "valu": valu,
         "hbm": {"algorithmic_bytes": abytes, "achieved_gbs": round(hbm_gbs, 1),
-                "frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4), "peak_gbs": HBM_PEAK_GBS},
+                "frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4), "peak_gbs": HBM_PEAK_GBS,
+                "traffic": profiled_traffic(elems, key="hbm_bytes_per_call") if long_shape else None},
         "kernels_ms": {k: round(v, 4) for k, v in per.items()},
         "general_A": {"ms_per_step": round(ms_step_gen, 4), "tokens_per_s": round(tokens / (ms_step_gen * 1e-3), 1),
                       "note": "A[d,n] = -(n+1)*(1+0.2*U(-1,1)): no per-channel geometric structure, one exp per "
@@ -619,6 +762,8 @@ def main():
                            "(bimamba_scan_fwd_untied): a forward-only and a reverse-only pass, twice the "
                            "activation bytes and no shared abar"},
     }
+    if micro:
+        line["micro"] = micro
     if not args.no_ssd:
         del x, dt, z, B, C, out, out_r, rev_set, fwd_set, ws
         torch.cuda.empty_cache()
@@ -633,10 +778,15 @@ def main():
         other["block_32k_bf16"] = {k: bl[k] for k in ("value", "unit", "ms_per_step", "us_per_block_graph",
                                                        "us_per_block_eager", "us_per_block_call_graph")}
         other["block_32k_bf16"]["metric"] = bl["metric"]
+        if micro:
+            other["block_32k_bf16"]["empty_kernel_graph_us"] = micro["empty_kernel_graph_us"]
         line["other_configs"] = other
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_channels} channels")
-        line["cpu_baseline"] = cpu_baseline(inp, w.seqlen, w.d_inner, min(args.cpu_channels, w.d_inner))
+        nw = host_workers()
+        log(f"cpu baseline: oracle on one thread ({args.cpu_channels} channels), then the whole workload on {nw} "
+            f"processes")
+        line["cpu_baseline"] = cpu_baseline(inp, w.seqlen, w.d_inner, min(args.cpu_channels, w.d_inner), nw)
+        log(f"cpu baseline: {line['cpu_baseline']['sample']}")
     print(json.dumps(line), flush=True)
 
 

@@ -191,15 +191,26 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context in which the binding allocates an output or workspace the caller did not pass: on the stream
+    the kernels run on, so that the caching allocator never hands the block to other work while those
+    kernels may still use it."""
+    import contextlib
+
+    torch = _torch()
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def bimamba_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, flags: int = 0, workspace=None,
                      stream=None):
     """Full-sequence bidirectional scan; returns out ([batch, seqlen, d_inner], x's dtype)."""
     torch = _torch()
-    nb, L, nd, ns, out = _common(x, dt, A, B, C, D, z, dt_bias, out)
     lib = load()
-    need = int(lib.bimamba_scan_fwd_workspace_bytes(nb, L, nd, ns))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        nb, L, nd, ns, out = _common(x, dt, A, B, C, D, z, dt_bias, out)
+        need = int(lib.bimamba_scan_fwd_workspace_bytes(nb, L, nd, ns))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = lib.bimamba_scan_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
                               _ptr(out), nb, L, nd, ns, _io_dtype(x), flags, _ptr(workspace), _nbytes(workspace),
                               _stream(stream, x.device))
@@ -214,15 +225,17 @@ def bimamba_scan_fwd_untied(fwd, rev, out_f=None, out_r=None, flags: int = 0, wo
     torch = _torch()
     f = {k: fwd.get(k) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")}
     r = {k: rev.get(k) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")}
-    nb, L, nd, ns, out_f = _common(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], f["z"], f["dt_bias"], out_f)
-    shape_r = _common(r["x"], r["dt"], r["A"], r["B"], r["C"], r["D"], r["z"], r["dt_bias"], out_r)
-    if shape_r[:4] != (nb, L, nd, ns) or r["x"].dtype != f["x"].dtype:
-        raise ValueError("the two directions must have the same shapes and I/O dtype")
-    out_r = shape_r[4]
     lib = load()
-    need = int(lib.bimamba_scan_fwd_workspace_bytes(nb, L, nd, ns))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=f["x"].device)
+    with _on(stream):
+        nb, L, nd, ns, out_f = _common(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], f["z"], f["dt_bias"],
+                                       out_f)
+        shape_r = _common(r["x"], r["dt"], r["A"], r["B"], r["C"], r["D"], r["z"], r["dt_bias"], out_r)
+        if shape_r[:4] != (nb, L, nd, ns) or r["x"].dtype != f["x"].dtype:
+            raise ValueError("the two directions must have the same shapes and I/O dtype")
+        out_r = shape_r[4]
+        need = int(lib.bimamba_scan_fwd_workspace_bytes(nb, L, nd, ns))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=f["x"].device)
     ptrs = [_ptr(f[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")] + [_ptr(out_f)]
     ptrs += [_ptr(r[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")] + [_ptr(out_r)]
     st = lib.bimamba_scan_fwd_untied(*ptrs, nb, L, nd, ns, _io_dtype(f["x"]), flags, _ptr(workspace),
@@ -236,7 +249,8 @@ def bimamba_scan_fwd_stage(stage: int, x, dt, A, B, C, D=None, z=None, dt_bias=N
                            workspace=None, stream=None):
     """One stage (0 summary, 1 carry, 2 output) of bimamba_scan_fwd; the caller keeps workspace and out across
     the three calls.  Returns out."""
-    nb, L, nd, ns, out = _common(x, dt, A, B, C, D, z, dt_bias, out)
+    with _on(stream):
+        nb, L, nd, ns, out = _common(x, dt, A, B, C, D, z, dt_bias, out)
     if workspace is None:
         raise ValueError("the staged entry point needs a caller-kept workspace")
     st = load().bimamba_scan_fwd_stage(int(stage), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
@@ -252,13 +266,14 @@ def bimamba_scan_block(x, dt, A, B, C, D=None, z=None, dt_bias=None, h_in=None, 
     """One block of block-cache decoding; returns out.  h_out (fp32 [batch, d_inner, d_state]) receives the
     forward state after the block when given (it may be the same tensor as h_in)."""
     torch = _torch()
-    nb, L, nd, ns, out = _common(x, dt, A, B, C, D, z, dt_bias, out)
-    _check(h_in, "h_in", (nb, nd, ns), torch.float32, x.device)
-    _check(h_out, "h_out", (nb, nd, ns), torch.float32, x.device)
     lib = load()
-    need = int(lib.bimamba_scan_block_workspace_bytes(nb, L, nd, ns))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        nb, L, nd, ns, out = _common(x, dt, A, B, C, D, z, dt_bias, out)
+        _check(h_in, "h_in", (nb, nd, ns), torch.float32, x.device)
+        _check(h_out, "h_out", (nb, nd, ns), torch.float32, x.device)
+        need = int(lib.bimamba_scan_block_workspace_bytes(nb, L, nd, ns))
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wbytes = _nbytes(workspace)
     st = lib.bimamba_scan_block(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
                                 _ptr(h_in), _ptr(h_out), _ptr(out), nb, L, nd, ns, _io_dtype(x), flags,
@@ -303,11 +318,12 @@ def bimamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, flag
     """Bidirectional Mamba-2 (SSD) scan over heads; returns out ([batch, seqlen, nheads*headdim], bf16).
     dt is [batch, seqlen, nheads]; A, D, dt_bias are [nheads] fp32."""
     torch = _torch()
-    nb, L, nh, hp, ns, out = _ssd_common(x, dt, A, B, C, D, z, dt_bias, out)
     lib = load()
-    need = int(lib.bimamba_ssd_fwd_workspace_bytes(nb, L, nh, hp, ns))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        nb, L, nh, hp, ns, out = _ssd_common(x, dt, A, B, C, D, z, dt_bias, out)
+        need = int(lib.bimamba_ssd_fwd_workspace_bytes(nb, L, nh, hp, ns))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = lib.bimamba_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
                              _ptr(out), nb, L, nh, hp, ns, _io_dtype(x), flags, _ptr(workspace), _nbytes(workspace),
                              _stream(stream, x.device))
@@ -319,7 +335,8 @@ def bimamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, flag
 def bimamba_ssd_fwd_stage(stage: int, x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, flags: int = 0,
                           workspace=None, stream=None):
     """One stage (0 B/C tiles, 1 summaries, 2 carry, 3 output) of bimamba_ssd_fwd with a caller-kept workspace."""
-    nb, L, nh, hp, ns, out = _ssd_common(x, dt, A, B, C, D, z, dt_bias, out)
+    with _on(stream):
+        nb, L, nh, hp, ns, out = _ssd_common(x, dt, A, B, C, D, z, dt_bias, out)
     if workspace is None:
         raise ValueError("the staged entry point needs a caller-kept workspace")
     st = load().bimamba_ssd_fwd_stage(int(stage), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
@@ -339,13 +356,14 @@ def bimamba_ssd_block(x, dt, A, B, C, D=None, z=None, dt_bias=None, h_in=None, h
     """One block of block-cache decoding with Mamba-2 heads; returns out.  h_in / h_out are fp32
     [batch, nheads, headdim, d_state] (h_out may be h_in): the cached forward state before and after the block."""
     torch = _torch()
-    nb, L, nh, hp, ns, out = _ssd_common(x, dt, A, B, C, D, z, dt_bias, out)
-    _check(h_in, "h_in", (nb, nh, hp, ns), torch.float32, x.device)
-    _check(h_out, "h_out", (nb, nh, hp, ns), torch.float32, x.device)
     lib = load()
-    need = int(lib.bimamba_ssd_block_workspace_bytes(nb, L, nh, hp, ns))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        nb, L, nh, hp, ns, out = _ssd_common(x, dt, A, B, C, D, z, dt_bias, out)
+        _check(h_in, "h_in", (nb, nh, hp, ns), torch.float32, x.device)
+        _check(h_out, "h_out", (nb, nh, hp, ns), torch.float32, x.device)
+        need = int(lib.bimamba_ssd_block_workspace_bytes(nb, L, nh, hp, ns))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = lib.bimamba_ssd_block(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
                                _ptr(h_in), _ptr(h_out), _ptr(out), nb, L, nh, hp, ns, _io_dtype(x), flags,
                                _ptr(workspace), _nbytes(workspace), _stream(stream, x.device))
@@ -379,7 +397,8 @@ def bimamba_conv1d_bidir(u, w_f=None, b_f=None, w_r=None, b_r=None, out_f=None, 
                          stream=None):
     """Causal (w_f) and anti-causal (w_r) depthwise convolution of u with SiLU; returns (out_f, out_r), None for a
     direction whose filter is None."""
-    nb, L, nc, K, out_f, out_r = _conv_common(u, w_f, b_f, w_r, b_r, out_f, out_r)
+    with _on(stream):
+        nb, L, nc, K, out_f, out_r = _conv_common(u, w_f, b_f, w_r, b_r, out_f, out_r)
     st = load().bimamba_conv1d_bidir(_ptr(u), _ptr(w_f), _ptr(b_f), _ptr(w_r), _ptr(b_r), _ptr(out_f), _ptr(out_r),
                                      nb, L, nc, K, _io_dtype(u), flags, _stream(stream, u.device))
     if st != BIMAMBA_OK:
@@ -392,7 +411,8 @@ def bimamba_conv1d_block(u, w_f=None, b_f=None, w_r=None, b_r=None, cache_in=Non
     """One block of block decoding: the causal filter continues from cache_in ([batch, 3, channels], u's dtype;
     None = zeros), the anti-causal one stops at the block end; cache_out (may be cache_in) receives the last 3
     tokens.  Returns (out_f, out_r)."""
-    nb, L, nc, K, out_f, out_r = _conv_common(u, w_f, b_f, w_r, b_r, out_f, out_r)
+    with _on(stream):
+        nb, L, nc, K, out_f, out_r = _conv_common(u, w_f, b_f, w_r, b_r, out_f, out_r)
     _check(cache_in, "cache_in", (nb, K - 1, nc), u.dtype, u.device)
     _check(cache_out, "cache_out", (nb, K - 1, nc), u.dtype, u.device)
     st = load().bimamba_conv1d_block(_ptr(u), _ptr(w_f), _ptr(b_f), _ptr(w_r), _ptr(b_r), _ptr(cache_in),

@@ -1,8 +1,10 @@
-"""Build libbimamba.so in-tree with hipcc for gfx950.
+"""Build libbimamba.so (and the benchmark's libbimamba_micro.so) in-tree with hipcc for gfx950.
 
     python -m bidirectional_mamba_selective_amd.build
 
-Compiles every source under csrc/ into one shared library next to this file.
+Compiles every source under csrc/ into one shared library next to this file,
+and micro/micro_kernels.hip (the microbenchmarks behind the reported rooflines)
+into a second one.
 """
 from __future__ import annotations
 
@@ -14,6 +16,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbimamba.so")
+MICRO_SRC = os.path.join(PKG, "micro", "micro_kernels.hip")
+MICRO_LIB = os.path.join(PKG, "libbimamba_micro.so")
 ARCH = "gfx950"
 
 # Packed fp32 instructions stay disabled for all device code.
@@ -39,9 +43,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libbimamba.so")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPFLAGS, *extra_flags, "-I", os.path.join(os.path.dirname(PKG), "include"), *sources(), "-o", tmp]
+def _compile(srcs, lib, verbose, extra_flags=()):
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *HIPFLAGS, *extra_flags, "-I", os.path.join(os.path.dirname(PKG), "include"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,8 +55,15 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(noise))
     if verbose and noise:
         print("\n".join(noise))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile both libraries; returns the path of libbimamba.so."""
+    lib = _compile(sources(), LIB, verbose, extra_flags)
+    _compile([MICRO_SRC], MICRO_LIB, verbose, extra_flags)
+    return lib
 
 
 if __name__ == "__main__":

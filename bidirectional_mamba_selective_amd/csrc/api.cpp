@@ -36,6 +36,12 @@ int check_shape(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
   // grid and index limits of the kernels: int token/channel indices, 16-bit grid y/z
   if (seqlen > INT32_MAX / 2 || d_inner > INT32_MAX / 2 || batch > 65535) return BIMAMBA_ERR_UNSUPPORTED;
   if (static_cast<double>(batch) * seqlen * d_inner > 9.0e15) return BIMAMBA_ERR_UNSUPPORTED;
+  // The chunked kernels address a tile's rows, a tile boundary's states and the carries through buffer
+  // resources with 32-bit byte offsets and a range of at most 2^31 - 1 bytes: a tile of kSub token rows
+  // of d_inner elements, and d_state rows of d_inner fp32 states (plus one 256-byte row of slack), must fit.
+  const int64_t es = io_dtype == BIMAMBA_BF16 ? 2 : 4;
+  if (bimamba::kSub * d_inner * es > INT32_MAX || d_state * d_inner * 4 + 256 > INT32_MAX)
+    return BIMAMBA_ERR_UNSUPPORTED;
   return BIMAMBA_OK;
 }
 
@@ -90,7 +96,8 @@ const char* bimamba_status_string(int status) {
 }
 
 size_t bimamba_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
-  if (check_shape(batch, seqlen, d_inner, d_state, BIMAMBA_F32) != BIMAMBA_OK) return 0;
+  // the size does not depend on the I/O dtype; bf16 admits the larger shapes
+  if (check_shape(batch, seqlen, d_inner, d_state, BIMAMBA_BF16) != BIMAMBA_OK) return 0;
   return bimamba::make_plan(batch, seqlen, d_inner, d_state).total;
 }
 
@@ -173,7 +180,7 @@ int bimamba_scan_fwd_untied(const void* x_f, const void* dt_f, const float* A_f,
 }
 
 size_t bimamba_scan_block_workspace_bytes(int64_t batch, int64_t block_len, int64_t d_inner, int64_t d_state) {
-  if (check_shape(batch, block_len, d_inner, d_state, BIMAMBA_F32) != BIMAMBA_OK) return 0;
+  if (check_shape(batch, block_len, d_inner, d_state, BIMAMBA_BF16) != BIMAMBA_OK) return 0;
   if (block_len <= bimamba::kBlockFusedMax) return 0;  // single-kernel path
   return bimamba::make_plan(batch, block_len, d_inner, d_state).total;
 }
@@ -214,7 +221,10 @@ int bimamba_scan_block(const void* x, const void* dt, const float* A, const void
   const Plan p = bimamba::make_plan(batch, block_len, d_inner, d_state);
   s = check_workspace(p, workspace, workspace_bytes, out, out_bytes);
   if (s != BIMAMBA_OK) return s;
-  if (h_out && overlap(range_of(h_out, st_bytes), range_of(workspace, p.total))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  // the staging and summary kernels write the workspace before the carry kernel reads h_in
+  if ((h_out && overlap(range_of(h_out, st_bytes), range_of(workspace, p.total))) ||
+      (h_in && overlap(range_of(h_in, st_bytes), range_of(workspace, p.total))))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
   return map_hip(bimamba::launch_chunked(a, p, workspace, stream));
 }
 
@@ -227,7 +237,9 @@ static int ssd_check_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
   if (io_dtype != BIMAMBA_F32 && io_dtype != BIMAMBA_BF16) return BIMAMBA_ERR_UNSUPPORTED;
   if (io_dtype != BIMAMBA_BF16 || headdim != ssd::kHeadDim || d_state != ssd::kState) return BIMAMBA_ERR_UNSUPPORTED;
   // grid limits: (sub-chunks, batch) for the tiling kernel, one workgroup per (batch, chunk, head) otherwise
-  if (batch > 65535 || nheads > (1 << 20) || seqlen > INT32_MAX / 2) return BIMAMBA_ERR_UNSUPPORTED;
+  // a run's output rows (64 tokens of nheads * headdim bf16 channels) are stored through one buffer
+  // resource whose range is at most 2^31 - 1 bytes
+  if (batch > 65535 || nheads > (1 << 18) || seqlen > INT32_MAX / 2) return BIMAMBA_ERR_UNSUPPORTED;
   const bimamba::ssd::SsdPlan p = bimamba::ssd::make_ssd_plan(batch, seqlen, nheads);
   if (static_cast<double>(batch) * p.nchunk * nheads > 2.0e9 ||
       static_cast<double>(batch) * nheads * ssd::kStateFloats > 2.0e9)

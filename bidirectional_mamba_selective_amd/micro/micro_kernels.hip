@@ -1,0 +1,94 @@
+// Microbenchmarks behind the rooflines the benchmark reports (gfx950): the HBM read and copy streams, the
+// issue rate of independent fp32 FMAs and of v_exp_f32, and an empty kernel for the launch floor.  Built
+// into libbimamba_micro.so, a library of its own: the scan library does not contain or call any of it.
+// Every entry point enqueues one kernel on `stream` and returns the HIP status; the caller times it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Grid-stride read of n float4; the sum is written only if it equals a value no input of the benchmark
+// produces (the store keeps the loads alive without writing anything in practice).
+__global__ __launch_bounds__(256) void k_read(const f32x4* __restrict__ src, size_t n, float* sink) {
+  float acc = 0.0f;
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const f32x4 v = __builtin_nontemporal_load(src + i);
+    acc += (v[0] + v[1]) + (v[2] + v[3]);
+  }
+  if (acc == -1.2345e37f) sink[threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void k_copy(const f32x4* __restrict__ src, f32x4* __restrict__ dst, size_t n) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+// 8 independent FMA chains per lane, `iters` steps each: 8 * iters lane-FMAs per thread.
+__global__ __launch_bounds__(64) void k_fma(float* out, int iters, float a, float b) {
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = static_cast<float>(threadIdx.x + k);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = fmaf(v[k], a, b);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += v[k];
+  if (s == -1.2345e37f) out[threadIdx.x] = s;
+}
+
+// 8 independent v_exp_f32 chains per lane (each step 2^(v * a), which stays finite for |a| < 1).
+__global__ __launch_bounds__(64) void k_exp(float* out, int iters, float a) {
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = 0.01f * static_cast<float>(threadIdx.x + k);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __builtin_amdgcn_exp2f(v[k] * a);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += v[k];
+  if (s == -1.2345e37f) out[threadIdx.x] = s;
+}
+
+__global__ void k_empty() {}
+
+}  // namespace
+
+extern "C" {
+
+int micro_read(const void* src, size_t bytes, float* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(k_read, dim3(256 * 8 * 4), dim3(256), 0, stream, static_cast<const f32x4*>(src), bytes / 16,
+                     sink);
+  return static_cast<int>(hipGetLastError());
+}
+
+int micro_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  hipLaunchKernelGGL(k_copy, dim3(256 * 8 * 4), dim3(256), 0, stream, static_cast<const f32x4*>(src),
+                     static_cast<f32x4*>(dst), bytes / 16);
+  return static_cast<int>(hipGetLastError());
+}
+
+// waves: wavefronts per SIMD (1024 SIMDs on a 256-CU part), one 64-lane wavefront per workgroup
+int micro_fma(float* out, int iters, int waves_per_simd, hipStream_t stream) {
+  hipLaunchKernelGGL(k_fma, dim3(1024 * waves_per_simd), dim3(64), 0, stream, out, iters, 0.999f, 0.001f);
+  return static_cast<int>(hipGetLastError());
+}
+
+int micro_exp(float* out, int iters, int waves_per_simd, hipStream_t stream) {
+  hipLaunchKernelGGL(k_exp, dim3(1024 * waves_per_simd), dim3(64), 0, stream, out, iters, 0.5f);
+  return static_cast<int>(hipGetLastError());
+}
+
+int micro_empty(int groups, int threads, hipStream_t stream) {
+  hipLaunchKernelGGL(k_empty, dim3(groups), dim3(threads), 0, stream);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // extern "C"

@@ -33,9 +33,12 @@
  *   - D == NULL means D = 0; dt_bias == NULL means dt_bias = 0; z may be NULL
  *     only together with BIMAMBA_FLAG_NO_GATE.  Inputs are read-only and out
  *     must not overlap any input or the workspace.
- *   - Supported shapes: batch >= 1, seqlen/block_len >= 1, d_inner a positive
- *     multiple of 64, 1 <= d_state <= 16; anything else returns
- *     BIMAMBA_ERR_UNSUPPORTED (bad values) or BIMAMBA_ERR_INVALID_ARGUMENT.
+ *   - Supported shapes: 1 <= batch <= 65535, seqlen/block_len >= 1, d_inner a
+ *     positive multiple of 64, 1 <= d_state <= 16, and the kernels' 32-bit
+ *     buffer offsets: 16 * d_inner * element size and d_state * d_inner * 4 + 256
+ *     bytes at most 2^31 - 1 (d_inner <= 33554368 at d_state 16); anything else
+ *     returns BIMAMBA_ERR_UNSUPPORTED (unsupported values) or
+ *     BIMAMBA_ERR_INVALID_ARGUMENT (non-positive sizes).
  *   - All arguments are validated before any HIP call, so a rejected call has
  *     no side effect.  Launch failures return BIMAMBA_ERR_HIP.
  *   - Calls are re-entrant; the library keeps no mutable global state.
@@ -146,7 +149,8 @@ size_t bimamba_scan_block_workspace_bytes(int64_t batch, int64_t block_len, int6
  *          otherwise overlap it, nor any input or out; h_in must not overlap
  *          out.  The flags select the directions summed into out; h_out is the
  *          forward state in every case.
- * workspace may be NULL when bimamba_scan_block_workspace_bytes returns 0. */
+ * workspace may be NULL when bimamba_scan_block_workspace_bytes returns 0;
+ * otherwise neither h_in nor h_out may overlap it. */
 int bimamba_scan_block(const void* x, const void* dt, const float* A, const void* B, const void* C,
                        const float* D, const void* z, const float* dt_bias,
                        const float* h_in, float* h_out, void* out,
@@ -171,7 +175,7 @@ int bimamba_scan_block(const void* x, const void* dt, const float* A, const void
  * carried in fp32.
  * Layouts: x, z, out [batch, seqlen, nheads * headdim]; dt [batch, seqlen,
  * nheads]; B, C [batch, seqlen, d_state]; A, D, dt_bias [nheads] fp32.
- * Supported: io_dtype BIMAMBA_BF16, headdim 32, d_state 128, any nheads >= 1,
+ * Supported: io_dtype BIMAMBA_BF16, headdim 32, d_state 128, 1 <= nheads <= 2^18,
  * seqlen >= 1, batch >= 1 (others return BIMAMBA_ERR_UNSUPPORTED).  x, z, out,
  * B and C must be 16-byte aligned, dt 2-byte aligned, A, D, dt_bias 4-byte
  * aligned.  Flags, D == NULL, dt_bias == NULL, z == NULL, ownership,

@@ -52,6 +52,70 @@ def tol_for(io_dtype):
     return 2e-2 if io_dtype == "bf16" else 1e-4
 
 
+class Bar:
+    """Parity bars for one kind of result.
+
+    norm: ||o - r|| / ||r|| over the whole compared tensor (the target's tolerance);
+    row:  the same ratio for every row (the last axis: the compared channels of one token, or the states of
+          one channel), with ||r_row|| floored at 5 % of the rms row norm so that rows the gate or the data
+          make nearly zero are held to an absolute bound instead;
+    rel, abs: every element satisfies |o - r| <= rel * |r| + abs * rms(r).
+    """
+
+    def __init__(self, norm, row, rel, abs_):
+        self.norm, self.row, self.rel, self.abs = norm, row, rel, abs_
+
+
+# bf16 output: the kernel's fp32 result is rounded to nearest even, |o - y| <= 2^-8 |y| (half an ulp of an
+# 8-bit significand); the fp32 arithmetic before it is good to ~1e-6 of the output's rms.
+_BF16_ROUND = 2.0 ** -8
+BARS = {
+    # per-channel S6 scan and the short convolution
+    "f32": Bar(1e-4, 1e-4, 1e-4, 1e-5),
+    "bf16": Bar(2e-2, 2e-2, _BF16_ROUND * 1.001, 2e-4),
+    # the short convolution in fp32: four products and a SiLU per output
+    "conv_f32": Bar(1e-5, 1e-5, 1e-5, 1e-6),
+    # fp32 states (the block cache of the S6 scan)
+    "state": Bar(1e-5, 1e-5, 1e-5, 1e-6),
+    # Mamba-2 heads: bf16 output; the products take bf16 operands with fp32 accumulation
+    "ssd": Bar(2e-2, 2e-2, _BF16_ROUND * 1.001, 2e-2),
+    "ssd_state": Bar(1e-2, 1e-2, 1e-2, 2e-2),
+}
+
+
+def bar_for(kind):
+    return BARS[kind]
+
+
+def check(got, want, kind, tag=""):
+    """Assert every bar of BARS[kind] (kind may also be a Bar) for got against want (fp64 arrays of one
+    shape, rows along the last axis).  Returns the measured figures."""
+    b = kind if isinstance(kind, Bar) else BARS[kind]
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, f"{tag}: shape {got.shape} != {want.shape}"
+    assert np.all(np.isfinite(got)), f"{tag}: non-finite output"
+    diff = got - want
+    den = np.linalg.norm(want.ravel())
+    norm = float(np.linalg.norm(diff.ravel()) / den) if den > 0 else float(np.linalg.norm(diff.ravel()))
+    w2 = want.reshape(-1, want.shape[-1]) if want.ndim > 1 else want.reshape(1, -1)
+    d2 = diff.reshape(w2.shape)
+    rn = np.linalg.norm(w2, axis=1)
+    floor = 0.05 * float(np.sqrt(np.mean(rn ** 2))) if rn.size else 0.0
+    floor = max(floor, 1e-300)
+    row = float(np.max(np.linalg.norm(d2, axis=1) / np.maximum(rn, floor))) if rn.size else 0.0
+    rms = float(np.sqrt(np.mean(want ** 2))) if want.size else 0.0
+    allow = b.rel * np.abs(want) + b.abs * rms
+    elem = float(np.max(np.abs(diff) / np.maximum(allow, 1e-300))) if want.size else 0.0
+    res = {"norm": norm, "row": row, "elem": elem}
+    say(f"{tag}: normwise {norm:.3e} (bar {b.norm:.0e}), worst row {row:.3e} (bar {b.row:.0e}), "
+        f"worst element at {elem:.3f} of its bound")
+    assert norm <= b.norm, f"{tag}: normwise rel err {norm:.3e} > {b.norm}"
+    assert row <= b.row, f"{tag}: worst row rel err {row:.3e} > {b.row}"
+    assert elem <= 1.0, f"{tag}: an element exceeds |o-r| <= {b.rel:.2e}|r| + {b.abs:.0e} rms (x{elem:.2f})"
+    return res
+
+
 def upload(inp, io_dtype):
     """Device tensors for one input dict of fp32 arrays (exact in io_dtype)."""
     dev = {}

@@ -359,3 +359,44 @@ def test_ssd_block_workspace():
     assert [_lib.bimamba_ssd_block_workspace_bytes(2, g, 8, 32, 128) for g in (1, 32, 64)] == [0, 0, 0]
     assert _lib.bimamba_ssd_block_workspace_bytes(2, 100, 8, 32, 128) == \
         _lib.bimamba_ssd_fwd_workspace_bytes(2, 100, 8, 32, 128) > 0
+
+
+def call_fwd_wide(d, n=16, io=_lib.BIMAMBA_BF16, L=1):
+    """scan_fwd with fake tensors 1 GiB apart (room for activations of tens of millions of channels)."""
+    lib = _lib.load()
+
+    def p(i):
+        return ctypes.c_void_p((1 << 40) + i * (1 << 30))
+
+    return lib.bimamba_scan_fwd(p(0), p(1), p(2), p(3), p(4), p(5), p(6), p(7), p(8), 1, L, d, n, io, 0, p(9), 0, None)
+
+
+def test_scan_rejects_channels_past_32bit_buffer_offsets():
+    """The chunked kernels address a tile's token rows and a boundary's d_state state rows through buffer
+    resources of at most 2^31 - 1 bytes with 32-bit offsets: d_inner <= 33554368 at d_state 16."""
+    edge, past = 33554368, 33554432
+    BF16, F32 = _lib.BIMAMBA_BF16, _lib.BIMAMBA_F32
+    assert call_fwd_wide(edge) == WS  # accepted: stops at the workspace size
+    assert call_fwd_wide(past) == UNS  # d_state rows of fp32 states exceed 2^31 - 1 bytes
+    assert call_fwd_wide(edge, io=F32) == WS
+    assert call_fwd_wide(past, io=F32, n=8) == UNS  # 16 token rows of fp32 exceed 2^31 - 1 bytes
+    assert call_fwd_wide(past, io=BF16, n=8) == WS  # bf16 rows and 8 state rows still fit
+    assert call_fwd_wide(2 * past, io=BF16, n=4) == UNS  # 16 bf16 token rows of 2^26 channels: 2^31 bytes
+    f = _lib.bimamba_scan_fwd_workspace_bytes
+    assert f(1, 1, edge, 16) > 0 and f(1, 1, past, 16) == 0
+
+
+def test_scan_block_rejects_cache_overlapping_workspace():
+    """Past the single-kernel limit the staging and summary kernels write the workspace before the carry
+    kernel reads h_in: a workspace over h_in (or h_out) is rejected."""
+    assert call_block(L=200, ws=fake(10), wsb=1 << 40) == INV  # over h_in
+    assert call_block(L=200, ws=fake(11), wsb=1 << 40) == INV  # over h_out
+    # with h_in NULL the workspace may sit where h_in was (h_out is 64 MiB further on): the call then gets
+    # as far as launching, which the fake pointers must not reach, so only the rejections are exercised here
+
+
+def test_ssd_rejects_head_counts_past_the_output_buffer_range():
+    lib = _lib.load()
+    f = lib.bimamba_ssd_fwd_workspace_bytes
+    assert f(1, 64, 1 << 18, 32, 128) > 0
+    assert f(1, 64, (1 << 18) + 1, 32, 128) == 0

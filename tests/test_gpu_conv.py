@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from bidirectional_mamba_selective_amd import inputs
-from tests.gpu_util import f32_dev, rel_err, say, to_dev, to_host64, tol_for, torch_mod
+from tests.gpu_util import check, f32_dev, say, to_dev, to_host64, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -41,10 +41,9 @@ def test_conv_bidir(batch, L, C, io):
     f, r = bimamba_conv1d_bidir(d["u"], d["w_f"], d["b_f"], d["w_r"], d["b_r"])
     torch.cuda.synchronize()
     wf, wr = oracle.conv_bidir(cs["u"], cs["w_f"], cs["b_f"], cs["w_r"], cs["b_r"])
-    ef, er = rel_err(to_host64(f), wf), rel_err(to_host64(r), wr)
-    say(f"  rel err fwd {ef:.3e} rev {er:.3e}")
-    tol = 1e-5 if io == "f32" else 1e-2
-    assert ef <= tol and er <= tol
+    kind = "conv_f32" if io == "f32" else "bf16"
+    check(to_host64(f), wf, kind, f"conv {batch}x{L}x{C} {io} fwd")
+    check(to_host64(r), wr, kind, f"conv {batch}x{L}x{C} {io} rev")
 
 
 @pytest.mark.parametrize("mode", ["fwd_only", "rev_only", "no_silu", "tied", "no_bias"])
@@ -68,11 +67,11 @@ def test_conv_variants(mode):
                                 None if mode == "fwd_only" else w_r, b_r, flags=flags)
     torch.cuda.synchronize()
     if mode != "rev_only":
-        assert rel_err(to_host64(f), oracle.conv_causal(cs["u"], cs["w_f"], bf_h, act=act)) <= 1e-5
+        check(to_host64(f), oracle.conv_causal(cs["u"], cs["w_f"], bf_h, act=act), "conv_f32", f"conv {mode} fwd")
     else:
         assert f is None
     if mode != "fwd_only":
-        assert rel_err(to_host64(r), oracle.conv_anticausal(cs["u"], wr_h, br_h, act=act)) <= 1e-5
+        check(to_host64(r), oracle.conv_anticausal(cs["u"], wr_h, br_h, act=act), "conv_f32", f"conv {mode} rev")
     else:
         assert r is None
 
@@ -93,7 +92,7 @@ def test_conv_blocks_chained(io):
     cache_dev = to_dev(np.zeros((2, 3, C), np.float32), io)
     cache_h = None
     pos = 0
-    tol = 1e-5 if io == "f32" else 1e-2
+    kind = "conv_f32" if io == "f32" else "bf16"
     for n, G in enumerate(sizes):
         blk = d["u"][:, pos:pos + G].contiguous()
         in_place = n % 2 == 0
@@ -102,8 +101,8 @@ def test_conv_blocks_chained(io):
                                     cache_in=cache_dev if n > 0 else None, cache_out=cout)
         torch.cuda.synchronize()
         wf, wr, wc = oracle.conv_block(cs["u"][:, pos:pos + G], cs["w_f"], cs["b_f"], cs["w_r"], cs["b_r"], cache_h)
-        assert rel_err(to_host64(f), wf) <= tol, f"block {n} fwd"
-        assert rel_err(to_host64(r), wr) <= tol, f"block {n} rev"
+        check(to_host64(f), wf, kind, f"conv block {n} fwd")
+        check(to_host64(r), wr, kind, f"conv block {n} rev")
         assert np.array_equal(to_host64(cout), wc), f"block {n} cache"  # the cache is a copy of inputs
         cache_dev, cache_h = cout, wc
         pos += G
@@ -122,10 +121,8 @@ def test_conv_full_size_sampled():
     torch.cuda.synchronize()
     ch = np.random.default_rng(1).choice(4096, 24, replace=False)
     wf, wr = oracle.conv_bidir(cs["u"][:, :, ch], cs["w_f"][ch], cs["b_f"][ch], cs["w_r"][ch], cs["b_r"][ch])
-    ef = rel_err(to_host64(f[:, :, torch.from_numpy(ch).cuda()]), wf)
-    er = rel_err(to_host64(r[:, :, torch.from_numpy(ch).cuda()]), wr)
-    say(f"  rel err fwd {ef:.3e} rev {er:.3e}")
-    assert ef <= 1e-2 and er <= 1e-2
+    check(to_host64(f[:, :, torch.from_numpy(ch).cuda()]), wf, "bf16", "conv 64k fwd")
+    check(to_host64(r[:, :, torch.from_numpy(ch).cuda()]), wr, "bf16", "conv 64k rev")
 
 
 def test_conv_then_untied_scan():
@@ -148,6 +145,5 @@ def test_conv_then_untied_scan():
     hf, hr = oracle.conv_bidir(cs["u"], cs["w_f"], cs["b_f"], cs["w_r"], cs["b_r"])
     host = dict(dt=act["dt"], B=act["B"], C=act["C"], z=act["z"], A=A, D=Dv, dt_bias=bias)
     want_f, want_r = oracle.scan_fwd_untied(dict(host, x=hf), dict(host, x=hr))
-    ef, er = rel_err(to_host64(of), want_f), rel_err(to_host64(orr), want_r)
-    say(f"  rel err fwd {ef:.3e} rev {er:.3e}")
-    assert ef <= tol_for("f32") and er <= tol_for("f32")
+    check(to_host64(of), want_f, "f32", "conv -> untied scan out_f")
+    check(to_host64(orr), want_r, "f32", "conv -> untied scan out_r")

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 from bidirectional_mamba_selective_amd import inputs as I
-from tests.gpu_util import rel_err, say, to_host64, tol_for, upload
+from tests.gpu_util import Bar, check, say, to_host64, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -55,9 +55,8 @@ def test_untied_two_sets(io, L):
     r = _set(2, L, 128, 16, io, seed=12, a_jitter=0.2, param_seed=5)
     got_f, got_r = _run(f, r, io)
     want_f, want_r = oracle.scan_fwd_untied(f, r)
-    ef, er = rel_err(got_f, want_f), rel_err(got_r, want_r)
-    say(f"untied {io} L={L}: out_f {ef:.3e} out_r {er:.3e}")
-    assert ef <= tol_for(io) and er <= tol_for(io)
+    check(got_f, want_f, io, f"untied {io} L={L} out_f")
+    check(got_r, want_r, io, f"untied {io} L={L} out_r")
 
 
 def test_untied_no_gate_and_small_states():
@@ -65,9 +64,8 @@ def test_untied_no_gate_and_small_states():
     r = _set(1, 777, 64, 5, "f32", seed=22, a_jitter=0.0, param_seed=2)
     got_f, got_r = _run(f, r, "f32", flags=1)
     want_f, want_r = oracle.scan_fwd_untied(f, r, gate=False)
-    ef, er = rel_err(got_f, want_f), rel_err(got_r, want_r)
-    say(f"untied no gate N=5: out_f {ef:.3e} out_r {er:.3e}")
-    assert ef <= 1e-4 and er <= 1e-4
+    check(got_f, want_f, "f32", "untied no gate N=5 out_f")
+    check(got_r, want_r, "f32", "untied no gate N=5 out_r")
 
 
 def test_untied_equal_sets_sum_to_tied():
@@ -81,9 +79,8 @@ def test_untied_equal_sets_sum_to_tied():
     d = upload(s, "f32")
     tied = to_host64(bimamba_scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], d["dt_bias"]))
     torch.cuda.synchronize()
-    err = rel_err(got_f + got_r, tied)
-    say(f"untied equal sets vs tied: {err:.3e}")
-    assert err <= 1e-5
+    # two fp32 computations of one result by different kernel paths: 1e-5 in every sense
+    check(got_f + got_r, tied, Bar(1e-5, 1e-5, 1e-5, 1e-6), "untied equal sets vs tied")
 
 
 def test_untied_layer_2k_subset():
@@ -99,9 +96,8 @@ def test_untied_layer_2k_subset():
                     else c[k])) for k in ("x", "dt", "z", "B", "C", "A", "D", "dt_bias")}
 
     want_f, want_r = oracle.scan_fwd_untied(sub(f), sub(r))
-    ef, er = rel_err(got_f[:, :, chan], want_f), rel_err(got_r[:, :, chan], want_r)
-    say(f"untied layer 2k subset: out_f {ef:.3e} out_r {er:.3e}")
-    assert ef <= tol_for("bf16") and er <= tol_for("bf16")
+    check(got_f[:, :, chan], want_f, "bf16", "untied layer 2k subset out_f")
+    check(got_r[:, :, chan], want_r, "bf16", "untied layer 2k subset out_r")
 
 
 @pytest.mark.parametrize("G", [32, 200])
@@ -137,8 +133,8 @@ def test_untied_block_decoding_from_two_block_calls(G):
                                            h_host, fwd=True, rev=False)
         want_r, _ = oracle.scan_block(hr["x"], hr["dt"], r["A"], hr["B"], hr["C"], r["D"], hr["z"], r["dt_bias"],
                                       None, fwd=False, rev=True)
-        ef, er, eh = rel_err(to_host64(out_f), want_f), rel_err(to_host64(out_r), want_r), rel_err(to_host64(h), want_h)
-        ec = rel_err(to_host64(out_f), full_f[:, sl])
-        say(f"untied block G={G} {k}: out_f {ef:.3e} out_r {er:.3e} cache {eh:.3e} vs full forward {ec:.3e}")
-        assert ef <= tol_for("f32") and er <= tol_for("f32") and eh <= 1e-5 and ec <= tol_for("f32")
+        check(to_host64(out_f), want_f, "f32", f"untied block G={G} {k} out_f")
+        check(to_host64(out_r), want_r, "f32", f"untied block G={G} {k} out_r")
+        check(to_host64(h), want_h, "state", f"untied block G={G} {k} cache")
+        check(to_host64(out_f), full_f[:, sl], "f32", f"untied block G={G} {k} out_f vs full forward")
         h_host = want_h
