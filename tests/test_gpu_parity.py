@@ -121,10 +121,10 @@ def test_impulse_crosses_chunks(a_jitter):
     dev = upload(inp, "f32")
     out = to_host64(run_fwd(dev, flags=NO_GATE, use_D=False, use_z=False))
     want = oracle_fwd(inp, gate=False, use_D=False)
-    check(out, want, "f32", "impulse")
-    # the far field on each side is carry-only: held to the bars against its own scale
-    check(out[:, :200], want[:, :200], "f32", "impulse far left")
-    check(out[:, 3800:], want[:, 3800:], "f32", "impulse far right")
+    # An impulse response is concentrated near its source, so the whole output's rms is no scale for the far
+    # field: every 200-token window is held to the bars against its own scale (the far windows on each side
+    # are carry-only).
+    check_windows(out, want, 200, "impulse")
 
 
 def test_deterministic():
@@ -179,6 +179,18 @@ def test_delta_limits(shift, a_jitter):
     inp = case(2, 300, 128, 16, "f32", seed=int(abs(shift)) + 3, a_jitter=a_jitter)
     inp["dt_bias"] = (inp["dt_bias"] + np.float32(shift)).astype(np.float32)
     check_variants(inp, "f32", variants=VARIANTS[:2], tag=f"delta_shift{shift:+.0f}")
+
+
+def check_windows(got, want, width, tag):
+    """check() on every window of `width` tokens whose reference rms lies well inside fp32's normal range
+    (1e-20): each window against its own scale.  Returns how many windows were checked."""
+    n = 0
+    for t0 in range(0, want.shape[1], width):
+        sl = slice(t0, t0 + width)
+        if np.sqrt(np.mean(want[:, sl] ** 2)) > 1e-20:
+            check(got[:, sl], want[:, sl], "f32", f"{tag} tokens {t0}..{min(t0 + width, want.shape[1]) - 1}")
+            n += 1
+    return n
 
 
 def _long_fp32_case(a_jitter):
@@ -245,9 +257,7 @@ def test_long_64k_impulse_carry(a_jitter):
     del out, dev
     torch.cuda.empty_cache()
     want = oracle.scan_fwd(hx, hdt, A[chan], hB, hC, None, None, bias[chan], gate=False)
-    check(got, want, "f32", "long_64k impulse")
-    # chunks of 1024 tokens: the source chunk, its neighbours and chunks far on either side
-    for c in (0, 27, 28, 29, 30, 31, 40, 63):
-        sl = slice(c * 1024, (c + 1) * 1024)
-        if np.sqrt(np.mean(want[:, sl] ** 2)) > 1e-20:  # well inside fp32's normal range
-            check(got[:, sl], want[:, sl], "f32", f"long_64k impulse chunk {c}")
+    # every chunk of 1024 tokens against its own scale: all but the source's are carried in from elsewhere
+    n = check_windows(got, want, 1024, "long_64k impulse")
+    say(f"long_64k impulse: {n} of 64 chunks carry a response inside fp32's normal range")
+    assert n >= 16
