@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     bimamba_scan_block,
     bimamba_scan_block_workspace_bytes,
     bimamba_scan_fwd,
+    bimamba_scan_fwd_noalloc,
     bimamba_scan_fwd_stage,
     bimamba_scan_fwd_untied,
     bimamba_scan_fwd_workspace_bytes,

@@ -19,6 +19,7 @@ BIMAMBA_ERR_INVALID_ARGUMENT = 1
 BIMAMBA_ERR_UNSUPPORTED = 2
 BIMAMBA_ERR_WORKSPACE_TOO_SMALL = 3
 BIMAMBA_ERR_HIP = 4
+BIMAMBA_ERR_SCRATCH_TOO_SMALL = 5
 
 BIMAMBA_F32 = 0
 BIMAMBA_BF16 = 1
@@ -35,6 +36,7 @@ EXPORTED = (
     "bimamba_scan_fwd_workspace_bytes",
     "bimamba_scan_fwd",
     "bimamba_scan_fwd_stage",
+    "bimamba_scan_fwd_noalloc",
     "bimamba_scan_fwd_untied",
     "bimamba_scan_block_workspace_bytes",
     "bimamba_scan_block",
@@ -79,6 +81,9 @@ def load() -> ctypes.CDLL:
     lib.bimamba_scan_fwd_stage.restype = ctypes.c_int
     lib.bimamba_scan_fwd_stage.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                            ctypes.c_int, ctypes.c_uint32, vp, sz, vp]
+    lib.bimamba_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.bimamba_scan_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                             ctypes.c_uint32, vp]
     lib.bimamba_scan_fwd_untied.restype = ctypes.c_int
     lib.bimamba_scan_fwd_untied.argtypes = [vp] * 18 + [i64, i64, i64, i64, ctypes.c_int, ctypes.c_uint32, vp, sz, vp]
     lib.bimamba_scan_block.restype = ctypes.c_int
@@ -216,6 +221,19 @@ def bimamba_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, fla
                               _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_scan_fwd")
+    return out
+
+
+def bimamba_scan_fwd_noalloc(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, flags: int = 0, stream=None):
+    """bimamba_scan_fwd with the library's fixed scratch buffer as its workspace (the C call allocates nothing;
+    out is allocated here only when not passed).  Returns out."""
+    lib = load()
+    with _on(stream):
+        nb, L, nd, ns, out = _common(x, dt, A, B, C, D, z, dt_bias, out)
+    st = lib.bimamba_scan_fwd_noalloc(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                                      _ptr(out), nb, L, nd, ns, _io_dtype(x), flags, _stream(stream, x.device))
+    if st != BIMAMBA_OK:
+        raise BimambaError(st, "bimamba_scan_fwd_noalloc")
     return out
 
 

@@ -91,6 +91,7 @@ const char* bimamba_status_string(int status) {
     case BIMAMBA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case BIMAMBA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case BIMAMBA_ERR_HIP: return "HIP launch error";
+    case BIMAMBA_ERR_SCRATCH_TOO_SMALL: return "problem too large for the library's 256 MiB scratch buffer";
     default: return "unknown status";
   }
 }
@@ -132,6 +133,28 @@ int bimamba_scan_fwd_stage(int stage, const void* x, const void* dt, const float
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return scan_fwd_impl(stage, x, dt, A, B, C, D, z, dt_bias, out, batch, seqlen, d_inner, d_state, io_dtype, flags,
                        workspace, workspace_bytes, stream);
+}
+
+int bimamba_scan_fwd_noalloc(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* dt_bias, void* out, int64_t batch,
+                             int64_t seqlen, int64_t d_inner, int64_t d_state, int io_dtype, uint32_t flags,
+                             hipStream_t stream) {
+  int s = check_shape(batch, seqlen, d_inner, d_state, io_dtype);
+  if (s != BIMAMBA_OK) return s;
+  s = check_tensors(x, dt, A, B, C, D, z, dt_bias, out, batch, seqlen, d_inner, d_state, io_dtype, flags);
+  if (s != BIMAMBA_OK) return s;
+  const Plan p = bimamba::make_plan(batch, seqlen, d_inner, d_state);
+  if (p.total > bimamba::kScratchBytes) return BIMAMBA_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  if (bimamba::scratch_address(&ws) != hipSuccess) return BIMAMBA_ERR_HIP;
+  // out must not overlap the scratch array (the library's own memory, so only a caller that passed a
+  // pointer into it could make them overlap)
+  const size_t es = io_dtype == BIMAMBA_BF16 ? 2 : 4;
+  if (overlap(range_of(ws, bimamba::kScratchBytes),
+              range_of(out, static_cast<size_t>(batch) * seqlen * d_inner * es)))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  bimamba::ScanArgs a{x, dt, A, B, C, D, z, dt_bias, out, nullptr, nullptr, io_dtype, flags};
+  return map_hip(bimamba::launch_chunked(a, p, ws, stream));
 }
 
 int bimamba_scan_fwd_untied(const void* x_f, const void* dt_f, const float* A_f, const void* B_f, const void* C_f,

@@ -31,6 +31,13 @@ struct ScanArgs {
 // stage < 0 launches all three; 0, 1, 2 launch one of them.
 hipError_t launch_chunked(const ScanArgs& a, const Plan& p, void* workspace, hipStream_t stream, int stage = -1);
 
+// Size of the library's fixed device scratch array (csrc/scratch.hip), which holds the workspace of
+// the allocation-free entry point.
+constexpr size_t kScratchBytes = size_t{256} << 20;
+
+// Address of the scratch array on the current device (looked up once per device).
+hipError_t scratch_address(void** out);
+
 // Single-kernel block step for block_len <= kBlockFusedMax: one workgroup per
 // (16 channels, batch element), one lane per (channel, state) recurrence; no workspace.
 hipError_t launch_block_fused(const ScanArgs& a, int64_t batch, int64_t block_len, int64_t d_inner,

@@ -59,7 +59,8 @@ typedef enum {
   BIMAMBA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad flag combination, misaligned pointer */
   BIMAMBA_ERR_UNSUPPORTED = 2,        /* shape or dtype outside the supported set */
   BIMAMBA_ERR_WORKSPACE_TOO_SMALL = 3,
-  BIMAMBA_ERR_HIP = 4                 /* a HIP launch returned an error */
+  BIMAMBA_ERR_HIP = 4,                /* a HIP launch returned an error */
+  BIMAMBA_ERR_SCRATCH_TOO_SMALL = 5   /* bimamba_scan_fwd_noalloc: the problem needs more than 256 MiB */
 } bimamba_status;
 
 typedef enum { BIMAMBA_F32 = 0, BIMAMBA_BF16 = 1 } bimamba_dtype;
@@ -107,6 +108,26 @@ int bimamba_scan_fwd_stage(int stage, const void* x, const void* dt, const float
                            int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                            int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/* bimamba_scan_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is the library's own
+ * fixed device array of 256 MiB (each GPU the library runs on holds one copy
+ * until the process ends); the call allocates and frees nothing.  A shape
+ * whose bimamba_scan_fwd_workspace_bytes exceeds 256 MiB (268435456 bytes;
+ * e.g. L * d_inner above about 2^25 at d_state 16) returns
+ * BIMAMBA_ERR_SCRATCH_TOO_SMALL, checked before any HIP call.  All other
+ * arguments, checks and results are those of bimamba_scan_fwd (bit for bit).
+ * Every call on one GPU uses that GPU's one array: two calls that overlap in
+ * time on the same GPU (different streams, or host threads without ordering)
+ * race and both produce garbage; calls ordered on one stream are safe.  The
+ * array's contents are not cleared between calls (nothing in it needs to start
+ * at zero).  The first call on each device looks up the array's address there
+ * (hipGetSymbolAddress with that device current). */
+int bimamba_scan_fwd_noalloc(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* dt_bias, void* out,
+                             int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                             int io_dtype, uint32_t flags, hipStream_t stream);
 
 /* Bidirectional scan with untied directions: the forward and the reverse
  * scans are two separate selective-SSM layers, each with its own input

@@ -400,3 +400,32 @@ def test_ssd_rejects_head_counts_past_the_output_buffer_range():
     f = lib.bimamba_ssd_fwd_workspace_bytes
     assert f(1, 64, 1 << 18, 32, 128) > 0
     assert f(1, 64, (1 << 18) + 1, 32, 128) == 0
+
+
+def test_noalloc_validates_and_rejects_problems_past_its_scratch():
+    """bimamba_scan_fwd_noalloc: the checks of bimamba_scan_fwd, then a problem whose workspace exceeds the
+    256 MiB scratch array is rejected before any HIP call."""
+    lib = _lib.load()
+
+    def call(**kw):
+        a = dict(x=fake(0), dt=fake(1), A=fake(2), B=fake(3), C=fake(4), D=fake(5), z=fake(6), dt_bias=fake(7),
+                 out=fake(8), batch=1, L=64, d=64, n=16, io=_lib.BIMAMBA_BF16, flags=0)
+        a.update(kw)
+        return lib.bimamba_scan_fwd_noalloc(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["dt_bias"],
+                                            a["out"], a["batch"], a["L"], a["d"], a["n"], a["io"], a["flags"], None)
+
+    assert call(x=None) == INV
+    assert call(d=100) == UNS
+    assert call(flags=_lib.FLAG_FWD_ONLY | _lib.FLAG_REV_ONLY) == INV
+    big = _lib.bimamba_scan_fwd_workspace_bytes(1, 16384, 4096, 16)
+    assert big > 256 << 20
+    # 16384 tokens of 4096 channels: the activations are 128 MiB apart, so the overlap checks pass
+    lib2 = lib
+
+    def p(i):
+        return ctypes.c_void_p((1 << 40) + i * (1 << 30))
+
+    st = lib2.bimamba_scan_fwd_noalloc(p(0), p(1), p(2), p(3), p(4), p(5), p(6), p(7), p(8), 1, 16384, 4096, 16,
+                                       _lib.BIMAMBA_BF16, 0, None)
+    assert st == _lib.BIMAMBA_ERR_SCRATCH_TOO_SMALL
+    assert "scratch" in _lib.status_string(st)
