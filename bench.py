@@ -169,7 +169,7 @@ def bench_micro(torch, dev, stream):
     vp, sz, ci = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     lib.micro_read.argtypes = [vp, sz, vp, vp]
     lib.micro_copy.argtypes = [vp, vp, sz, vp]
-    lib.micro_fma.argtypes = [vp, ci, ci, vp]
+    lib.micro_fma.argtypes = [vp, ci, ci, vp, vp]
     lib.micro_exp.argtypes = [vp, ci, ci, vp]
     lib.micro_empty.argtypes = [ci, ci, vp]
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -199,14 +199,22 @@ def bench_micro(torch, dev, stream):
                                      sp))
     res["hbm_copy_gbs"] = round(2 * half / t / 1e9, 1)  # bytes read + bytes written
     del src
+    clk = torch.zeros(8192, dtype=torch.int64, device=dev)
+    # the shader clock under a full FMA load at 4 wavefronts per SIMD (the scans' occupancy)
+    lib.micro_fma(ctypes.c_void_p(sink.data_ptr()), 4096, 4, ctypes.c_void_p(clk.data_ptr()), sp)
+    torch.cuda.synchronize()
+    c = clk.cpu().numpy().reshape(-1, 2)
+    ghz = float(np.median(c[:, 0] / np.maximum(c[:, 1], 1))) * 0.1
+    res["clock_ghz_under_fma_load"] = round(ghz, 3)
     fma, ex = {}, {}
     for w in (1, 2, 4, 8):
         iters = 4096
-        t = timed(lambda: lib.micro_fma(ctypes.c_void_p(sink.data_ptr()), iters, w, sp))
+        t = timed(lambda: lib.micro_fma(ctypes.c_void_p(sink.data_ptr()), iters, w, ctypes.c_void_p(clk.data_ptr()),
+                                        sp))
         rate = N_SIMD * w * 64 * 8 * iters / t  # lane-FMAs per second
-        fma[str(w)] = round(rate / (256 * NOMINAL_CLOCK_GHZ * 1e9), 1)  # per clock and CU at the nominal clock
+        fma[str(w)] = round(rate / (256 * ghz * 1e9), 1)  # per clock and CU at the measured clock
         t = timed(lambda: lib.micro_exp(ctypes.c_void_p(sink.data_ptr()), 1024, w, sp))
-        ex[str(w)] = round(N_SIMD * w * 64 * 8 * 1024 / t / (256 * NOMINAL_CLOCK_GHZ * 1e9), 1)
+        ex[str(w)] = round(N_SIMD * w * 64 * 8 * 1024 / t / (256 * ghz * 1e9), 1)
     res["fma_lanes_per_clk_per_cu"] = fma
     res["exp_lanes_per_clk_per_cu"] = ex
     # clocks per wave64 FMA instruction and SIMD at 4 wavefronts per SIMD (the scan kernels' occupancy)
@@ -720,16 +728,18 @@ def main():
     cnt = profiled_counters() if long_shape else None
     valu = None
     if cnt:
-        clk = per["k_output"] * 1e-3 * NOMINAL_CLOCK_GHZ * 1e9 / cnt["instructions_per_simd"]
+        ghz = micro["clock_ghz_under_fma_load"] if micro else NOMINAL_CLOCK_GHZ
+        clk = per["k_output"] * 1e-3 * ghz * 1e9 / cnt["instructions_per_simd"]
         valu = {"kernel": "k_output", "lane_ops_per_element": cnt["lane_ops_per_element"],
-                "instructions_per_simd": cnt["instructions_per_simd"],
+                "instructions_per_simd": cnt["instructions_per_simd"], "clock_ghz": ghz,
                 "clk_per_instruction": round(clk, 3)}
         if micro:
             floor = micro["fma_clk_per_instruction_4waves"]
             valu.update(issue_clk_per_instruction=floor, frac=round(floor / clk, 4))
         valu["note"] = ("wavefront VALU instructions of one launch per SIMD (committed SQ counters of this kernel "
-                        "source) and the clocks each took at the nominal 2.4 GHz, against independent FMAs issued at "
-                        "4 wavefronts per SIMD (micro)")
+                        "source) and the clocks each took at the shader clock measured under load (micro), against "
+                        "independent VGPR-operand FMAs issued at 4 wavefronts per SIMD (micro); the kernel's "
+                        "transcendentals issue at a quarter of that rate")
     hbm_gbs = abytes / (ms_step * 1e-3) / 1e9
     line = {
         "metric": METRIC,

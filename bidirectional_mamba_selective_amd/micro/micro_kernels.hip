@@ -1,5 +1,6 @@
 // Microbenchmarks behind the rooflines the benchmark reports (gfx950): the HBM read and copy streams, the
-// issue rate of independent fp32 FMAs and of v_exp_f32, and an empty kernel for the launch floor.  Built
+// issue rate of independent fp32 FMAs and of v_exp_f32, the shader clock under that load, and an empty
+// kernel for the launch floor.  Built
 // into libbimamba_micro.so, a library of its own: the scan library does not contain or call any of it.
 // Every entry point enqueues one kernel on `stream` and returns the HIP status; the caller times it.
 #include <hip/hip_runtime.h>
@@ -27,8 +28,15 @@ __global__ __launch_bounds__(256) void k_copy(const f32x4* __restrict__ src, f32
     __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
-// 8 independent FMA chains per lane, `iters` steps each: 8 * iters lane-FMAs per thread.
-__global__ __launch_bounds__(64) void k_fma(float* out, int iters, float a, float b) {
+// 8 independent FMA chains per lane, `iters` steps each: 8 * iters lane-FMAs per thread.  Every operand is a
+// VGPR (a and b are made lane-varying), the form of the scans' state arithmetic: a VALU instruction that reads
+// an SGPR issues more slowly when several follow each other, though not when mixed with VGPR-only ones.
+// Wavefront 0 of each workgroup records the shader clock (s_memtime) and the 100 MHz reference
+// (s_memrealtime) around its loop in clk[2 * block], [2 * block + 1] for the first 4096 workgroups.
+__global__ __launch_bounds__(64) void k_fma(float* out, int iters, float a0, float b0, unsigned long long* clk) {
+  const float a = a0 * (1.0f + 1e-30f * static_cast<float>(threadIdx.x));
+  const float b = b0 * (1.0f + 1e-30f * static_cast<float>(threadIdx.x));
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
   float v[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) v[k] = static_cast<float>(threadIdx.x + k);
@@ -40,6 +48,11 @@ __global__ __launch_bounds__(64) void k_fma(float* out, int iters, float a, floa
 #pragma unroll
   for (int k = 0; k < 8; ++k) s += v[k];
   if (s == -1.2345e37f) out[threadIdx.x] = s;
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0 && blockIdx.x < 4096) {
+    clk[2 * blockIdx.x] = c1 - c0;
+    clk[2 * blockIdx.x + 1] = r1 - r0;
+  }
 }
 
 // 8 independent v_exp_f32 chains per lane (each step 2^(v * a), which stays finite for |a| < 1).
@@ -75,9 +88,10 @@ int micro_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-// waves: wavefronts per SIMD (1024 SIMDs on a 256-CU part), one 64-lane wavefront per workgroup
-int micro_fma(float* out, int iters, int waves_per_simd, hipStream_t stream) {
-  hipLaunchKernelGGL(k_fma, dim3(1024 * waves_per_simd), dim3(64), 0, stream, out, iters, 0.999f, 0.001f);
+// waves: wavefronts per SIMD (1024 SIMDs on a 256-CU part), one 64-lane wavefront per workgroup; clk: 8192
+// 64-bit counters (see k_fma)
+int micro_fma(float* out, int iters, int waves_per_simd, unsigned long long* clk, hipStream_t stream) {
+  hipLaunchKernelGGL(k_fma, dim3(1024 * waves_per_simd), dim3(64), 0, stream, out, iters, 0.999f, 0.001f, clk);
   return static_cast<int>(hipGetLastError());
 }
 
