@@ -541,6 +541,70 @@ def ssd_block_latency(torch, bm, I, dev, w, A, Dv, bias):
     return res
 
 
+def bench_ssd_conv(args, torch, bm, I, dev, stream):
+    """Mamba-2 layers with untied directions and their short convolution, at the 1.3B layer's shape (120 heads
+    of 32, state 128, the 4096-channel xBC stream, L = 65536): both layers fused (bimamba_ssd_conv_untied with
+    the taps) against the two-pass pipeline (each layer's stream through bimamba_conv1d_bidir in its direction,
+    then the same entry point without the convolution)."""
+    L, H, P, N = 65536, 120, 32, 128
+    xs = H * P + 2 * N
+    sets = []
+    for s_ in (61, 62):
+        d = I.device_normals({"xbc": (1, L, xs), "dt": (1, L, H), "z": (1, L, H * P)}, seed=s_, io_dtype="bf16",
+                             device=dev, scales={"dt": 0.5})
+        A, Dv, bias = (torch.from_numpy(a).to(dev) for a in I.make_ssd_params(H, seed=s_ - 60))
+        cw = torch.from_numpy(I.normal(s_, "conv_w", (xs, 4), 0.5, "f32")).to(dev)
+        cb = torch.from_numpy(I.normal(s_, "conv_b", (xs,), 0.1, "f32")).to(dev)
+        d.update(A=A, D=Dv, dt_bias=bias, cw=cw, cb=cb)
+        sets.append(d)
+    f, r = sets
+    out_f, out_r = torch.empty(1, L, H * P, dtype=torch.bfloat16, device=dev), torch.empty(
+        1, L, H * P, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(bm.bimamba_ssd_fwd_workspace_bytes(1, L, H, P, N), dtype=torch.uint8, device=dev)
+    uf, ur = torch.empty_like(f["xbc"]), torch.empty_like(r["xbc"])
+
+    def fused():
+        bm.bimamba_ssd_conv_untied(f, r, out_f=out_f, out_r=out_r, workspace=ws, stream=stream)
+
+    def conv_pass():
+        bm.bimamba_conv1d_bidir(f["xbc"], f["cw"], f["cb"], None, None, out_f=uf, stream=stream)
+        bm.bimamba_conv1d_bidir(r["xbc"], None, None, r["cw"], r["cb"], out_r=ur, stream=stream)
+
+    def layers_unfused():
+        bm.bimamba_ssd_conv_untied(dict(f, xbc=uf, cw=None, cb=None), dict(r, xbc=ur, cw=None, cb=None),
+                                   out_f=out_f, out_r=out_r, workspace=ws, stream=stream)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_fused = timed(fused)
+    ms_conv = timed(conv_pass)
+    ms_layers = timed(layers_unfused)
+    # algorithmic bytes of the fused call: per layer the stream read once, dt, z read once, out written once
+    nbytes = 2 * L * (xs * 2 + H * 2 + 2 * H * P * 2)
+    log(f"ssd conv layers (untied, fused): {ms_fused:.4f} ms; two-pass: conv {ms_conv:.4f} + layers "
+        f"{ms_layers:.4f} ms")
+    return {"workload": "ssd_conv_untied_long_64k_bf16", "seq_len": L, "nheads": H, "headdim": P, "d_state": N,
+            "conv_channels": xs, "d_conv": 4, "layers": 2, "ms_per_call_fused": round(ms_fused, 4),
+            "ms_two_pass": round(ms_conv + ms_layers, 4), "ms_conv_pass": round(ms_conv, 4),
+            "ms_layers_unfused": round(ms_layers, 4),
+            "tokens_per_s_fused": round(L / (ms_fused * 1e-3), 1),
+            "hbm": {"algorithmic_bytes": nbytes, "achieved_gbs": round(nbytes / (ms_fused * 1e-3) / 1e9, 1),
+                    "frac_of_peak": round(nbytes / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "note": "two untied Mamba-2 layers (forward: causal conv, reverse: anti-causal conv, each its own "
+                    "stream, dt, z and parameters); two-pass = the convolution kernel on each stream, then the "
+                    "same layers reading the stored convolution output"}
+
+
 def bench_conv(args, torch, bm, I, dev, stream):
     """The short causal / anti-causal convolution at the 1.3B layer's conv width (4096 channels), L = 65536, bf16:
     both directions from one read of the input."""
@@ -780,6 +844,8 @@ def main():
         line["ssd"] = bench_ssd(args, torch, bm, I, dev, stream)
         torch.cuda.empty_cache()
         line["conv"] = bench_conv(args, torch, bm, I, dev, stream)
+        torch.cuda.empty_cache()
+        line["ssd_conv_layers"] = bench_ssd_conv(args, torch, bm, I, dev, stream)
     if not args.no_configs and w.name == "long_64k_bf16":
         torch.cuda.empty_cache()
         other = {"batched_8k_bf16": bench_batched(args, torch, bm, I, dev, stream)}

@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     bimamba_scan_fwd_workspace_bytes,
     bimamba_ssd_block,
     bimamba_ssd_block_workspace_bytes,
+    bimamba_ssd_conv_untied,
     bimamba_ssd_fwd,
     bimamba_ssd_fwd_stage,
     bimamba_ssd_fwd_workspace_bytes,

@@ -45,6 +45,7 @@ EXPORTED = (
     "bimamba_ssd_fwd_stage",
     "bimamba_ssd_block_workspace_bytes",
     "bimamba_ssd_block",
+    "bimamba_ssd_conv_untied",
     "bimamba_conv1d_bidir",
     "bimamba_conv1d_block",
 )
@@ -100,6 +101,8 @@ def load() -> ctypes.CDLL:
     lib.bimamba_ssd_block_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
     lib.bimamba_ssd_block.restype = ctypes.c_int
     lib.bimamba_ssd_block.argtypes = [vp] * 11 + [i64] * 5 + [ctypes.c_int, ctypes.c_uint32, vp, sz, vp]
+    lib.bimamba_ssd_conv_untied.restype = ctypes.c_int
+    lib.bimamba_ssd_conv_untied.argtypes = [vp] * 18 + [i64] * 6 + [ctypes.c_int, ctypes.c_uint32, vp, sz, vp]
     lib.bimamba_conv1d_bidir.restype = ctypes.c_int
     lib.bimamba_conv1d_bidir.argtypes = [vp] * 7 + [i64] * 4 + [ctypes.c_int, ctypes.c_uint32, vp]
     lib.bimamba_conv1d_block.restype = ctypes.c_int
@@ -388,6 +391,67 @@ def bimamba_ssd_block(x, dt, A, B, C, D=None, z=None, dt_bias=None, h_in=None, h
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_ssd_block")
     return out
+
+
+_LAYER_KEYS = ("xbc", "cw", "cb", "dt", "A", "D", "z", "dt_bias")
+
+
+def bimamba_ssd_conv_untied(fwd=None, rev=None, out_f=None, out_r=None, flags: int = 0, d_state: int = 128,
+                            workspace=None, stream=None):
+    """Mamba-2 layers with untied directions, each with its short convolution.  fwd and rev are dicts with keys
+    xbc ([batch, seqlen, H*P + 2*d_state] bf16), dt ([batch, seqlen, H]), A ([H]) and optionally cw
+    ([H*P + 2*d_state, 4] fp32; None: no convolution), cb, D, dt_bias, z; either may be None to skip that layer.
+    Returns (out_f, out_r), None for a skipped layer."""
+    torch = _torch()
+    sets = []
+    with _on(stream):
+        shape = None
+        for d, o in ((fwd, out_f), (rev, out_r)):
+            if d is None:
+                sets.append(None)
+                continue
+            t = {k: d.get(k) for k in _LAYER_KEYS}
+            xbc, A = t["xbc"], t["A"]
+            if xbc.dim() != 3 or A.dim() != 1:
+                raise ValueError("xbc must be [batch, seqlen, channels] and A [nheads]")
+            nb, L, xs = xbc.shape
+            nh = A.shape[0]
+            hp = xs - 2 * d_state
+            if nh == 0 or hp <= 0 or hp % nh:
+                raise ValueError("xbc's channels must be nheads * headdim + 2 * d_state")
+            if shape is not None and shape != (nb, L, xs, nh):
+                raise ValueError("the two layers must have the same shapes")
+            shape = (nb, L, xs, nh)
+            dev, io = xbc.device, xbc.dtype
+            _check(xbc, "xbc", (nb, L, xs), io, dev)
+            _check(t["dt"], "dt", (nb, L, nh), io, dev)
+            _check(t["z"], "z", (nb, L, hp), io, dev)
+            for k in ("A", "D", "dt_bias"):
+                _check(t[k], k, (nh,), torch.float32, dev)
+            _check(t["cw"], "cw", (xs, 4), torch.float32, dev)
+            _check(t["cb"], "cb", (xs,), torch.float32, dev)
+            if o is None:
+                o = torch.empty((nb, L, hp), dtype=io, device=dev)
+            _check(o, "out", (nb, L, hp), io, dev)
+            t["out"] = o
+            sets.append(t)
+        if shape is None:
+            raise ValueError("at least one of fwd, rev is required")
+        nb, L, xs, nh = shape
+        hp = xs - 2 * d_state
+        lib = load()
+        if workspace is None:
+            need = int(lib.bimamba_ssd_fwd_workspace_bytes(nb, L, nh, hp // nh, d_state))
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=next(t for t in sets if t)["xbc"].device)
+    ptrs = []
+    for t in sets:
+        ptrs += [None] * 9 if t is None else [_ptr(t[k]) for k in _LAYER_KEYS + ("out",)]
+    first = next(t for t in sets if t)
+    st = lib.bimamba_ssd_conv_untied(*ptrs, nb, L, nh, hp // nh, d_state, 4, _io_dtype(first["xbc"]), flags,
+                                     _ptr(workspace), _nbytes(workspace), _stream(stream, first["xbc"].device))
+    if st != BIMAMBA_OK:
+        raise BimambaError(st, "bimamba_ssd_conv_untied")
+    return tuple(None if t is None else t["out"] for t in sets)
 
 
 def _conv_common(u, w_f, b_f, w_r, b_r, out_f, out_r):

@@ -362,6 +362,72 @@ int bimamba_ssd_block(const void* x, const void* dt, const float* A, const void*
                   out, batch, block_len, nheads, headdim, d_state, io_dtype, flags, workspace, workspace_bytes, stream);
 }
 
+int bimamba_ssd_conv_untied(const void* xbc_f, const float* cw_f, const float* cb_f, const void* dt_f,
+                            const float* A_f, const float* D_f, const void* z_f, const float* dt_bias_f, void* out_f,
+                            const void* xbc_r, const float* cw_r, const float* cb_r, const void* dt_r,
+                            const float* A_r, const float* D_r, const void* z_r, const float* dt_bias_r, void* out_r,
+                            int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
+                            int64_t d_conv, int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  int s = ssd_check_shape(batch, seqlen, nheads, headdim, d_state, io_dtype);
+  if (s != BIMAMBA_OK) return s;
+  if (d_conv != 4) return d_conv <= 0 ? BIMAMBA_ERR_INVALID_ARGUMENT : BIMAMBA_ERR_UNSUPPORTED;
+  if (flags & ~static_cast<uint32_t>(BIMAMBA_FLAG_NO_GATE)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  if (!out_f && !out_r) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const bool gate = !(flags & BIMAMBA_FLAG_NO_GATE);
+  const int64_t xs = nheads * headdim + 2 * d_state;  // stream channels: x, then B, then C
+  const size_t act_x = static_cast<size_t>(batch) * seqlen * xs * 2;
+  const size_t act_o = static_cast<size_t>(batch) * seqlen * nheads * headdim * 2;
+  const size_t dtb = static_cast<size_t>(batch) * seqlen * nheads * 2;
+  const size_t par = static_cast<size_t>(nheads) * 4;
+  const size_t cwb = static_cast<size_t>(xs) * 4 * 4, cbb = static_cast<size_t>(xs) * 4;
+  struct Set {
+    const void* xbc; const float* cw; const float* cb; const void* dt; const float* A; const float* D;
+    const void* z; const float* bias; void* out;
+  };
+  const Set sets[2] = {{xbc_f, cw_f, cb_f, dt_f, A_f, D_f, z_f, dt_bias_f, out_f},
+                       {xbc_r, cw_r, cb_r, dt_r, A_r, D_r, z_r, dt_bias_r, out_r}};
+  for (const Set& t : sets) {
+    if (!t.out) continue;
+    if (!t.xbc || !t.dt || !t.A || (gate && !t.z)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+    if (!aligned(t.xbc, 16) || !aligned(t.out, 16) || (t.z && !aligned(t.z, 16)) || !aligned(t.dt, 2) ||
+        !aligned(t.A, 4) || (t.D && !aligned(t.D, 4)) || (t.bias && !aligned(t.bias, 4)) ||
+        (t.cw && !aligned(t.cw, 4)) || (t.cb && !aligned(t.cb, 4)))
+      return BIMAMBA_ERR_INVALID_ARGUMENT;
+  }
+  // an output may not overlap anything either pass reads or writes
+  auto clash = [&](Range o) {
+    for (const Set& t : sets) {
+      if (!t.out) continue;
+      if (overlap(o, range_of(t.xbc, act_x)) || overlap(o, range_of(t.dt, dtb)) || overlap(o, range_of(t.A, par)) ||
+          (t.D && overlap(o, range_of(t.D, par))) || (t.bias && overlap(o, range_of(t.bias, par))) ||
+          (t.z && overlap(o, range_of(t.z, act_o))) || (t.cw && overlap(o, range_of(t.cw, cwb))) ||
+          (t.cb && overlap(o, range_of(t.cb, cbb))))
+        return true;
+    }
+    return false;
+  };
+  if ((out_f && clash(range_of(out_f, act_o))) || (out_r && clash(range_of(out_r, act_o))) ||
+      (out_f && out_r && overlap(range_of(out_f, act_o), range_of(out_r, act_o))))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const bimamba::ssd::SsdPlan p = bimamba::ssd::make_ssd_plan(batch, seqlen, nheads);
+  if (workspace_bytes < p.total) return BIMAMBA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned(workspace, 256)) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const Range wr = range_of(workspace, p.total);
+  if ((out_f && overlap(wr, range_of(out_f, act_o))) || (out_r && overlap(wr, range_of(out_r, act_o))) ||
+      clash(wr))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  // the forward layer, then the reverse layer, in stream order, sharing the workspace
+  for (int d = 0; d < 2; ++d) {
+    const Set& t = sets[d];
+    if (!t.out) continue;
+    const bimamba::ssd::SsdArgs a{t.xbc, t.dt, t.A, nullptr, nullptr, t.D, t.z, t.bias, t.out, flags, nullptr, nullptr};
+    s = map_hip(bimamba::ssd::launch_ssd_one_dir(a, t.cw, t.cb, xs, p, workspace, d + 1, stream));
+    if (s != BIMAMBA_OK) return s;
+  }
+  return BIMAMBA_OK;
+}
+
 // ---- Short causal / anti-causal convolution ----
 
 static int conv_impl(const void* u, const float* w_f, const float* b_f, const float* w_r, const float* b_r,

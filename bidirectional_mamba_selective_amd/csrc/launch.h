@@ -86,6 +86,13 @@ struct SsdArgs {
 // through the carry stage.
 hipError_t launch_ssd(const SsdArgs& a, const SsdPlan& p, void* workspace, hipStream_t stream, int stage = -1);
 
+// One direction of a Mamba-2 layer (dir 1 forward, 2 reverse) on a projection stream of xs elements per token
+// holding x, B and C as channels [0, H*P), [H*P, H*P+N), [H*P+N, H*P+2N) (in.x is the stream; in.B, in.C,
+// in.h_in and in.h_out are not used), with the short convolution of taps cw [xs, 4] and bias cb applied to
+// the stream first when cw is not null: causal for dir 1, anti-causal for dir 2.
+hipError_t launch_ssd_one_dir(const SsdArgs& in, const float* cw, const float* cb, int64_t xs, const SsdPlan& p,
+                              void* workspace, int dir, hipStream_t stream);
+
 // One block-cache decoding step of at most kQ tokens in a single kernel (no workspace).
 hipError_t launch_ssd_block(const SsdArgs& a, int64_t batch, int64_t block_len, int64_t nheads, hipStream_t stream);
 

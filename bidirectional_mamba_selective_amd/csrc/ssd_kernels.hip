@@ -124,6 +124,12 @@ struct Args {
   int gate;
   const float* h_in;  // [batch, H, P, N] forward state entering the sequence, or null (zeros)
   float* h_out;       // [batch, H, P, N] forward state after the sequence, or null
+  // one-direction layers only: x (and B, C) are columns of one projection stream of xs elements per token
+  // (x = channels [0, H*P), B = [H*P, H*P+N), C = [H*P+N, H*P+2N)); cw [xs, 4] and cb [xs] are the short
+  // convolution's taps and bias (cw null: no convolution, cb null: no bias)
+  int64_t xs;
+  const float* cw;
+  const float* cb;
 };
 
 // (batch, chunk, head) of a workgroup.  Workgroups are dispatched round-robin
@@ -852,6 +858,428 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_block(Args a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// One-direction Mamba-2 layers (the paper's untied directions: each direction is its own layer), with the
+// layer's short convolution optionally applied as the inputs are loaded.
+//
+// x, B and C are columns of one projection stream of a.xs elements per token.  With a.cw set, the stream
+// first goes through the width-4 depthwise convolution of its channel and the SiLU: causal for the forward
+// layer, anti-causal for the reverse one (the forward layer applied to the flipped sequence); the result is
+// rounded to bf16 as if it had been stored between two passes.  A one-direction scan needs no partial
+// output between passes:
+//   k_ssd1_stage    per run: B, C (convolved) into the run tiles: C, B^T and C B^T;
+//   k_ssd1_summary  per (chunk, head), in the scan's direction over the runs: the state update only, giving
+//                   the chunk's end state from zero and the product of abar over the chunk;
+//   k_ssd_carry     the chunk maps across the sequence (the bidirectional pass's kernel, one direction);
+//   k_ssd1_walk     per (chunk, head), in the scan's direction: the intra-run product of the one-direction
+//                   mask, the readout of the running state, the skip term and the gate, the store, and the
+//                   state update.
+// DIR = 1: forward (runs left to right), 2: reverse (right to left).
+// ---------------------------------------------------------------------------
+
+// One stream channel of a run through the convolution: rows of the run's 64 tokens t0 .. t0 + 63 and the
+// 3-token halo (before them for the causal filter, after them for the anti-causal one), zero outside the
+// sequence; every load is issued from a clamped in-bounds row and the value selected afterwards.
+template <int DIR, int NT>
+__device__ __forceinline__ void conv_rows(const uint16_t* col, int64_t xs, int64_t L, int64_t tfirst,
+                                          uint16_t (&r)[NT + 3]) {
+#pragma unroll
+  for (int i = 0; i < NT + 3; ++i) {
+    const int64_t t = tfirst + i;
+    const int64_t tc = t < 0 ? 0 : (t >= L ? L - 1 : t);
+    const uint16_t v = col[tc * xs];
+    r[i] = (t >= 0 && t < L) ? v : static_cast<uint16_t>(0);
+  }
+}
+
+// NT outputs from the rows of conv_rows (r[0] is row tfirst): causal out[t] = silu(b + sum_k w[k] u[t-3+k])
+// with tfirst = t0 - 3, anti-causal out[t] = silu(b + sum_k w[k] u[t+3-k]) with tfirst = t0; rounded to
+// bf16; tokens at or past L give 0 (padding of the last run).
+template <int DIR, int NT>
+__device__ __forceinline__ void conv_outputs(const uint16_t (&r)[NT + 3], const float (&w)[4], float bias,
+                                             int64_t t0, int64_t L, uint16_t (&o)[NT]) {
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    float acc = bias;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = fmaf(w[k], bf(DIR == 1 ? r[i + k] : r[i + 3 - k]), acc);
+    o[i] = (t0 + i < L) ? to_bf(silu_f32(acc)) : static_cast<uint16_t>(0);
+  }
+}
+
+// The channel's conv taps and bias (stream channel ch).
+__device__ __forceinline__ void conv_taps(const Args& a, int64_t ch, float (&w)[4], float& bias) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = a.cw[ch * 4 + k];
+  bias = a.cb ? a.cb[ch] : 0.0f;
+}
+
+// k_ssd1_stage: one workgroup per (run, batch element).  With the convolution, thread n < 128 convolves B
+// channel n and thread 128 + n C channel n over the run's 64 tokens into LDS; without it the rows are copied
+// (zero past the sequence end).  Then, as in k_ssd_stage: the C tile, B^T and C B^T.
+template <int DIR, bool CONV>
+__global__ __launch_bounds__(kThreads) void k_ssd1_stage(Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sBs[Q * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sCs[Q * N];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q4 = l >> 4, l16 = l & 15;
+  const int64_t sub = blockIdx.x, b = blockIdx.y;
+  const int64_t t0 = sub * Q;
+  const int64_t HP = a.H * P;
+  const int64_t tile = (b * a.nsub + sub) * static_cast<int64_t>(Q * N);
+  const uint16_t* rows = a.x + b * a.L * a.xs;  // this batch element's stream
+  if (CONV) {
+    const int n = tid & (N - 1);
+    const bool isC = tid >= N;
+    const int64_t ch = HP + (isC ? N : 0) + n;
+    float wv[4], bias;
+    conv_taps(a, ch, wv, bias);
+    uint16_t* dst = isC ? sCs : sBs;
+    // 64 tokens in 4 groups of 16, so that the rows of one group stay in registers
+#pragma unroll 1
+    for (int g = 0; g < Q / 16; ++g) {
+      uint16_t r[16 + 3], o[16];
+      conv_rows<DIR, 16>(rows + ch, a.xs, a.L, t0 + 16 * g + (DIR == 1 ? -3 : 0), r);
+      conv_outputs<DIR, 16>(r, wv, bias, t0 + 16 * g, a.L, o);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[sw256(16 * g + i, n >> 3) + (n & 7)] = o[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = tid + kThreads * i;
+      const int j = ci >> 4, cc = ci & 15;
+      uint4 vb = make_uint4(0, 0, 0, 0), vc = make_uint4(0, 0, 0, 0);
+      if (t0 + j < a.L) {
+        vb = *reinterpret_cast<const uint4*>(rows + (t0 + j) * a.xs + HP + 8 * cc);
+        vc = *reinterpret_cast<const uint4*>(rows + (t0 + j) * a.xs + HP + N + 8 * cc);
+      }
+      *reinterpret_cast<uint4*>(sBs + sw256(j, cc)) = vb;
+      *reinterpret_cast<uint4*>(sCs + sw256(j, cc)) = vc;
+    }
+  }
+  __syncthreads();
+  // the C tile (rows of N states per token)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ci = tid + kThreads * i;
+    const int j = ci >> 4, cc = ci & 15;
+    *reinterpret_cast<uint4*>(a.cp + tile + j * N + 8 * cc) = *reinterpret_cast<const uint4*>(sCs + sw256(j, cc));
+  }
+  // B^T rows n, 8 tokens per 16-byte chunk
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ci = tid + kThreads * i;
+    const int n = ci >> 3, jc = ci & 7;
+    uint32_t w2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j0 = 8 * jc + 2 * e;
+      w2[e] = static_cast<uint32_t>(sBs[sw256(j0, n >> 3) + (n & 7)]) |
+              (static_cast<uint32_t>(sBs[sw256(j0 + 1, n >> 3) + (n & 7)]) << 16);
+    }
+    *reinterpret_cast<uint4*>(a.bt + tile + n * Q + 8 * jc) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+  }
+  // C B^T: wavefront w forms the 4 tiles of row block ib = w
+  bf16x8 cf[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) cf[k] = lds8(sCs, sw256(16 * w + l16, 4 * k + q4));
+  float* gout = a.g + (b * a.nsub + sub) * static_cast<int64_t>(Q * Q);
+#pragma unroll
+  for (int tj = 0; tj < 4; ++tj) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = mfma(lds8(sBs, sw256(16 * tj + l16, 4 * k + q4)), cf[k], acc);
+    *reinterpret_cast<f32x4*>(gout + ((w * 4 + tj) * 64 + l) * 4) = acc;
+  }
+}
+
+// A run's x for one head, the way the walks consume it.  With the convolution: thread tid owns channel
+// c = tid % 32 of the head and tokens 8g .. 8g + 7 of the run (g = tid / 32): it loads those 8 rows and the
+// 3-token halo of its channel (raw, 11 values), convolves them at commit time and writes one 16-byte chunk
+// of the channel-major LDS tiles.  Without it: 16 bytes (token tid / 4, channels 8(tid % 4) .. + 7) as in
+// the bidirectional sweeps.
+template <int DIR, bool CONV>
+struct XRun;
+
+template <int DIR>
+struct XRun<DIR, true> {
+  uint16_t r[8 + 3];
+  __device__ __forceinline__ void load(const Args& a, int64_t b, int64_t t0, int64_t h, int tid) {
+    const int c = tid & 31, g = tid >> 5;
+    conv_rows<DIR, 8>(a.x + b * a.L * a.xs + h * P + c, a.xs, a.L, t0 + 8 * g + (DIR == 1 ? -3 : 0), r);
+  }
+  // x into sXT (when given) and x weighted per token (weights wtok[j] * wscale) into sXW (when given)
+  __device__ __forceinline__ void commit(uint16_t* sXT, uint16_t* sXW, const float* wtok, float wscale,
+                                         const float (&w)[4], float bias, int64_t t0, int64_t L, int tid) const {
+    const int c = tid & 31, g = tid >> 5;
+    uint16_t o[8];
+    conv_outputs<DIR, 8>(r, w, bias, t0 + 8 * g, L, o);
+    if (sXT) {
+      const uint4 v = make_uint4(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16),
+                                 o[4] | (static_cast<uint32_t>(o[5]) << 16), o[6] | (static_cast<uint32_t>(o[7]) << 16));
+      *reinterpret_cast<uint4*>(sXT + sw128(c, g)) = v;
+    }
+    if (sXW) {
+      uint16_t q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = to_bf(bf(o[i]) * (wtok[8 * g + i] * wscale));
+      const uint4 v = make_uint4(q[0] | (static_cast<uint32_t>(q[1]) << 16), q[2] | (static_cast<uint32_t>(q[3]) << 16),
+                                 q[4] | (static_cast<uint32_t>(q[5]) << 16), q[6] | (static_cast<uint32_t>(q[7]) << 16));
+      *reinterpret_cast<uint4*>(sXW + sw128(c, g)) = v;
+    }
+  }
+};
+
+template <int DIR>
+struct XRun<DIR, false> {
+  uint4 px;
+  __device__ __forceinline__ void load(const Args& a, int64_t b, int64_t t0, int64_t h, int tid) {
+    const int j = tid >> 2, pc = tid & 3;
+    px = (t0 + j >= a.L) ? make_uint4(0, 0, 0, 0)
+                         : *reinterpret_cast<const uint4*>(a.x + (b * a.L + t0 + j) * a.xs + h * P + 8 * pc);
+  }
+  __device__ __forceinline__ void commit(uint16_t* sXT, uint16_t* sXW, const float* wtok, float wscale,
+                                         const float (&)[4], float, int64_t, int64_t, int tid) const {
+    if (sXT) put_xt(sXT, px, tid, nullptr, 1.0f);
+    if (sXW) put_xt(sXW, px, tid, wtok, wscale);
+  }
+};
+
+// k_ssd1_summary: one workgroup per (batch, chunk, head), over the chunk's runs in the scan's direction:
+// state <- e^{S_run} state + B^T (weighted x), from zero.  The forward layer's end state (slot 0 of the
+// chunk's state pair) weights token j by e^{S_run - s_j} delta_j, the reverse layer's (slot 1) by e^{e_j}
+// delta_j.  Also the product of abar over the chunk.
+template <int DIR, bool CONV>
+__global__ __launch_bounds__(kThreads, 2) void k_ssd1_summary(Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sBT[N * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sXW[P * Q];
+  __shared__ __attribute__((aligned(16))) float sTok[2][kTokRows * 64];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  int64_t b, c, h;
+  decode_item(a, b, c, h);
+  const float Ah = a.A[h];
+  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const int64_t sub0 = c * a.rpc;
+  const int64_t nrun = a.nsub - sub0 < a.rpc ? a.nsub - sub0 : a.rpc;
+  const int64_t item = (b * a.nchunk + c) * a.H + h;
+  float cw[4] = {0.f, 0.f, 0.f, 0.f}, cbias = 0.0f;
+  if (CONV) conv_taps(a, h * P + (tid & 31), cw, cbias);
+  State S;
+  state_zero(S);
+  float prod = 1.0f;  // product of abar over the runs done
+  u32x4 pbt[4];
+  XRun<DIR, CONV> xr;
+  uint16_t pdt = 0, pdt2 = 0;  // step sizes two steps ahead
+  auto run_of = [&](int64_t st) { return DIR == 1 ? st : nrun - 1 - st; };
+  auto issue = [&](int64_t st) {
+    const int64_t sub = sub0 + run_of(st);
+    if (w == 0 && st + 1 < nrun) pdt2 = load_dt(a, b, (sub0 + run_of(st + 1)) * Q, h, l);
+    const u32x4* b4 = reinterpret_cast<const u32x4*>(a.bt + (b * a.nsub + sub) * static_cast<int64_t>(Q * N));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pbt[i] = b4[tid + kThreads * i];
+    xr.load(a, b, sub * Q, h, tid);
+  };
+  if (w == 0) pdt = load_dt(a, b, (sub0 + run_of(0)) * Q, h, l);
+  issue(0);
+  if (w == 0) token_prep(sTok[0], pdt, (sub0 + run_of(0)) * Q + l < a.L, Ah, bias, l);
+  pdt = pdt2;
+  for (int64_t st = 0; st < nrun; ++st) {
+    const int64_t t0 = (sub0 + run_of(st)) * Q;
+    const float* tok = sTok[st & 1];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = tid + kThreads * i;
+      *reinterpret_cast<u32x4*>(sBT + sw128(ci >> 3, ci & 7)) = pbt[i];
+    }
+    xr.commit(nullptr, sXW, tok + (DIR == 1 ? kWf : kWr) * 64, 1.0f, cw, cbias, t0, a.L, tid);
+    __syncthreads();
+    if (st + 1 < nrun) issue(st + 1);
+    const float eS = ex(tok[kS * 64 + 63]);
+    state_update(S, eS, sBT, sXW, w, l);
+    prod *= eS;
+    if (w == 0 && st + 1 < nrun)
+      token_prep(sTok[(st + 1) & 1], pdt, (sub0 + run_of(st + 1)) * Q + l < a.L, Ah, bias, l);
+    pdt = pdt2;
+  }
+  state_store(S, a.S + (item * 2 + (DIR == 1 ? 0 : 1)) * kSF, w, l);
+  if (tid == 0) a.Pc[item] = prod;
+}
+
+// k_ssd1_walk: one workgroup per (batch, chunk, head), over the chunk's runs in the scan's direction, from
+// the state entering the chunk (the carry pass's output).  Wavefront w owns output rows 16w .. 16w + 15 and
+// state row blocks 2w, 2w + 1, as in the bidirectional sweeps.
+template <int DIR, bool CONV>
+__global__ __launch_bounds__(kThreads, 2) void k_ssd1_walk(Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sBT[N * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sXT[P * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sXW[P * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sHs[P * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sZ[4 * 16 * P];
+  __shared__ __attribute__((aligned(16))) uint16_t sY[4 * 16 * P];
+  __shared__ __attribute__((aligned(16))) float sTok[2][kTokRows * 64];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q4 = l >> 4, l16 = l & 15;
+  int64_t b, c, h;
+  decode_item(a, b, c, h);
+  const float Ah = a.A[h];
+  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const float Dfac = a.D ? a.D[h] : 0.0f;
+  const int64_t sub0 = c * a.rpc;
+  const int64_t nrun = a.nsub - sub0 < a.rpc ? a.nsub - sub0 : a.rpc;
+  const int64_t item = (b * a.nchunk + c) * a.H + h;
+  const int64_t HP = a.H * P;
+  uint16_t* zslot = sZ + w * 16 * P;
+  uint16_t* yslot = sY + w * 16 * P;
+  float cw[4] = {0.f, 0.f, 0.f, 0.f}, cbias = 0.0f;
+  if (CONV) conv_taps(a, h * P + (tid & 31), cw, cbias);
+  State H;
+  state_load(H, a.S + (item * 2 + (DIR == 1 ? 0 : 1)) * kSF, w, l);
+
+  u32x4 pc[4], pbt[4];
+  f32x4 pg[4];
+  uint4 pz;
+  XRun<DIR, CONV> xr;
+  uint16_t pdt = 0, pdt2 = 0;
+  auto run_of = [&](int64_t st) { return DIR == 1 ? st : nrun - 1 - st; };
+  auto issue = [&](int64_t st) {
+    const int64_t sub = sub0 + run_of(st), t0 = sub * Q;
+    if (w == 0 && st + 1 < nrun) pdt2 = load_dt(a, b, (sub0 + run_of(st + 1)) * Q, h, l);
+    const int64_t tile = (b * a.nsub + sub) * static_cast<int64_t>(Q * N);
+    const u32x4* b4 = reinterpret_cast<const u32x4*>(a.bt + tile);
+    load_cfrag(pc, a.cp + tile, w, l);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pbt[i] = b4[tid + kThreads * i];
+    const float* gg = a.g + (b * a.nsub + sub) * static_cast<int64_t>(Q * Q);
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) pg[tj] = *reinterpret_cast<const f32x4*>(gg + ((w * 4 + tj) * 64 + l) * 4);
+    xr.load(a, b, t0, h, tid);
+    if (a.gate) pz = load_act(a.z, a, b, t0, h, 64 * w + l);
+  };
+  if (w == 0) pdt = load_dt(a, b, (sub0 + run_of(0)) * Q, h, l);
+  issue(0);
+  if (w == 0) token_prep(sTok[0], pdt, (sub0 + run_of(0)) * Q + l < a.L, Ah, bias, l);
+  pdt = pdt2;
+  // a run's output is stored at the start of the next step's computation, before that step's loads
+  uint4 pend = make_uint4(0, 0, 0, 0);
+  int64_t t_pend = 0;
+
+  for (int64_t st = 0; st < nrun; ++st) {
+    const int64_t t0 = (sub0 + run_of(st)) * Q;
+    const float* tok = sTok[st & 1];
+    bf16x8 cf[4];
+    f32x4 gcur[4];
+    __syncthreads();
+    // ---- commit the prefetched registers ----
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = tid + kThreads * i;
+      *reinterpret_cast<u32x4*>(sBT + sw128(ci >> 3, ci & 7)) = pbt[i];
+      cf[i] = __builtin_bit_cast(bf16x8, pc[i]);
+    }
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) gcur[tj] = pg[tj];
+    xr.commit(sXT, sXW, tok + (DIR == 1 ? kWf : kWr) * 64, 1.0f, cw, cbias, t0, a.L, tid);
+    if (a.gate) *reinterpret_cast<uint4*>(zslot + (l >> 2) * P + 8 * (l & 3)) = pz;
+    state_to_lds(H, sHs, w, l);
+    __syncthreads();
+    if (st > 0) store_run_row(a.out, b, a.L, HP, t_pend, h, 16 * w + (l >> 2), l & 3, pend);
+    if (st + 1 < nrun) issue(st + 1);
+
+    // ---- compute ----
+    // W = mask o (C B^T) o delta_j for rows i = 16w + l16, k-slots permuted as in the bidirectional sweeps;
+    // the mask keeps one direction: forward e^{s_i - s_j} for j < i, reverse e^{e_j - e_i} for j > i, 1 on
+    // the diagonal
+    const int i = 16 * w + l16;
+    const float si = tok[kS * 64 + i], ei = tok[kE * 64 + i];
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      const int j0 = 16 * tj + 4 * q4;
+      const f32x4 sj = *reinterpret_cast<const f32x4*>(tok + kS * 64 + j0);
+      const f32x4 ej = *reinterpret_cast<const f32x4*>(tok + kE * 64 + j0);
+      const f32x4 dj = *reinterpret_cast<const f32x4*>(tok + kDl * 64 + j0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = j0 + r;
+        float m;
+        if (j == i) m = 1.0f;
+        else if (DIR == 1) m = j < i ? ex(si - sj[r]) : 0.0f;
+        else m = j > i ? ex(ej[r] - ei) : 0.0f;
+        gcur[tj][r] *= m * dj[r];
+      }
+    }
+    f32x4 y[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      bf16x8 wa;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        wa[r] = static_cast<__bf16>(gcur[2 * k2][r]);
+        wa[4 + r] = static_cast<__bf16>(gcur[2 * k2 + 1][r]);
+      }
+      const int jlo = 32 * k2 + 4 * q4;
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) {
+        const int p = 16 * tp + l16;
+        const uint2 lo = *reinterpret_cast<const uint2*>(sXT + sw128(p, jlo >> 3) + (jlo & 7));
+        const uint2 hi = *reinterpret_cast<const uint2*>(sXT + sw128(p, (jlo + 16) >> 3) + (jlo & 7));
+        y[tp] = mfma(wa, __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), y[tp]);
+      }
+    }
+    {
+      // the running state's readout: forward e^{s_i} C_i . H, reverse e^{S - e_i} C_i . G
+      f32x4 ys[2];
+      readout(ys, cf, sHs, l);
+      const f32x4 rs = *reinterpret_cast<const f32x4*>(tok + (DIR == 1 ? kRf : kRr) * 64 + 16 * w + 4 * q4);
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[tp][r] += rs[r] * ys[tp][r];
+    }
+    // skip term and gate
+    float o[2][4];
+    const int i0 = 16 * w + 4 * q4;
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+      const int p = 16 * tp + l16;
+      const uint2 xv = *reinterpret_cast<const uint2*>(sXT + sw128(p, i0 >> 3) + (i0 & 7));
+      const float xs[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xffff0000u),
+                           __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xffff0000u)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        o[tp][r] = y[tp][r] + Dfac * xs[r];
+        if (a.gate) o[tp][r] *= silu_f32(bf(zslot[(4 * q4 + r) * P + p]));
+      }
+    }
+    tile_rows_to_lds(yslot, o, l);
+    pend = *reinterpret_cast<const uint4*>(yslot + (l >> 2) * P + 8 * (l & 3));
+    t_pend = t0;
+    state_update(H, ex(tok[kS * 64 + 63]), sBT, sXW, w, l);
+    if (w == 0 && st + 1 < nrun)
+      token_prep(sTok[(st + 1) & 1], pdt, (sub0 + run_of(st + 1)) * Q + l < a.L, Ah, bias, l);
+    pdt = pdt2;
+  }
+  store_run_row(a.out, b, a.L, HP, t_pend, h, 16 * w + (l >> 2), l & 3, pend);
+}
+
+template <int DIR, bool CONV>
+hipError_t launch_one_dir(const Args& a, int64_t batch, hipStream_t stream) {
+  hipLaunchKernelGGL((k_ssd1_stage<DIR, CONV>), dim3(static_cast<unsigned>(a.nsub), static_cast<unsigned>(batch)),
+                     dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned groups = static_cast<unsigned>(batch * a.nchunk * a.H);
+  hipLaunchKernelGGL((k_ssd1_summary<DIR, CONV>), dim3(groups), dim3(kThreads), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = batch * a.H * kSF;
+  hipLaunchKernelGGL(k_ssd_carry, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream, a.S,
+                     a.Pc, batch, a.H, a.nchunk, DIR, nullptr, nullptr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_ssd1_walk<DIR, CONV>), dim3(groups), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int DIRS>
 hipError_t launch_dirs(const Args& a, int64_t batch, hipStream_t stream, int stage) {
   const unsigned groups = static_cast<unsigned>(batch * a.nchunk * a.H);
@@ -902,6 +1330,36 @@ hipError_t launch_ssd_block(const SsdArgs& in, int64_t batch, int64_t block_len,
     hipLaunchKernelGGL(k_ssd_block<3>, grid, dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_ssd_one_dir(const SsdArgs& in, const float* cw, const float* cb, int64_t xs, const SsdPlan& p,
+                              void* workspace, int dir, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  Args a{};
+  a.x = static_cast<const uint16_t*>(in.x);
+  a.dt = static_cast<const uint16_t*>(in.dt);
+  a.A = in.A;
+  a.D = in.D;
+  a.z = static_cast<const uint16_t*>(in.z);
+  a.dt_bias = in.dt_bias;
+  a.out = static_cast<uint16_t*>(in.out);
+  a.L = p.seqlen;
+  a.H = p.nheads;
+  a.nsub = p.nsub;
+  a.rpc = p.rpc;
+  a.nchunk = p.nchunk;
+  a.g = reinterpret_cast<float*>(ws + p.off_g);
+  a.cp = reinterpret_cast<uint16_t*>(ws + p.off_cp);
+  a.bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
+  a.S = reinterpret_cast<float*>(ws + p.off_s);
+  a.Pc = reinterpret_cast<float*>(ws + p.off_p);
+  a.tau = reinterpret_cast<float*>(ws + p.off_tau);
+  a.gate = (in.flags & kNoGate) ? 0 : 1;
+  a.xs = xs;
+  a.cw = cw;
+  a.cb = cb;
+  if (dir == 1) return cw ? launch_one_dir<1, true>(a, p.batch, stream) : launch_one_dir<1, false>(a, p.batch, stream);
+  return cw ? launch_one_dir<2, true>(a, p.batch, stream) : launch_one_dir<2, false>(a, p.batch, stream);
 }
 
 hipError_t launch_ssd(const SsdArgs& in, const SsdPlan& p, void* workspace, hipStream_t stream, int stage) {

@@ -31,7 +31,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-_TENSOR_IDS = {"x": 1, "dt": 2, "z": 3, "B": 4, "C": 5, "dt_bias": 11, "A_jitter": 12, "A_head": 13}
+_TENSOR_IDS = {"x": 1, "dt": 2, "z": 3, "B": 4, "C": 5, "xbc": 6, "dt_bias": 11, "A_jitter": 12, "A_head": 13,
+               "conv_w": 14, "conv_b": 15}
 
 
 @dataclass(frozen=True)
@@ -182,6 +183,24 @@ def make_ssd_inputs(w: SSDWorkload, seed: int = 1):
     act = make_ssd_activations(w.batch, w.seqlen, w.nheads, w.headdim, w.d_state, w.io_dtype, seed=seed)
     act.update(A=A, D=D, dt_bias=dt_bias)
     return act
+
+
+def make_ssd_layer_inputs(batch: int, seqlen: int, nheads: int, headdim: int = 32, d_state: int = 128,
+                          seed: int = 1, param_seed: int = 0):
+    """One Mamba-2 layer's inputs with its short convolution (the xBC stream of the projection):
+    xbc [B, L, H*P + 2N] ~ N(0, 1), dt [B, L, H] ~ 0.5 N(0, 1), z [B, L, H*P] ~ N(0, 1), all rounded to bf16;
+    conv taps [H*P + 2N, 4] ~ 0.5 N(0, 1) and bias [H*P + 2N] ~ 0.1 N(0, 1) (fp32, as in the convolution's
+    tests), and the SSD parameters A, D, dt_bias per head (make_ssd_params)."""
+    xs = nheads * headdim + 2 * d_state
+    A, D, dt_bias = make_ssd_params(nheads, seed=param_seed)
+    return {
+        "xbc": normal(seed, "xbc", (batch, seqlen, xs), 1.0, "bf16"),
+        "dt": normal(seed, "dt", (batch, seqlen, nheads), 0.5, "bf16"),
+        "z": normal(seed, "z", (batch, seqlen, nheads * headdim), 1.0, "bf16"),
+        "cw": normal(param_seed, "conv_w", (xs, 4), 0.5, "f32"),
+        "cb": normal(param_seed, "conv_b", (xs,), 0.1, "f32"),
+        "A": A, "D": D, "dt_bias": dt_bias,
+    }
 
 
 def device_normals(shapes: dict, seed: int, io_dtype: str, device="cuda", scales: dict | None = None):

@@ -245,6 +245,41 @@ int bimamba_ssd_block(const void* x, const void* dt, const float* A, const void*
                       int64_t batch, int64_t block_len, int64_t nheads, int64_t headdim, int64_t d_state,
                       int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Mamba-2 layers with untied directions, each with its short convolution: the
+ * bidirectional mixer as the paper runs it (Section 3.2: two independent
+ * layers, the reverse one on the flipped sequence; Section 4.1 Table 8: the
+ * directions' weights are not tied, convolution width 4; Appendix C Table 12:
+ * the projection's xBC stream of conv_ch = d_inner + 2 d_state channels goes
+ * through Conv1d before the scan, and the gate z and the step dt come from the
+ * same projection).  For each direction's set (xbc, cw, cb, dt, A, D, z,
+ * dt_bias, out), with P = headdim, N = d_state and channel c of the stream:
+ *   u[t,c]  = silu(cb[c] + sum_k cw[c,k] * xbc[t-3+k, c])   forward set (causal)
+ *   u[t,c]  = silu(cb[c] + sum_k cw[c,k] * xbc[t+3-k, c])   reverse set (anti-causal)
+ *   (xbc = 0 outside the sequence; u is rounded to nearest even bf16, as when
+ *   the convolution's output is stored before the scan)
+ *   x = u[:, 0 : H*P], B = u[:, H*P : H*P+N], C = u[:, H*P+N : H*P+2N]
+ *   out_f = (y_fwd(x, B, C) + D * x) * silu(z)   (bimamba_ssd_fwd's forward scan)
+ *   out_r = (y_rev(x, B, C) + D * x) * silu(z)   (its reverse scan)
+ * with each set's own dt [batch, seqlen, nheads], A, D, dt_bias [nheads] and
+ * z [batch, seqlen, H*P].  cw == NULL skips the convolution (x, B, C are then
+ * the stream itself); cb == NULL means no bias.  out_f or out_r may be NULL to
+ * skip that layer (not both); its set's pointers are then not read.
+ * Layouts: xbc [batch, seqlen, H*P + 2N] bf16, cw [H*P + 2N, 4] and cb
+ * [H*P + 2N] fp32, out [batch, seqlen, H*P] bf16.  Shapes, dtype, heads and
+ * D / dt_bias NULL are as for bimamba_ssd_fwd; d_conv must be 4; flags may only
+ * be BIMAMBA_FLAG_NO_GATE (then z may be NULL).  xbc, z and out 16-byte
+ * aligned, dt 2-byte, the fp32 parameters 4-byte.  The workspace
+ * (bimamba_ssd_fwd_workspace_bytes(batch, seqlen, nheads, headdim, d_state)
+ * bytes, 256-byte aligned) is used by the two layers in turn.  Neither output
+ * may overlap any tensor of either set, the other output or the workspace. */
+int bimamba_ssd_conv_untied(const void* xbc_f, const float* cw_f, const float* cb_f, const void* dt_f,
+                            const float* A_f, const float* D_f, const void* z_f, const float* dt_bias_f, void* out_f,
+                            const void* xbc_r, const float* cw_r, const float* cb_r, const void* dt_r,
+                            const float* A_r, const float* D_r, const void* z_r, const float* dt_bias_r, void* out_r,
+                            int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
+                            int64_t d_conv, int io_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* ---- Short causal / anti-causal convolution ------------------------------
  * Each direction of the mixer runs a depthwise Conv1d of width d_conv = 4
  * ahead of its scan (Appendix C Table 12: conv_ch = 4096 channels at the 1.3B

@@ -429,3 +429,45 @@ def test_noalloc_validates_and_rejects_problems_past_its_scratch():
                                        _lib.BIMAMBA_BF16, 0, None)
     assert st == _lib.BIMAMBA_ERR_SCRATCH_TOO_SMALL
     assert "scratch" in _lib.status_string(st)
+
+
+def call_ssd_conv(**kw):
+    lib = _lib.load()
+    # 2 heads of 32 and 128 states: stream rows of 320 channels; tensors 64 MiB apart
+    a = dict(xf=fake(0), cwf=fake(1), cbf=fake(2), dtf=fake(3), Af=fake(4), Df=fake(5), zf=fake(6), bf=fake(7),
+             of=fake(8), xr=fake(12), cwr=fake(13), cbr=fake(14), dtr=fake(15), Ar=fake(16), Dr=fake(17),
+             zr=fake(18), br=fake(19), orr=fake(20), batch=1, L=64, nh=2, hd=32, ns=128, dconv=4,
+             io=_lib.BIMAMBA_BF16, flags=0, ws=fake(9), wsb=0)
+    a.update(kw)
+    return lib.bimamba_ssd_conv_untied(a["xf"], a["cwf"], a["cbf"], a["dtf"], a["Af"], a["Df"], a["zf"], a["bf"],
+                                       a["of"], a["xr"], a["cwr"], a["cbr"], a["dtr"], a["Ar"], a["Dr"], a["zr"],
+                                       a["br"], a["orr"], a["batch"], a["L"], a["nh"], a["hd"], a["ns"], a["dconv"],
+                                       a["io"], a["flags"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(of=None, orr=None), INV),  # neither layer
+    (dict(dconv=3), UNS),
+    (dict(dconv=0), INV),
+    (dict(hd=16), UNS),
+    (dict(ns=64), UNS),
+    (dict(io=_lib.BIMAMBA_F32), UNS),
+    (dict(flags=_lib.FLAG_FWD_ONLY), INV),  # the directions are chosen by the outputs given
+    (dict(dtf=None), INV),
+    (dict(Ar=None), INV),
+    (dict(zf=None), INV),  # gate without z
+    (dict(xf=fake(0, 8)), INV),  # misaligned stream
+    (dict(of=fake(12)), INV),  # out_f over the reverse layer's stream
+    (dict(orr=fake(8)), INV),  # the outputs overlap
+    (dict(of=fake(1)), INV),  # out_f over the forward layer's conv taps
+    (dict(wsb=0), WS),
+])
+def test_ssd_conv_untied_rejects(kw, want):
+    assert call_ssd_conv(**kw) == want
+
+
+def test_ssd_conv_untied_checks_run_in_order():
+    # one layer alone, no convolution, no gate, no D or bias: the call gets as far as the workspace check
+    assert call_ssd_conv(orr=None, xr=None, dtr=None, Ar=None, cwf=None, cbf=None, zf=None, Df=None, bf=None,
+                         flags=_lib.FLAG_NO_GATE) == WS
+    assert call_ssd_conv(of=None, xf=None, dtf=None, Af=None) == WS

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from bidirectional_mamba_selective_amd import inputs as I
-from tests.gpu_util import check, oracle_fwd, run_fwd, say, to_host64, upload
+from tests.gpu_util import Bar, check, oracle_fwd, run_fwd, say, to_host64, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -181,6 +181,15 @@ def test_delta_limits(shift, a_jitter):
     check_variants(inp, "f32", variants=VARIANTS[:2], tag=f"delta_shift{shift:+.0f}")
 
 
+# Windows of a lone impulse's response: the target's 1e-4 normwise, per-token rows and elements at 2e-4
+# relative plus 6e-5 of the window's rms.  A window away from the source holds only carried-in, decayed
+# terms: the geometric-A path forms abar_n as the (n+1)-th power of w = e^{delta A[d,0]}, so the rounding of
+# w (up to 2^-25 relative) enters abar_n (n+1)-fold and accumulates along the decay chain, about
+# (n+1) 2^-25 sqrt(tokens) of the carried state (measured 2e-5 of a window's rms 700 to 1700 tokens past
+# the source, against 3e-6 on the general path, whose abar takes one exponential each).
+IMPULSE_BAR = Bar(1e-4, 2e-4, 2e-4, 6e-5)
+
+
 def check_windows(got, want, width, tag):
     """check() on every window of `width` tokens whose reference rms lies well inside fp32's normal range
     (1e-20): each window against its own scale.  Returns how many windows were checked."""
@@ -188,7 +197,7 @@ def check_windows(got, want, width, tag):
     for t0 in range(0, want.shape[1], width):
         sl = slice(t0, t0 + width)
         if np.sqrt(np.mean(want[:, sl] ** 2)) > 1e-20:
-            check(got[:, sl], want[:, sl], "f32", f"{tag} tokens {t0}..{min(t0 + width, want.shape[1]) - 1}")
+            check(got[:, sl], want[:, sl], IMPULSE_BAR, f"{tag} tokens {t0}..{min(t0 + width, want.shape[1]) - 1}")
             n += 1
     return n
 
