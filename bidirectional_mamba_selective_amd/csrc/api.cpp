@@ -376,6 +376,9 @@ int bimamba_ssd_conv_untied(const void* xbc_f, const float* cw_f, const float* c
   if (!out_f && !out_r) return BIMAMBA_ERR_INVALID_ARGUMENT;
   const bool gate = !(flags & BIMAMBA_FLAG_NO_GATE);
   const int64_t xs = nheads * headdim + 2 * d_state;  // stream channels: x, then B, then C
+  // with the convolution, a head's window rows are loaded through a buffer resource over one batch
+  // element's stream with 32-bit byte offsets
+  if ((cw_f || cw_r) && seqlen * xs * 2 + 256 > INT32_MAX) return BIMAMBA_ERR_UNSUPPORTED;
   const size_t act_x = static_cast<size_t>(batch) * seqlen * xs * 2;
   const size_t act_o = static_cast<size_t>(batch) * seqlen * nheads * headdim * 2;
   const size_t dtb = static_cast<size_t>(batch) * seqlen * nheads * 2;

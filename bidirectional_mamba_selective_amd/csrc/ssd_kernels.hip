@@ -100,6 +100,13 @@ __device__ __forceinline__ bf16x8 lds8(const uint16_t* s, int idx) {
 
 __device__ __forceinline__ float ex(float v) { return fast_exp2(v * kLog2e); }
 
+// s_waitcnt vmcnt(0): every vector memory operation this wavefront issued is complete (direct-to-LDS loads
+// included, which the compiler does not track); the empty asm keeps LDS accesses from moving across it.
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt at their maxima (not waited for)
+  asm volatile("" ::: "memory");
+}
+
 // Per-token quantities of one run, one lane per token, in LDS rows of 64.
 enum Tok { kDl = 0, kS, kE, kWr, kWf, kRr, kRf, kTokRows };
 
@@ -1001,45 +1008,78 @@ __global__ __launch_bounds__(kThreads) void k_ssd1_stage(Args a) {
 template <int DIR, bool CONV>
 struct XRun;
 
+// Rows of a run's window for the convolution: the run's 64 tokens and the 3-token halo (before them for the
+// causal filter, after them for the anti-causal one).
+constexpr int kWinRows = Q + 3;
+
 template <int DIR>
 struct XRun<DIR, true> {
-  uint16_t r[8 + 3];
-  __device__ __forceinline__ void load(const Args& a, int64_t b, int64_t t0, int64_t h, int tid) {
-    const int c = tid & 31, g = tid >> 5;
-    conv_rows<DIR, 8>(a.x + b * a.L * a.xs + h * P + c, a.xs, a.L, t0 + 8 * g + (DIR == 1 ? -3 : 0), r);
+  // The window's rows of the head's 32 x channels (64 bytes each) are brought into LDS (sRaw, double
+  // buffered) by direct-to-LDS buffer loads, 16 bytes per lane: chunk q = 4 row + part lands at byte 16 q.
+  // The resource starts at channel h P of the batch element's first token and ends with its last token, so
+  // the rows before the sequence (negative offsets wrap to huge ones) and after it are out of range and read
+  // as zero.  The compiler does not track these loads: the walk waits for them (vmcnt 0) before the barrier
+  // that precedes their use.
+  uint16_t* sRaw;  // [2][kWinRows * P]
+  __device__ __forceinline__ void load(const Args& a, int64_t b, int64_t t0, int64_t h, int tid, int buf) {
+    const int64_t tfirst = t0 + (DIR == 1 ? -3 : 0);
+    const uint16_t* base = a.x + b * a.L * a.xs + h * P;
+    const int64_t bytes = (a.L * a.xs - h * P) * 2;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base), static_cast<short>(0), static_cast<int>(bytes), 0x00020000);
+    uint16_t* dst = sRaw + buf * (kWinRows * P);
+    const int w = tid >> 6, lane = tid & 63;
+    // chunks 64 w + lane (rows 16 w .. 16 w + 15), then chunks 256 .. 267 (the last 3 rows) by wavefront 0
+    for (int pass = 0; pass < 2; ++pass) {
+      const int q = pass == 0 ? 64 * w + lane : 256 + lane;
+      if (pass == 1 && (w != 0 || lane >= 4 * kWinRows - 256)) break;
+      const int row = q >> 2, part = q & 3;
+      const int32_t off = static_cast<int32_t>((tfirst + row) * a.xs * 2) + part * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (q - lane) * 8),
+                                               16, static_cast<uint32_t>(off), 0, 0, 0);
+    }
   }
-  // x into sXT (when given) and x weighted per token (weights wtok[j] * wscale) into sXW (when given)
-  __device__ __forceinline__ void commit(uint16_t* sXT, uint16_t* sXW, const float* wtok, float wscale,
-                                         const float (&w)[4], float bias, int64_t t0, int64_t L, int tid) const {
+  // the convolution of the window in sRaw[buf]: thread tid convolves channel c = tid % 32 over tokens
+  // 8 g .. 8 g + 7 (g = tid / 32); returns that chunk of the x tile (8 bf16 values, token order)
+  __device__ __forceinline__ uint4 conv(const float (&w)[4], float bias, int64_t t0, int64_t L, int tid, int buf) const {
     const int c = tid & 31, g = tid >> 5;
-    uint16_t o[8];
-    conv_outputs<DIR, 8>(r, w, bias, t0 + 8 * g, L, o);
-    if (sXT) {
-      const uint4 v = make_uint4(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16),
-                                 o[4] | (static_cast<uint32_t>(o[5]) << 16), o[6] | (static_cast<uint32_t>(o[7]) << 16));
-      *reinterpret_cast<uint4*>(sXT + sw128(c, g)) = v;
-    }
-    if (sXW) {
-      uint16_t q[8];
+    const uint16_t* src = sRaw + buf * (kWinRows * P);
+    uint16_t r[8 + 3], o[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = to_bf(bf(o[i]) * (wtok[8 * g + i] * wscale));
-      const uint4 v = make_uint4(q[0] | (static_cast<uint32_t>(q[1]) << 16), q[2] | (static_cast<uint32_t>(q[3]) << 16),
-                                 q[4] | (static_cast<uint32_t>(q[5]) << 16), q[6] | (static_cast<uint32_t>(q[7]) << 16));
-      *reinterpret_cast<uint4*>(sXW + sw128(c, g)) = v;
+    for (int i = 0; i < 11; ++i) r[i] = src[(8 * g + i) * P + c];
+    conv_outputs<DIR, 8>(r, w, bias, t0 + 8 * g, L, o);
+    return make_uint4(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16),
+                      o[4] | (static_cast<uint32_t>(o[5]) << 16), o[6] | (static_cast<uint32_t>(o[7]) << 16));
+  }
+  // this thread's chunk v of the x tile into the channel-major tile dst (sXT's layout)
+  __device__ __forceinline__ void put(uint16_t* dst, uint4 v, int tid) const {
+    *reinterpret_cast<uint4*>(dst + sw128(tid & 31, tid >> 5)) = v;
+  }
+  // this thread's chunk v weighted per token (weights wtok[j] * wscale) into dst
+  __device__ __forceinline__ void weight(uint16_t* dst, uint4 v, const float* wtok, float wscale, int tid) const {
+    const int c = tid & 31, g = tid >> 5;
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t q[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = __uint_as_float(in[e] << 16) * (wtok[8 * g + 2 * e] * wscale);
+      const float hi = __uint_as_float(in[e] & 0xffff0000u) * (wtok[8 * g + 2 * e + 1] * wscale);
+      q[e] = static_cast<uint32_t>(to_bf(lo)) | (static_cast<uint32_t>(to_bf(hi)) << 16);
     }
+    *reinterpret_cast<uint4*>(dst + sw128(c, g)) = make_uint4(q[0], q[1], q[2], q[3]);
   }
 };
 
 template <int DIR>
 struct XRun<DIR, false> {
   uint4 px;
-  __device__ __forceinline__ void load(const Args& a, int64_t b, int64_t t0, int64_t h, int tid) {
+  __device__ __forceinline__ void load(const Args& a, int64_t b, int64_t t0, int64_t h, int tid, int) {
     const int j = tid >> 2, pc = tid & 3;
     px = (t0 + j >= a.L) ? make_uint4(0, 0, 0, 0)
                          : *reinterpret_cast<const uint4*>(a.x + (b * a.L + t0 + j) * a.xs + h * P + 8 * pc);
   }
   __device__ __forceinline__ void commit(uint16_t* sXT, uint16_t* sXW, const float* wtok, float wscale,
-                                         const float (&)[4], float, int64_t, int64_t, int tid) const {
+                                         const float (&)[4], float, int64_t, int64_t, int tid, int) const {
     if (sXT) put_xt(sXT, px, tid, nullptr, 1.0f);
     if (sXW) put_xt(sXW, px, tid, wtok, wscale);
   }
@@ -1054,6 +1094,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd1_summary(Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t sBT[N * Q];
   __shared__ __attribute__((aligned(16))) uint16_t sXW[P * Q];
   __shared__ __attribute__((aligned(16))) float sTok[2][kTokRows * 64];
+  // with the convolution: the raw windows, double buffered (the next run's arrives during this run's step)
+  __shared__ __attribute__((aligned(16))) uint16_t sRaw[CONV ? 2 * kWinRows * P : 8];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   int64_t b, c, h;
   decode_item(a, b, c, h);
@@ -1069,6 +1111,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd1_summary(Args a) {
   float prod = 1.0f;  // product of abar over the runs done
   u32x4 pbt[4];
   XRun<DIR, CONV> xr;
+  if constexpr (CONV) xr.sRaw = sRaw;
   uint16_t pdt = 0, pdt2 = 0;  // step sizes two steps ahead
   auto run_of = [&](int64_t st) { return DIR == 1 ? st : nrun - 1 - st; };
   auto issue = [&](int64_t st) {
@@ -1077,7 +1120,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd1_summary(Args a) {
     const u32x4* b4 = reinterpret_cast<const u32x4*>(a.bt + (b * a.nsub + sub) * static_cast<int64_t>(Q * N));
 #pragma unroll
     for (int i = 0; i < 4; ++i) pbt[i] = b4[tid + kThreads * i];
-    xr.load(a, b, sub * Q, h, tid);
+    xr.load(a, b, sub * Q, h, tid, static_cast<int>(st & 1));
   };
   if (w == 0) pdt = load_dt(a, b, (sub0 + run_of(0)) * Q, h, l);
   issue(0);
@@ -1086,13 +1129,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd1_summary(Args a) {
   for (int64_t st = 0; st < nrun; ++st) {
     const int64_t t0 = (sub0 + run_of(st)) * Q;
     const float* tok = sTok[st & 1];
+    if (CONV) wait_vmem();  // this run's window, brought into LDS by the last step's direct loads
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ci = tid + kThreads * i;
       *reinterpret_cast<u32x4*>(sBT + sw128(ci >> 3, ci & 7)) = pbt[i];
     }
-    xr.commit(nullptr, sXW, tok + (DIR == 1 ? kWf : kWr) * 64, 1.0f, cw, cbias, t0, a.L, tid);
+    if constexpr (CONV) {
+      xr.weight(sXW, xr.conv(cw, cbias, t0, a.L, tid, static_cast<int>(st & 1)), tok + (DIR == 1 ? kWf : kWr) * 64,
+                1.0f, tid);
+    } else {
+      xr.commit(nullptr, sXW, tok + (DIR == 1 ? kWf : kWr) * 64, 1.0f, cw, cbias, t0, a.L, tid, 0);
+    }
     __syncthreads();
     if (st + 1 < nrun) issue(st + 1);
     const float eS = ex(tok[kS * 64 + 63]);
@@ -1118,6 +1167,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd1_walk(Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t sZ[4 * 16 * P];
   __shared__ __attribute__((aligned(16))) uint16_t sY[4 * 16 * P];
   __shared__ __attribute__((aligned(16))) float sTok[2][kTokRows * 64];
+  // with the convolution: the raw windows, double buffered (the next run's arrives during this run's step);
+  // each is convolved in the commit phase, whose VALU slots are otherwise mostly idle
+  __shared__ __attribute__((aligned(16))) uint16_t sRaw[CONV ? 2 * kWinRows * P : 8];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, q4 = l >> 4, l16 = l & 15;
   int64_t b, c, h;
   decode_item(a, b, c, h);
@@ -1139,6 +1191,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd1_walk(Args a) {
   f32x4 pg[4];
   uint4 pz;
   XRun<DIR, CONV> xr;
+  if constexpr (CONV) xr.sRaw = sRaw;
   uint16_t pdt = 0, pdt2 = 0;
   auto run_of = [&](int64_t st) { return DIR == 1 ? st : nrun - 1 - st; };
   auto issue = [&](int64_t st) {
@@ -1152,7 +1205,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd1_walk(Args a) {
     const float* gg = a.g + (b * a.nsub + sub) * static_cast<int64_t>(Q * Q);
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) pg[tj] = *reinterpret_cast<const f32x4*>(gg + ((w * 4 + tj) * 64 + l) * 4);
-    xr.load(a, b, t0, h, tid);
+    xr.load(a, b, t0, h, tid, static_cast<int>(st & 1));
     if (a.gate) pz = load_act(a.z, a, b, t0, h, 64 * w + l);
   };
   if (w == 0) pdt = load_dt(a, b, (sub0 + run_of(0)) * Q, h, l);
@@ -1166,8 +1219,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd1_walk(Args a) {
   for (int64_t st = 0; st < nrun; ++st) {
     const int64_t t0 = (sub0 + run_of(st)) * Q;
     const float* tok = sTok[st & 1];
+    uint16_t* xt = sXT;
     bf16x8 cf[4];
     f32x4 gcur[4];
+    if (CONV) wait_vmem();  // this run's window, brought into LDS by the last step's direct loads
     __syncthreads();
     // ---- commit the prefetched registers ----
 #pragma unroll
@@ -1178,7 +1233,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd1_walk(Args a) {
     }
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) gcur[tj] = pg[tj];
-    xr.commit(sXT, sXW, tok + (DIR == 1 ? kWf : kWr) * 64, 1.0f, cw, cbias, t0, a.L, tid);
+    if constexpr (CONV) {
+      const uint4 xc = xr.conv(cw, cbias, t0, a.L, tid, static_cast<int>(st & 1));
+      xr.put(sXT, xc, tid);
+      xr.weight(sXW, xc, tok + (DIR == 1 ? kWf : kWr) * 64, 1.0f, tid);
+    } else {
+      xr.commit(sXT, sXW, tok + (DIR == 1 ? kWf : kWr) * 64, 1.0f, cw, cbias, t0, a.L, tid, 0);
+    }
     if (a.gate) *reinterpret_cast<uint4*>(zslot + (l >> 2) * P + 8 * (l & 3)) = pz;
     state_to_lds(H, sHs, w, l);
     __syncthreads();
@@ -1220,8 +1281,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd1_walk(Args a) {
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
         const int p = 16 * tp + l16;
-        const uint2 lo = *reinterpret_cast<const uint2*>(sXT + sw128(p, jlo >> 3) + (jlo & 7));
-        const uint2 hi = *reinterpret_cast<const uint2*>(sXT + sw128(p, (jlo + 16) >> 3) + (jlo & 7));
+        const uint2 lo = *reinterpret_cast<const uint2*>(xt + sw128(p, jlo >> 3) + (jlo & 7));
+        const uint2 hi = *reinterpret_cast<const uint2*>(xt + sw128(p, (jlo + 16) >> 3) + (jlo & 7));
         y[tp] = mfma(wa, __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), y[tp]);
       }
     }
@@ -1241,7 +1302,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd1_walk(Args a) {
 #pragma unroll
     for (int tp = 0; tp < 2; ++tp) {
       const int p = 16 * tp + l16;
-      const uint2 xv = *reinterpret_cast<const uint2*>(sXT + sw128(p, i0 >> 3) + (i0 & 7));
+      const uint2 xv = *reinterpret_cast<const uint2*>(xt + sw128(p, i0 >> 3) + (i0 & 7));
       const float xs[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xffff0000u),
                            __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xffff0000u)};
 #pragma unroll

@@ -266,7 +266,9 @@ int bimamba_ssd_block(const void* x, const void* dt, const float* A, const void*
  * skip that layer (not both); its set's pointers are then not read.
  * Layouts: xbc [batch, seqlen, H*P + 2N] bf16, cw [H*P + 2N, 4] and cb
  * [H*P + 2N] fp32, out [batch, seqlen, H*P] bf16.  Shapes, dtype, heads and
- * D / dt_bias NULL are as for bimamba_ssd_fwd; d_conv must be 4; flags may only
+ * D / dt_bias NULL are as for bimamba_ssd_fwd, and with a convolution one
+ * batch element's stream must stay below 2^31 bytes (seqlen * (H*P + 2N) * 2
+ * + 256, e.g. seqlen <= 262143 at 4096 channels); d_conv must be 4; flags may only
  * be BIMAMBA_FLAG_NO_GATE (then z may be NULL).  xbc, z and out 16-byte
  * aligned, dt 2-byte, the fp32 parameters 4-byte.  The workspace
  * (bimamba_ssd_fwd_workspace_bytes(batch, seqlen, nheads, headdim, d_state)

@@ -471,3 +471,21 @@ def test_ssd_conv_untied_checks_run_in_order():
     assert call_ssd_conv(orr=None, xr=None, dtr=None, Ar=None, cwf=None, cbf=None, zf=None, Df=None, bf=None,
                          flags=_lib.FLAG_NO_GATE) == WS
     assert call_ssd_conv(of=None, xf=None, dtf=None, Af=None) == WS
+
+
+def test_ssd_conv_untied_limits_the_stream_to_32bit_offsets():
+    # 2 heads: 320 channels, 640 bytes per token
+    lib = _lib.load()
+
+    def p(i):
+        return ctypes.c_void_p((1 << 42) + i * (1 << 33))
+
+    def call(L, cw):
+        ptr = [p(i) for i in range(18)]
+        ptr[1] = cw(1)
+        ptr[10] = cw(10)
+        return lib.bimamba_ssd_conv_untied(*ptr, 1, L, 2, 32, 128, 4, _lib.BIMAMBA_BF16, 0, p(30), 0, None)
+
+    assert call(3355443, lambda i: p(i)) == UNS  # the stream (+ 256) passes 2^31 - 1 bytes
+    assert call(3355442, lambda i: p(i)) == WS  # just below
+    assert call(3355443, lambda i: None) == WS  # without the convolution there is no such limit
