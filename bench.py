@@ -54,6 +54,7 @@ SSD_SOURCE = os.path.join(ROOT, "bidirectional_mamba_selective_amd", "csrc", "ss
 CONV_SOURCE = os.path.join(ROOT, "bidirectional_mamba_selective_amd", "csrc", "conv_kernels.hip")
 SSD_PROFILE = os.path.join(ROOT, "profiles", "k_ssd_long_64k_bf16_traffic.txt")
 CONV_PROFILE = os.path.join(ROOT, "profiles", "k_conv_long_64k_bf16_traffic.txt")
+SSDCONV_PROFILE = os.path.join(ROOT, "profiles", "k_ssd1_conv_long_64k_bf16_traffic.txt")
 
 
 def log(msg):
@@ -159,7 +160,7 @@ def host_workers():
 def bench_micro(torch, dev, stream):
     """Microbenchmarks on this machine, each timed with HIP events on `stream` (median of 5): HBM read-only and
     copy streams over 4 GiB and 2 GiB, the issue rate of independent fp32 FMAs and of v_exp_f32 at 1 to 8
-    wavefronts per SIMD, and an empty kernel's launch floor replayed from a graph (one 64-lane workgroup,
+    wavefronts per SIMD, FMAs with an SGPR operand, and an empty kernel's launch floor replayed from a graph (one 64-lane workgroup,
     and the block step's grid of 256 workgroups of 512 threads)."""
     import ctypes
 
@@ -171,6 +172,7 @@ def bench_micro(torch, dev, stream):
     lib.micro_copy.argtypes = [vp, vp, sz, vp]
     lib.micro_fma.argtypes = [vp, ci, ci, vp, vp]
     lib.micro_exp.argtypes = [vp, ci, ci, vp]
+    lib.micro_fma_sgpr.argtypes = [vp, ci, ci, ci, vp]
     lib.micro_empty.argtypes = [ci, ci, vp]
     sp = ctypes.c_void_p(stream.cuda_stream)
 
@@ -219,6 +221,14 @@ def bench_micro(torch, dev, stream):
     res["exp_lanes_per_clk_per_cu"] = ex
     # clocks per wave64 FMA instruction and SIMD at 4 wavefronts per SIMD (the scan kernels' occupancy)
     res["fma_clk_per_instruction_4waves"] = round(64 * 4 / fma["4"], 3)
+    # the same at 8 wavefronts per SIMD, and with a wave-uniform (SGPR) multiplier in every FMA or in every
+    # other one: clocks per wavefront instruction and SIMD
+    res["fma_clk_per_instruction_8waves"] = round(64 * 4 / fma["8"], 3)
+    sg = {}
+    for mode, name in ((0, "every_fma"), (1, "every_other_fma")):
+        t = timed(lambda: lib.micro_fma_sgpr(ctypes.c_void_p(sink.data_ptr()), 4096, 8, mode, sp))
+        sg[name] = round(t * ghz * 1e9 / (8 * 8 * 4096), 3)
+    res["fma_sgpr_operand_clk_per_instruction_8waves"] = sg
 
     floor = {}
     for groups, threads in ((1, 64), (256, 512)):
@@ -239,7 +249,7 @@ def bench_micro(torch, dev, stream):
         floor[f"{groups}x{threads}"] = round(float(np.median(ts[1:])) * 1e6 / 200, 2)
     res["empty_kernel_graph_us"] = floor
     log(f"micro: read {res['hbm_read_gbs']} GB/s, copy {res['hbm_copy_gbs']} GB/s, fma lanes/clk/CU {fma}, "
-        f"exp {ex}, empty-kernel graph floor {floor} us")
+        f"exp {ex}, SGPR-operand fma clk/instr {sg}, empty-kernel graph floor {floor} us")
     return res
 
 
@@ -599,7 +609,11 @@ def bench_ssd_conv(args, torch, bm, I, dev, stream):
             "ms_layers_unfused": round(ms_layers, 4),
             "tokens_per_s_fused": round(L / (ms_fused * 1e-3), 1),
             "hbm": {"algorithmic_bytes": nbytes, "achieved_gbs": round(nbytes / (ms_fused * 1e-3) / 1e9, 1),
-                    "frac_of_peak": round(nbytes / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                    "frac_of_peak": round(nbytes / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "traffic_fused": profiled_traffic(profile=SSDCONV_PROFILE, source=SSD_SOURCE,
+                                                      key="hbm_bytes_per_call_fused"),
+                    "traffic_two_pass": profiled_traffic(profile=SSDCONV_PROFILE, source=SSD_SOURCE,
+                                                         key="hbm_bytes_per_call_two_pass")},
             "note": "two untied Mamba-2 layers (forward: causal conv, reverse: anti-causal conv, each its own "
                     "stream, dt, z and parameters); two-pass = the convolution kernel on each stream, then the "
                     "same layers reading the stored convolution output"}

@@ -1,10 +1,17 @@
 """Build libbimamba.so (and the benchmark's libbimamba_micro.so) in-tree with hipcc for gfx950.
 
     python -m bidirectional_mamba_selective_amd.build
+    python -m bidirectional_mamba_selective_amd.build --asan-host
 
 Compiles every source under csrc/ into one shared library next to this file,
 and micro/micro_kernels.hip (the microbenchmarks behind the reported rooflines)
-into a second one.
+into a second one.  --asan-host instead writes libbimamba_asan.so: the same
+sources with AddressSanitizer on the host code only (argument checking, plans,
+launches; device code is built as usual), for the ABI tests on the CPU:
+
+    LD_PRELOAD=$(gcc -print-file-name=libasan.so) ASAN_OPTIONS=detect_leaks=0 \
+        python -m pytest tests/test_abi.py -m "not gpu" -p no:cacheprovider \
+        --bimamba-lib bidirectional_mamba_selective_amd/libbimamba_asan.so
 """
 from __future__ import annotations
 
@@ -18,6 +25,9 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbimamba.so")
 MICRO_SRC = os.path.join(PKG, "micro", "micro_kernels.hip")
 MICRO_LIB = os.path.join(PKG, "libbimamba_micro.so")
+ASAN_LIB = os.path.join(PKG, "libbimamba_asan.so")
+# AddressSanitizer for the host pass only (each -fsanitize= behind -Xarch_host)
+ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions stay disabled for all device code.
@@ -66,5 +76,13 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     return lib
 
 
+def build_asan_host(verbose: bool = False) -> str:
+    """The library with AddressSanitizer on its host code, as libbimamba_asan.so."""
+    return _compile(sources(), ASAN_LIB, verbose, ASAN_HOST_FLAGS)
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--asan-host" in sys.argv:
+        print(build_asan_host(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

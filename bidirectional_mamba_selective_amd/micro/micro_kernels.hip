@@ -55,6 +55,32 @@ __global__ __launch_bounds__(64) void k_fma(float* out, int iters, float a0, flo
   }
 }
 
+// The same chains with a wave-uniform multiplier, which the compiler keeps in an SGPR and feeds to
+// v_fma_f32 as a scalar operand: mode 0 gives every chain the SGPR operand, mode 1 only the even chains (the
+// odd ones keep a lane-varying VGPR multiplier), so SGPR-operand instructions alternate with VGPR-only ones.
+__global__ __launch_bounds__(64) void k_fma_sgpr(float* out, int iters, float a0, float b0, int mode) {
+  const float av = a0 * (1.0f + 1e-30f * static_cast<float>(threadIdx.x));
+  const float b = b0 * (1.0f + 1e-30f * static_cast<float>(threadIdx.x));
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = static_cast<float>(threadIdx.x + k);
+  if (mode == 0) {
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = fmaf(v[k], a0, b);
+    }
+  } else {
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = fmaf(v[k], (k & 1) ? av : a0, b);
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += v[k];
+  if (s == -1.2345e37f) out[threadIdx.x] = s;
+}
+
 // 8 independent v_exp_f32 chains per lane (each step 2^(v * a), which stays finite for |a| < 1).
 __global__ __launch_bounds__(64) void k_exp(float* out, int iters, float a) {
   float v[8];
@@ -92,6 +118,12 @@ int micro_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
 // 64-bit counters (see k_fma)
 int micro_fma(float* out, int iters, int waves_per_simd, unsigned long long* clk, hipStream_t stream) {
   hipLaunchKernelGGL(k_fma, dim3(1024 * waves_per_simd), dim3(64), 0, stream, out, iters, 0.999f, 0.001f, clk);
+  return static_cast<int>(hipGetLastError());
+}
+
+// mode 0: every FMA reads an SGPR multiplier; mode 1: every other one (see k_fma_sgpr)
+int micro_fma_sgpr(float* out, int iters, int waves_per_simd, int mode, hipStream_t stream) {
+  hipLaunchKernelGGL(k_fma_sgpr, dim3(1024 * waves_per_simd), dim3(64), 0, stream, out, iters, 0.999f, 0.001f, mode);
   return static_cast<int>(hipGetLastError());
 }
 
