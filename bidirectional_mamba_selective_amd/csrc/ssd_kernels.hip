@@ -156,18 +156,30 @@ __device__ __forceinline__ uint16_t load_dt(const Args& a, int64_t b, int64_t t0
   return (t0 + l < a.L) ? a.dt[(b * a.L + t0 + l) * a.H + h] : static_cast<uint16_t>(0);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront: shifts within rows of 16 lanes (DPP row_shr, lanes
+// shifted in from outside the row read 0), then each row's total carried into the rows after it (DPP
+// row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3; rows left out of the row mask add 0).
+template <int CTRL, int ROW_MASK, bool BOUND0>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, BOUND0));
+}
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp_f32<0x111, 0xf, true>(v);   // row_shr:1
+  v += dpp_f32<0x112, 0xf, true>(v);   // row_shr:2
+  v += dpp_f32<0x114, 0xf, true>(v);   // row_shr:4
+  v += dpp_f32<0x118, 0xf, true>(v);   // row_shr:8
+  v += dpp_f32<0x142, 0xa, false>(v);  // row_bcast:15
+  v += dpp_f32<0x143, 0xc, false>(v);  // row_bcast:31
+  return v;
+}
+
 // One run's per-token quantities, computed by one wavefront (lane = token).
 // Tokens past the sequence end get delta = 0: no decay and no input.
 __device__ __forceinline__ void token_prep(float* tok, uint16_t dtv, bool valid, float Ah, float bias, int l) {
   const float dl = valid ? softplus_f32(bf(dtv) + bias) : 0.0f;
   const float av = dl * Ah;
-  float s = av;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float t = __shfl_up(s, o, 64);
-    if (l >= o) s += t;
-  }
-  const float S = __shfl(s, 63, 64);
+  const float s = wave_prefix_sum(av);
+  const float S = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 63));
   const float e = s - av;
   tok[kDl * 64 + l] = dl;
   tok[kS * 64 + l] = s;
@@ -176,6 +188,32 @@ __device__ __forceinline__ void token_prep(float* tok, uint16_t dtv, bool valid,
   tok[kWf * 64 + l] = ex(S - s) * dl;
   tok[kRr * 64 + l] = ex(S - e);
   tok[kRf * 64 + l] = ex(s);
+}
+
+// The decay mask on wavefront w's block tj of C B^T (rows i = 16w + l16, columns j = j0 + r, j0 = 16tj + 4q4),
+// times delta_j: forward e^{s_i - s_j} below the diagonal, reverse e^{e_j - e_i} above it, `diag` on it.  A
+// block lies wholly below the diagonal when tj < w and wholly above it when tj > w; w is wavefront-uniform, so
+// only the diagonal block selects per lane.
+template <bool FWD, bool REV>
+__device__ __forceinline__ void mask_block(f32x4& g, int tj, int w, int i, int j0, float si, float ei,
+                                           const f32x4& sj, const f32x4& ej, const f32x4& dj, float diag) {
+  if (tj < w) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) g[r] = FWD ? g[r] * (ex(si - sj[r]) * dj[r]) : 0.0f;
+  } else if (tj > w) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) g[r] = REV ? g[r] * (ex(ej[r] - ei) * dj[r]) : 0.0f;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + r;
+      float m;
+      if (j < i) m = FWD ? ex(si - sj[r]) : 0.0f;
+      else if (j > i) m = REV ? ex(ej[r] - ei) : 0.0f;
+      else m = diag;
+      g[r] *= m * dj[r];
+    }
+  }
 }
 
 // 16 bytes of a [batch, L, H*P] tensor: token t0 + j of the run with j = q/4 and
@@ -447,15 +485,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_rsweep(Args a) {
       const f32x4 sj = *reinterpret_cast<const f32x4*>(tok + kS * 64 + j0);
       const f32x4 ej = *reinterpret_cast<const f32x4*>(tok + kE * 64 + j0);
       const f32x4 dj = *reinterpret_cast<const f32x4*>(tok + kDl * 64 + j0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + r;
-        float m;
-        if (j < i) m = kFwd ? ex(si - sj[r]) : 0.0f;
-        else if (j > i) m = kRev ? ex(ej[r] - ei) : 0.0f;
-        else m = kDiag;
-        gcur[tj][r] *= m * dj[r];
-      }
+      mask_block<kFwd, kRev>(gcur[tj], tj, __builtin_amdgcn_readfirstlane(w), i, j0, si, ei, sj, ej, dj, kDiag);
     }
     f32x4 y[2] = {zero4(), zero4()};
 #pragma unroll
@@ -791,15 +821,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_block(Args a) {
     const f32x4 sj = *reinterpret_cast<const f32x4*>(tok + kS * 64 + j0);
     const f32x4 ej = *reinterpret_cast<const f32x4*>(tok + kE * 64 + j0);
     const f32x4 dj = *reinterpret_cast<const f32x4*>(tok + kDl * 64 + j0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = j0 + r;
-      float m;
-      if (j < i) m = kFwd ? ex(si - sj[r]) : 0.0f;
-      else if (j > i) m = kRev ? ex(ej[r] - ei) : 0.0f;
-      else m = kDiag;
-      gcur[tj][r] *= m * dj[r];
-    }
+    mask_block<kFwd, kRev>(gcur[tj], tj, __builtin_amdgcn_readfirstlane(w), i, j0, si, ei, sj, ej, dj, kDiag);
   }
   f32x4 y[2] = {zero4(), zero4()};
 #pragma unroll
@@ -1258,15 +1280,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd1_walk(Args a) {
       const f32x4 sj = *reinterpret_cast<const f32x4*>(tok + kS * 64 + j0);
       const f32x4 ej = *reinterpret_cast<const f32x4*>(tok + kE * 64 + j0);
       const f32x4 dj = *reinterpret_cast<const f32x4*>(tok + kDl * 64 + j0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + r;
-        float m;
-        if (j == i) m = 1.0f;
-        else if (DIR == 1) m = j < i ? ex(si - sj[r]) : 0.0f;
-        else m = j > i ? ex(ej[r] - ei) : 0.0f;
-        gcur[tj][r] *= m * dj[r];
-      }
+      mask_block<DIR == 1, DIR == 2>(gcur[tj], tj, __builtin_amdgcn_readfirstlane(w), i, j0, si, ei, sj, ej, dj,
+                                     1.0f);
     }
     f32x4 y[2] = {zero4(), zero4()};
 #pragma unroll
