@@ -36,7 +36,11 @@
 //              C . (h_fwd + h_rev) per token; then skip term, gate, store.  A
 //              reverse-only pass walks the tiles right to left instead and
 //              carries its reverse state from tile to tile.
-//   k_block    a whole short block of block-cache decoding in one kernel.
+//   k_block    a whole short block of block-cache decoding in one kernel
+//              (blocks of up to 16 tokens, and of 65 to 128, in two halves).
+//   k_block_parts  the same for blocks of 17 to 64 tokens, cut into parts of
+//              16 tokens whose chains run from zero side by side and are
+//              corrected afterwards by the decayed entering states.
 // The transition is diagonal per (d, n), so nothing here is a dense
 // contraction; the kernels are bound by VALU and transcendental issue.
 //
@@ -799,6 +803,89 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
+// Step 1 of the block kernels.  Every global load is issued at once, from clamped in-bounds addresses (a load
+// under a branch is waited for at the branch's end), and the values are selected afterwards; stand-ins for
+// absent tensors: A for h_in, D and dt_bias, x for z (their values are not used).  Then delta, delta * x, the
+// skip term D x (counted once per direction the output keeps) and the gate SiLU(z) per (token, channel), and
+// B, C per (state, token), go to LDS, zero past the block and for states n >= N.  Returns the lane's A[d, n]
+// and cached state (read before any write: h_out may alias h_in, and every write of h_out follows a barrier
+// after this).  The caller synchronises before reading the LDS.
+template <typename T, int GM, int kThreads, typename SM>
+__device__ __forceinline__ void block_stage(SM& sm, const T* __restrict__ x, const T* __restrict__ dt,
+                                            const T* __restrict__ z, const float* __restrict__ A,
+                                            const T* __restrict__ Bm, const T* __restrict__ Cm,
+                                            const float* __restrict__ Dv, const float* __restrict__ dt_bias,
+                                            const float* h_in, int G, int D, int N, bool gate, bool both, int n,
+                                            int d, int b, float& av, float& hv) {
+  // (token, channel) pairs, and B, C elements, per thread: GM * 16 of each over kThreads threads (with more
+  // threads than pairs, the threads past them only load clamped stand-ins and store nothing)
+  constexpr int kPairs = GM * 16;
+  constexpr int kTpt = (kPairs + kThreads - 1) / kThreads;
+  constexpr bool kAll = kPairs % kThreads == 0;
+  const int tid = threadIdx.x;
+  const size_t row = static_cast<size_t>(b) * G;  // first token row of this batch element
+  const int nc = min(n, N - 1);
+  av = A[static_cast<size_t>(d) * N + nc];
+  const size_t hs = h_in ? (static_cast<size_t>(b) * D + d) * N + nc : static_cast<size_t>(d) * N + nc;
+  hv = (h_in ? h_in : A)[hs];
+  const int c1 = tid & 15;  // channel of this thread's (token, channel) pairs
+  const int d1 = blockIdx.x * 16 + c1;
+  const float dvv = (Dv ? Dv : A)[d1];
+  const float bsv = (dt_bias ? dt_bias : A)[d1];
+  const T* zbase = gate ? z : x;
+  float xv[kTpt], dv[kTpt], zv[kTpt], bv[kTpt], cv[kTpt];
+#pragma unroll
+  for (int k = 0; k < kTpt; ++k) {
+    const int i = min(tid + kThreads * k, kPairs - 1);  // pair (token i / 16, channel i % 16); B, C element
+    const int t = i / 16;                               // (state i / GM, token i % GM)
+    const size_t o = (row + min(t, G - 1)) * D + d1;
+    xv[k] = ld_any(x + o);
+    dv[k] = ld_any(dt + o);
+    zv[k] = ld_any(zbase + o);
+    const size_t ob = (row + min(i % GM, G - 1)) * N + min(i / GM, N - 1);
+    bv[k] = ld_any(Bm + ob);
+    cv[k] = ld_any(Cm + ob);
+  }
+  const float bias = dt_bias ? bsv : 0.0f;
+  const float skip = Dv ? (both ? 2.0f : 1.0f) * dvv : 0.0f;
+#pragma unroll
+  for (int k = 0; k < kTpt; ++k) {
+    const int i = tid + kThreads * k;
+    if (!kAll && i >= kPairs) break;
+    const int t = i / 16;
+    const bool live = t < G;
+    const float dl = live ? softplus_f32(dv[k] + bias) : 0.0f;
+    const float xl = live ? xv[k] : 0.0f;
+    sm.dl[t][c1] = dl;
+    sm.u[t][c1] = dl * xl;
+    sm.sx[t][c1] = skip * xl;
+    sm.g[t][c1] = (live && gate) ? silu_f32(zv[k]) : 1.0f;
+    const bool ok = i / GM < N && i % GM < G;
+    sm.b[i / GM][i % GM] = ok ? bv[k] : 0.0f;
+    sm.c[i / GM][i % GM] = ok ? cv[k] : 0.0f;
+  }
+}
+
+// Step 3 of the block kernels: the four wavefronts' sums of a token (in sm.part) in a fixed order, the skip
+// term and the gate, and the store.
+template <typename T, int GM, int kThreads, typename SM>
+__device__ __forceinline__ void block_store(const SM& sm, T* __restrict__ out, int G, int D, int b) {
+  constexpr int kPairs = GM * 16;
+  constexpr int kTpt = (kPairs + kThreads - 1) / kThreads;
+  const int tid = threadIdx.x, c1 = tid & 15;
+  const int d1 = blockIdx.x * 16 + c1;
+  const size_t row = static_cast<size_t>(b) * G;
+#pragma unroll
+  for (int k = 0; k < kTpt; ++k) {
+    const int i = tid + kThreads * k;
+    const int t = i / 16;
+    if (i < kPairs && t < G) {
+      const float acc = ((sm.part[0][t][c1] + sm.part[1][t][c1]) + sm.part[2][t][c1]) + sm.part[3][t][c1];
+      st_any(out + (row + t) * D + d1, (acc + sm.sx[t][c1]) * sm.g[t][c1]);
+    }
+  }
+}
+
 template <typename T, int GM, int HV>
 __global__ __launch_bounds__(256 * HV) void k_block(const T* __restrict__ x, const T* __restrict__ dt,
                                                     const T* __restrict__ z, const float* __restrict__ A,
@@ -809,8 +896,7 @@ __global__ __launch_bounds__(256 * HV) void k_block(const T* __restrict__ x, con
   using S = BlockSmem<GM, HV>;
   static_assert(HV == 1 || (HV == 2 && GM >= 32), "halves of at least 16 tokens");
   constexpr int kThreads = 256 * HV;
-  constexpr int GH = GM / HV;             // tokens per half
-  constexpr int kTpt = GM * 16 / kThreads;  // (token, channel) pairs and B, C elements per thread
+  constexpr int GH = GM / HV;  // tokens per half
   __shared__ S sm;
   const int tid = threadIdx.x;
   const int half = HV == 2 ? tid / 256 : 0;  // wavefront-uniform
@@ -820,55 +906,14 @@ __global__ __launch_bounds__(256 * HV) void k_block(const T* __restrict__ x, con
   const int n = wv * 4 + (lane & 3);  // its state
   const int d = blockIdx.x * 16 + cl;
   const int b = blockIdx.y;
-  const size_t row = static_cast<size_t>(b) * G;  // first token row of this batch element
   const bool gate = (flags & kNoGate) == 0;
   const bool fwd = (flags & kRevOnly) == 0;
   const bool rev = (flags & kFwdOnly) == 0;
 
-  // 1. All loads first, unconditionally from clamped addresses (a load under a branch is waited for
-  //    at the branch's end); the values are selected afterwards.  Stand-ins for absent tensors: A for
-  //    h_in, D and dt_bias, x for z (their values are not used).
-  const int nc = min(n, N - 1);
-  const float av = A[static_cast<size_t>(d) * N + nc];
-  const size_t hs = h_in ? (static_cast<size_t>(b) * D + d) * N + nc : static_cast<size_t>(d) * N + nc;
-  // read before any write: h_out may alias h_in (the lanes that use it consume it before the barrier
-  // that precedes every write of h_out)
-  const float hv = (h_in ? h_in : A)[hs];
-  const int c1 = tid & 15;  // channel of this thread's (token, channel) pairs
-  const int d1 = blockIdx.x * 16 + c1;
-  const float dvv = (Dv ? Dv : A)[d1];
-  const float bsv = (dt_bias ? dt_bias : A)[d1];
-  const T* zbase = gate ? z : x;
-  float xv[kTpt], dv[kTpt], zv[kTpt], bv[kTpt], cv[kTpt];
-#pragma unroll
-  for (int k = 0; k < kTpt; ++k) {
-    const int t = tid / 16 + (kThreads / 16) * k;
-    const size_t o = (row + min(t, G - 1)) * D + d1;
-    xv[k] = ld_any(x + o);
-    dv[k] = ld_any(dt + o);
-    zv[k] = ld_any(zbase + o);
-    const int i = tid + kThreads * k;  // B, C element (state i / GM, token i % GM)
-    const size_t ob = (row + min(i % GM, G - 1)) * N + min(i / GM, N - 1);
-    bv[k] = ld_any(Bm + ob);
-    cv[k] = ld_any(Cm + ob);
-  }
-  const float bias = dt_bias ? bsv : 0.0f;
-  const float skip = Dv ? ((fwd && rev) ? 2.0f : 1.0f) * dvv : 0.0f;
-#pragma unroll
-  for (int k = 0; k < kTpt; ++k) {
-    const int t = tid / 16 + (kThreads / 16) * k;
-    const bool live = t < G;
-    const float dl = live ? softplus_f32(dv[k] + bias) : 0.0f;
-    const float xl = live ? xv[k] : 0.0f;
-    sm.dl[t][c1] = dl;
-    sm.u[t][c1] = dl * xl;
-    sm.sx[t][c1] = skip * xl;
-    sm.g[t][c1] = (live && gate) ? silu_f32(zv[k]) : 1.0f;
-    const int i = tid + kThreads * k;
-    const bool ok = i / GM < N && i % GM < G;
-    sm.b[i / GM][i % GM] = ok ? bv[k] : 0.0f;
-    sm.c[i / GM][i % GM] = ok ? cv[k] : 0.0f;
-  }
+  // 1. loads and LDS staging
+  float av, hv;
+  block_stage<T, GM, kThreads>(sm, x, dt, z, A, Bm, Cm, Dv, dt_bias, h_in, G, D, N, gate, fwd && rev, n, d, b, av,
+                               hv);
   __syncthreads();
 
   // 2. this lane's recurrences over the tokens t0 .. t0 + GH - 1 of its half (states n >= N have
@@ -957,24 +1002,161 @@ __global__ __launch_bounds__(256 * HV) void k_block(const T* __restrict__ x, con
   __syncthreads();
 
   // 3. the four wavefronts' sums in a fixed order; skip term, gate, store
+  block_store<T, GM, kThreads>(sm, out, G, D, b);
+}
+
+// ---------------------------------------------------------------------------
+// k_block_parts: the block step with the block cut into NQ parts of GP = GM / NQ tokens, one group of four
+// wavefronts per part (lane l of wavefront w of a group: channel 16 blockIdx.x + l / 4, state 4 w + l % 4, as
+// in k_block).  A linear recurrence started from zero at a part's edge differs from the true one by the
+// entering state carried through the part's decay, so a token's two states are
+//   h_fwd(t) = hf(t) + (abar_t0 ... abar_t) h_fwd_in,   h_rev(t) = hr(t) + (abar_t ... abar_t1) h_rev_in
+// with hf, hr the part-local chains (t0, t1 the part's first and last token).  Phase 1 runs both local chains
+// and the two running products (chains of GP tokens, side by side), keeps C_t (hf + hr) and the two products
+// times C_t per token, and leaves the part's product and end states in LDS.  Phase 2 forms the entering
+// states from the parts before (forward, from the cache) and after (reverse, from zero) and adds the two
+// corrections per token: no chain.  The last part's lanes write the new cache.
+// ---------------------------------------------------------------------------
+template <int GM, int NQ>
+struct BlockSmemParts {
+  static constexpr int kRow = GM + 4;  // B and C rows padded as in BlockSmem
+  float dl[GM][16];
+  float u[GM][16];
+  float sx[GM][16];
+  float g[GM][16];
+  __attribute__((aligned(16))) float b[16][kRow];
+  __attribute__((aligned(16))) float c[16][kRow];
+  float part[4][GM][16];
+  float prod[NQ][16][16];  // [part][state][channel]: product of abar over the part
+  float fend[NQ][16][16];  // forward chain from zero, after the part's last token
+  float rbeg[NQ][16][16];  // reverse chain from zero, at the part's first token
+};
+
+template <typename T, int GM, int NQ>
+__global__ __launch_bounds__(256 * NQ) void k_block_parts(const T* __restrict__ x, const T* __restrict__ dt,
+                                                          const T* __restrict__ z, const float* __restrict__ A,
+                                                          const T* __restrict__ Bm, const T* __restrict__ Cm,
+                                                          const float* __restrict__ Dv,
+                                                          const float* __restrict__ dt_bias, const float* h_in,
+                                                          float* h_out, T* __restrict__ out, int G, int D, int N,
+                                                          int flags) {
+  constexpr int kThreads = 256 * NQ;
+  constexpr int GP = GM / NQ;  // tokens per part
+  // every value of a part's tokens stays in registers across the barrier: 16 tokens at most
+  static_assert(GP % 4 == 0 && GP <= 16, "parts of 4 to 16 tokens");
+  __shared__ BlockSmemParts<GM, NQ> sm;
+  const int tid = threadIdx.x;
+  const int p = tid / 256;  // part, wavefront-uniform
+  const int wv = (tid % 256) / 64;
+  const int lane = tid % 64;
+  const int cl = lane >> 2;
+  const int n = wv * 4 + (lane & 3);
+  const int d = blockIdx.x * 16 + cl;
+  const int b = blockIdx.y;
+  const bool gate = (flags & kNoGate) == 0;
+  const bool fwd = (flags & kRevOnly) == 0;
+  const bool rev = (flags & kFwdOnly) == 0;
+
+  float av, hv;
+  block_stage<T, GM, kThreads>(sm, x, dt, z, A, Bm, Cm, Dv, dt_bias, h_in, G, D, N, gate, fwd && rev, n, d, b, av,
+                               hv);
+  __syncthreads();
+
+  // phase 1: the part's chains from zero and the running products of abar
+  const int t0 = p * GP;
+  const float a2 = n < N ? av * kLog2e : 0.0f;
+  float a[GP], bb[GP];
 #pragma unroll
-  for (int k = 0; k < kTpt; ++k) {
-    const int t = tid / 16 + (kThreads / 16) * k;
-    if (t < G) {
-      const float acc = ((sm.part[0][t][c1] + sm.part[1][t][c1]) + sm.part[2][t][c1]) + sm.part[3][t][c1];
-      st_any(out + (row + t) * D + d1, (acc + sm.sx[t][c1]) * sm.g[t][c1]);
+  for (int t4 = 0; t4 < GP / 4; ++t4) {
+    const float4 bq = *reinterpret_cast<const float4*>(&sm.b[n][t0 + 4 * t4]);
+    const float bq4[4] = {bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * t4 + i;
+      a[t] = fast_exp2(sm.dl[t0 + t][cl] * a2);
+      bb[t] = sm.u[t0 + t][cl] * bq4[i];
     }
   }
+  float y[GP], pf[GP], pr[GP];  // y: C_t (hf + hr); pf, pr: C_t times the forward / reverse product
+  float hf = 0.0f, qf = 1.0f;
+#pragma unroll
+  for (int t = 0; t < GP; ++t) {
+    hf = fmaf(a[t], hf, bb[t]);
+    qf *= a[t];
+    y[t] = fwd ? hf : 0.0f;
+    pf[t] = qf;
+  }
+  float hr = 0.0f, qr = 1.0f;
+#pragma unroll
+  for (int t = GP - 1; t >= 0; --t) {
+    hr = fmaf(a[t], hr, bb[t]);
+    qr *= a[t];
+    if (rev) y[t] += hr;
+    pr[t] = qr;
+  }
+#pragma unroll
+  for (int t4 = 0; t4 < GP / 4; ++t4) {
+    const float4 cq = *reinterpret_cast<const float4*>(&sm.c[n][t0 + 4 * t4]);
+    const float cq4[4] = {cq.x, cq.y, cq.z, cq.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * t4 + i;
+      y[t] *= cq4[i];
+      pf[t] *= cq4[i];
+      pr[t] *= cq4[i];
+    }
+  }
+  sm.prod[p][n][cl] = qf;
+  sm.fend[p][n][cl] = hf;
+  sm.rbeg[p][n][cl] = hr;
+  __syncthreads();
+
+  // phase 2: the entering states and each token's corrections
+  float hin_f = (n < N && h_in) ? hv : 0.0f;
+#pragma unroll
+  for (int q = 0; q < NQ - 1; ++q)
+    if (q < p) hin_f = fmaf(sm.prod[q][n][cl], hin_f, sm.fend[q][n][cl]);
+  float hin_r = 0.0f;
+#pragma unroll
+  for (int q = NQ - 1; q > 0; --q)
+    if (q > p) hin_r = fmaf(sm.prod[q][n][cl], hin_r, sm.rbeg[q][n][cl]);
+  if (!fwd) hin_f = 0.0f;
+  if (!rev) hin_r = 0.0f;
+#pragma unroll
+  for (int t = 0; t < GP; ++t) y[t] = quad_sum(fmaf(pf[t], hin_f, fmaf(pr[t], hin_r, y[t])));
+  if (p == NQ - 1 && h_out && n < N) {
+    // the forward state after the block's last token (padding leaves it unchanged); the entering state is
+    // formed again with the cache, whatever the forward readout flag
+    float h = h_in ? hv : 0.0f;
+#pragma unroll
+    for (int q = 0; q < NQ - 1; ++q) h = fmaf(sm.prod[q][n][cl], h, sm.fend[q][n][cl]);
+    h_out[(static_cast<size_t>(b) * D + d) * N + n] = fmaf(qf, h, hf);
+  }
+  if ((lane & 3) == 0) {
+#pragma unroll
+    for (int t = 0; t < GP; ++t) sm.part[wv][t0 + t][cl] = y[t];
+  }
+  __syncthreads();
+  block_store<T, GM, kThreads>(sm, out, G, D, b);
 }
 
 template <typename T, int GM>
 static void launch_block_gm(const ScanArgs& a, int batch, int G, int D, int N, hipStream_t stream) {
-  constexpr int HV = GM >= 32 ? 2 : 1;  // halves of 16 tokens or more
   const dim3 grid(static_cast<unsigned>(D / 16), static_cast<unsigned>(batch));
-  hipLaunchKernelGGL((k_block<T, GM, HV>), grid, dim3(256 * HV), 0, stream, static_cast<const T*>(a.x),
-                     static_cast<const T*>(a.dt), static_cast<const T*>(a.z), a.A, static_cast<const T*>(a.B),
-                     static_cast<const T*>(a.C), a.D, a.dt_bias, a.h_in, a.h_out, static_cast<T*>(a.out), G, D, N,
-                     static_cast<int>(a.flags));
+  if constexpr (GM == 32 || GM == 64) {
+    // parts of 16 tokens: two (512 threads) or four (1024 threads)
+    constexpr int NQ = GM / 16;
+    hipLaunchKernelGGL((k_block_parts<T, GM, NQ>), grid, dim3(256 * NQ), 0, stream, static_cast<const T*>(a.x),
+                       static_cast<const T*>(a.dt), static_cast<const T*>(a.z), a.A, static_cast<const T*>(a.B),
+                       static_cast<const T*>(a.C), a.D, a.dt_bias, a.h_in, a.h_out, static_cast<T*>(a.out), G, D,
+                       N, static_cast<int>(a.flags));
+  } else {
+    constexpr int HV = GM >= 32 ? 2 : 1;  // halves of 16 tokens or more
+    hipLaunchKernelGGL((k_block<T, GM, HV>), grid, dim3(256 * HV), 0, stream, static_cast<const T*>(a.x),
+                       static_cast<const T*>(a.dt), static_cast<const T*>(a.z), a.A, static_cast<const T*>(a.B),
+                       static_cast<const T*>(a.C), a.D, a.dt_bias, a.h_in, a.h_out, static_cast<T*>(a.out), G, D,
+                       N, static_cast<int>(a.flags));
+  }
 }
 
 template <typename T>
