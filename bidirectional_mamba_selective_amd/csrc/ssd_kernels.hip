@@ -44,6 +44,10 @@
 // LDS, issues the next step's loads, then computes; one wavefront forms the
 // next run's per-token terms at the end of the step.  Two workgroups fit on a
 // CU, so one computes while the other waits.
+//
+// Also here: the block-cache step in one kernel (k_ssd_block), and the
+// one-direction layers with the short convolution applied on load (k_ssd1_*),
+// each described at its definition.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -63,10 +63,13 @@ def _slice(dev, b0, b1):
     return {k: dev[k][:, b0:b1].contiguous() for k in ("x", "dt", "z", "B", "C")}
 
 
-@pytest.mark.parametrize("G", [1, 5, 16, 32, 64, 100, 128, 129, 200])
+@pytest.mark.parametrize("G", [1, 5, 16, 17, 31, 32, 48, 63, 64, 100, 128, 129, 200])
 @pytest.mark.parametrize("flags", [0, NO_GATE, FWD_ONLY, REV_ONLY | NO_GATE])
 def test_block_small(G, flags):
-    """One block with a random cached state; out and h_out against oracle.scan_block (fp32 I/O)."""
+    """One block with a random cached state; out and h_out against oracle.scan_block (fp32 I/O).  The sizes
+    cover each single-kernel form and its padding: one group (up to 16 tokens), parts of 16 tokens (17-31 and
+    32 in two parts, 48, 63 and 64 in four, with a whole part of padding at 48), halves (100, 128), and
+    the chunked path past 128."""
     import torch
 
     inp = _case(2, G, 128, 16, "f32", seed=G)
