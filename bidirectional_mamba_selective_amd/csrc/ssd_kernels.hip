@@ -242,6 +242,26 @@ __device__ __forceinline__ void put_xt(uint16_t* dst, uint4 v, int tid, const fl
   }
 }
 
+// An fp32 value as a pair of bf16 operands, hi = bf16(v) and lo = bf16(v - hi) (both rounded to nearest
+// even): hi + lo carries v to about 2^-17 relative, so a product taken as hi * b + lo * b on the matrix cores
+// loses no more than that to its operand's rounding (b exact in bf16).
+__device__ __forceinline__ uint16_t bf_rest(float v, uint16_t hi) { return to_bf(v - bf(hi)); }
+
+// put_xt's weighted copy as two tiles, the rounded values and their rounding residuals.
+__device__ __forceinline__ void put_xt_split(uint16_t* dst, uint16_t* dst_lo, uint4 v, int tid, const float* wtok) {
+  const int j = tid >> 2, pc = tid & 3;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const float f = wtok[j];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = bf(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)))) * f;
+    const uint16_t hi = to_bf(x);
+    const int o = sw128(8 * pc + e, j >> 3) + (j & 7);
+    dst[o] = hi;
+    dst_lo[o] = bf_rest(x, hi);
+  }
+}
+
 // Head states are held transposed (rows = state index n, columns = channel p)
 // in 16x16 accumulator tiles.  Tile (nb, tp) element r in lane l is
 // n = 16nb + 4(l/16) + r, p = 16tp + l%16; in memory a state is stored as
@@ -287,6 +307,29 @@ __device__ __forceinline__ void state_to_lds(const State& s, uint16_t* sHs, int 
       const uint32_t lo = static_cast<uint32_t>(to_bf(v[0])) | (static_cast<uint32_t>(to_bf(v[1])) << 16);
       const uint32_t hi = static_cast<uint32_t>(to_bf(v[2])) | (static_cast<uint32_t>(to_bf(v[3])) << 16);
       *reinterpret_cast<uint2*>(sHs + sw256(p, n0 >> 3) + (n0 & 7)) = make_uint2(lo, hi);
+    }
+}
+
+// state_to_lds as two copies, the rounded state (sHs) and its rounding residuals (sHr).
+__device__ __forceinline__ void state_to_lds_split(const State& s, uint16_t* sHs, uint16_t* sHr, int w, int l) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+      const f32x4 v = s.t[i][tp];
+      const int p = 16 * tp + (l & 15);
+      const int n0 = 16 * (2 * w + i) + 4 * (l >> 4);
+      uint16_t hb[4], rb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        hb[r] = to_bf(v[r]);
+        rb[r] = bf_rest(v[r], hb[r]);
+      }
+      const int o = sw256(p, n0 >> 3) + (n0 & 7);
+      *reinterpret_cast<uint2*>(sHs + o) = make_uint2(hb[0] | (static_cast<uint32_t>(hb[1]) << 16),
+                                                      hb[2] | (static_cast<uint32_t>(hb[3]) << 16));
+      *reinterpret_cast<uint2*>(sHr + o) = make_uint2(rb[0] | (static_cast<uint32_t>(rb[1]) << 16),
+                                                      rb[2] | (static_cast<uint32_t>(rb[3]) << 16));
     }
 }
 
@@ -729,7 +772,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_fsweep(Args a) {
 // block plus the block's own update.  Wavefront w owns output rows 16w..16w+15
 // and state row blocks 2w, 2w + 1, as in the sweeps.  The cache is read and
 // written in the caller's layout [batch, H, P, N]; each element is read and
-// written by the same lane, so h_out may be h_in.
+// written by the same lane, so h_out may be h_in.  The products whose operand
+// is not exact in bf16 (the decay-weighted C B^T of the intra-block product,
+// the cached state in its readout, the weighted x of the cache update) take
+// that operand as a rounded value and its rounding residual, two products
+// each, so the cache and the output before its own rounding keep fp32-level
+// accuracy (2^-16 of each term) over any number of chained blocks.
 // ---------------------------------------------------------------------------
 template <int DIRS>
 __global__ __launch_bounds__(kThreads, 2) void k_ssd_block(Args a) {
@@ -738,7 +786,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_block(Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t sBT[N * Q];
   __shared__ __attribute__((aligned(16))) uint16_t sXT[P * Q];
   __shared__ __attribute__((aligned(16))) uint16_t sXW[P * Q];
+  __shared__ __attribute__((aligned(16))) uint16_t sXWr[P * Q];  // rounding residuals of sXW
   __shared__ __attribute__((aligned(16))) uint16_t sHs[P * N];
+  __shared__ __attribute__((aligned(16))) uint16_t sHr[P * N];   // rounding residuals of sHs
   __shared__ __attribute__((aligned(16))) uint16_t sZ[4 * 16 * P];
   __shared__ __attribute__((aligned(16))) uint16_t sY[4 * 16 * P];
   __shared__ __attribute__((aligned(16))) float sTok[kTokRows * 64];
@@ -811,8 +861,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_block(Args a) {
   }
   const float* tok = sTok;
   put_xt(sXT, px, tid, nullptr, 1.0f);
-  if (kFwd) put_xt(sXW, px, tid, tok + kWf * 64, 1.0f);
-  if (kFwd) state_to_lds(H, sHs, w, l);
+  if (kFwd) put_xt_split(sXW, sXWr, px, tid, tok + kWf * 64);
+  if (kFwd) state_to_lds_split(H, sHs, sHr, w, l);
   __syncthreads();
 
   // 3. out.  W = mask o (C B^T) o delta_j for rows i = 16w + l16 as the A operand, k-slots permuted as in
@@ -830,11 +880,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_block(Args a) {
   f32x4 y[2] = {zero4(), zero4()};
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2) {
-    bf16x8 wa;
+    // the weights as rounded values and residuals (x is exact in bf16)
+    bf16x8 wa, wr;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      wa[r] = static_cast<__bf16>(gcur[2 * k2][r]);
-      wa[4 + r] = static_cast<__bf16>(gcur[2 * k2 + 1][r]);
+      const uint16_t h0 = to_bf(gcur[2 * k2][r]), h1 = to_bf(gcur[2 * k2 + 1][r]);
+      wa[r] = __builtin_bit_cast(__bf16, h0);
+      wa[4 + r] = __builtin_bit_cast(__bf16, h1);
+      wr[r] = __builtin_bit_cast(__bf16, bf_rest(gcur[2 * k2][r], h0));
+      wr[4 + r] = __builtin_bit_cast(__bf16, bf_rest(gcur[2 * k2 + 1][r], h1));
     }
     const int jlo = 32 * k2 + 4 * q4;
 #pragma unroll
@@ -842,12 +896,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_block(Args a) {
       const int p = 16 * tp + l16;
       const uint2 lo = *reinterpret_cast<const uint2*>(sXT + sw128(p, jlo >> 3) + (jlo & 7));
       const uint2 hi = *reinterpret_cast<const uint2*>(sXT + sw128(p, (jlo + 16) >> 3) + (jlo & 7));
-      y[tp] = mfma(wa, __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), y[tp]);
+      const bf16x8 xb = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      y[tp] = mfma(wr, xb, mfma(wa, xb, y[tp]));
     }
   }
   if (kFwd) {
-    f32x4 yf[2];
+    f32x4 yf[2], yr[2];
     readout(yf, cf, sHs, l);
+    readout(yr, cf, sHr, l);
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) yf[tp] += yr[tp];
     const f32x4 rf = *reinterpret_cast<const f32x4*>(tok + kRf * 64 + 16 * w + 4 * q4);
 #pragma unroll
     for (int tp = 0; tp < 2; ++tp)
@@ -879,6 +937,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ssd_block(Args a) {
   // 4. the new cache: the cached state decayed over the block plus the block's update
   if (kFwd && a.h_out) {
     state_update(H, ex(tok[kS * 64 + 63]), sBT, sXW, w, l);
+    state_update(H, 1.0f, sBT, sXWr, w, l);
 #pragma unroll
     for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll

@@ -90,6 +90,13 @@ BARS = {
     # up to ~6.4 % (one in 4 million) and single tokens' rows up to ~4.4 % of the output's rms
     "ssd": Bar(2e-2, 1e-1, _BF16_ROUND * 1.01, 8e-2),
     "ssd_state": Bar(1e-2, 1e-2, 1e-2, 2e-2),
+    # Mamba-2 cache of the single-kernel block step, whose products take each fp32 operand as two bf16 values:
+    # hi = bf16(v) within 2^-8 |v|, lo = bf16(v - hi) within 2^-8 |v - hi|, so each term of a 64-token
+    # increment is carried to 2^-16 of its size; for N(0,1) operands the sum of the terms' magnitudes is about
+    # 5x the rms of the sum, so an element's error stays under 2^-16 * 5 = 8e-5 of the rms (abs); normwise and
+    # per row the errors are independent across terms, far below that (measured over 256 chained blocks:
+    # 3.8e-6 normwise, 9.2e-6 per row, 3.4e-5 of the rms on single elements)
+    "ssd_split_state": Bar(1e-5, 3e-5, 2e-5, 8e-5),
 }
 
 

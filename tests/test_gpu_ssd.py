@@ -14,7 +14,14 @@ pytestmark = pytest.mark.gpu
 
 # Bars (tests/gpu_util.py BARS): "ssd" for the bf16 output (normwise and per token 2e-2, every element within
 # the rounding of its bf16 value plus a share of the output's rms that covers the bf16 operands of the matrix-core
-# products); "ssd_state" for the fp32 cache, whose increments are matrix-core products too.
+# products); "ssd_state" for the fp32 cache, whose increments are matrix-core products too.  A block of up to 64
+# tokens runs as one kernel whose products take each fp32 operand as a pair of bf16 values (the rounded value
+# and its residual), so its output is held to the "bf16" bars (its own rounding) and its cache to the
+# "ssd_split_state" bars.
+
+
+def _block_bars(G):
+    return ("bf16", "ssd_split_state") if G <= 64 else ("ssd", "ssd_state")
 
 
 def _inputs(batch, L, nh, seed=1):
@@ -130,8 +137,7 @@ def test_ssd_deterministic_and_staged():
 def test_ssd_block_step(G, flags):
     """One block with a random cached state (block-cache decoding, Section 4.3): out and the new cache
     against oracle.ssd_scan_block; flags 0 (both directions, gated), 1 (no gate), 2 (forward only).
-    The output is held to the "ssd" bars; the cache (carried in fp32, its increments formed by matrix-core
-    products) to the "ssd_state" bars."""
+    Bars by path (_block_bars): one kernel up to 64 tokens, the chunked kernels beyond."""
     import oracle
     from bidirectional_mamba_selective_amd import bimamba_ssd_block
 
@@ -150,8 +156,9 @@ def test_ssd_block_step(G, flags):
     want, want_h = oracle.ssd_scan_block(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
                                          inp["z"] if gate else None, inp["dt_bias"], h0, gate=gate,
                                          fwd=True, rev=not (flags & 2))
-    check(to_host64(out), want, "ssd", f"ssd block G={G} flags={flags} out")
-    check(to_host64(h_out), want_h, "ssd_state", f"ssd block G={G} flags={flags} cache")
+    out_bar, cache_bar = _block_bars(G)
+    check(to_host64(out), want, out_bar, f"ssd block G={G} flags={flags} out")
+    check(to_host64(h_out), want_h, cache_bar, f"ssd block G={G} flags={flags} cache")
 
 
 @pytest.mark.parametrize("G", [64, 96])
@@ -189,9 +196,10 @@ def test_ssd_block_chain_and_reruns(G):
         torch.cuda.synchronize()
         want, want_h = oracle.ssd_scan_block(hb["x"], hb["dt"], inp["A"], hb["B"], hb["C"], inp["D"], hb["z"],
                                              inp["dt_bias"], h_host)
-        check(to_host64(out), want, "ssd", f"ssd block chain G={G} block {k} out")
-        check(to_host64(h), want_h, "ssd_state", f"ssd block chain G={G} block {k} cache")
-        check(to_host64(out_f), full_f[:, sl], "ssd", f"ssd block chain G={G} block {k} forward vs full scan")
+        out_bar, cache_bar = _block_bars(G)
+        check(to_host64(out), want, out_bar, f"ssd block chain G={G} block {k} out")
+        check(to_host64(h), want_h, cache_bar, f"ssd block chain G={G} block {k} cache")
+        check(to_host64(out_f), full_f[:, sl], out_bar, f"ssd block chain G={G} block {k} forward vs full scan")
         h_host = want_h
 
 
@@ -223,7 +231,8 @@ def test_ssd_full_shape_ssm_only():
 def test_ssd_block_long_chain():
     """Block decoding over 256 blocks of 64 tokens (16384 tokens) with the cache committed in place after
     each block: the cache at every 16th boundary and every block's output against the oracle chained over the
-    same blocks, so a cache error that grew from block to block would fail.  8 heads (heads are independent)."""
+    same blocks, so a cache error that grew from block to block would fail.  8 heads (heads are independent).
+    64-token blocks run as one kernel: "ssd_split_state" bars for the cache, "bf16" for the output."""
     import oracle
     from bidirectional_mamba_selective_amd import bimamba_ssd_block
 
@@ -254,10 +263,10 @@ def test_ssd_block_long_chain():
         want[:, sl], h_host = oracle.ssd_scan_block(hb["x"], hb["dt"], inp["A"], hb["B"], hb["C"], inp["D"],
                                                     hb["z"], inp["dt_bias"], h_host)
         if k % 16 == 15:
-            r = check(to_host64(caches[k]), h_host, "ssd_state", f"ssd long chain cache after block {k}")
+            r = check(to_host64(caches[k]), h_host, "ssd_split_state", f"ssd long chain cache after block {k}")
             worst_cache = max(worst_cache, r["norm"])
     # every token row of every block (the per-row bar), and the sampled blocks against their own scale
-    check(got, want, "ssd", "ssd long chain, all blocks")
+    check(got, want, "bf16", "ssd long chain, all blocks")
     for k in (0, 127, 255):
-        check(got[:, k * G:(k + 1) * G], want[:, k * G:(k + 1) * G], "ssd", f"ssd long chain block {k}")
+        check(got[:, k * G:(k + 1) * G], want[:, k * G:(k + 1) * G], "bf16", f"ssd long chain block {k}")
     say(f"ssd long chain: worst cache normwise error over {nblk} blocks {worst_cache:.3e}")
