@@ -729,6 +729,15 @@ def main():
     ms_step = wall * 1e3 / args.steps
     ms_step_ev = ev0.elapsed_time(ev1) / args.steps
     log(f"timed {args.steps} steps: {ms_step:.4f} ms/step wall, {ms_step_ev:.4f} ms/step events")
+    # each call timed on its own (HIP events around it): the median and the minimum beside the mean
+    evp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evp:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_call = [e0.elapsed_time(e1) for e0, e1 in evp]
+    log(f"per call: median {np.median(per_call):.4f} ms, min {min(per_call):.4f} ms")
 
     # the general-A path on the same inputs (reported beside the headline)
     for _ in range(2):
@@ -844,6 +853,8 @@ def main():
                       "note": "A[d,n] = -(n+1)*(1+0.2*U(-1,1)): no per-channel geometric structure, one exp per "
                               "(token, channel, state) in each pass"},
         "ms_per_step_events": round(ms_step_ev, 4),
+        "ms_per_call_median": round(float(np.median(per_call)), 4),
+        "ms_per_call_min": round(float(min(per_call)), 4),
         "untied": {"ms_per_step": round(ms_step_untied, 4),
                    "tokens_per_s": round(tokens / (ms_step_untied * 1e-3), 1),
                    "note": "each direction its own x, dt, B, C, z, A, D, dt_bias and its own gated output "

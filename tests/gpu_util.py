@@ -104,9 +104,9 @@ def bar_for(kind):
     return BARS[kind]
 
 
-def check(got, want, kind, tag=""):
+def check(got, want, kind, tag="", quiet=False):
     """Assert every bar of BARS[kind] (kind may also be a Bar) for got against want (fp64 arrays of one
-    shape, rows along the last axis).  Returns the measured figures."""
+    shape, rows along the last axis).  Returns the measured figures; quiet leaves out the log line."""
     b = kind if isinstance(kind, Bar) else BARS[kind]
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
@@ -125,8 +125,9 @@ def check(got, want, kind, tag=""):
     allow = b.rel * np.abs(want) + b.abs * rms
     elem = float(np.max(np.abs(diff) / np.maximum(allow, 1e-300))) if want.size else 0.0
     res = {"norm": norm, "row": row, "elem": elem}
-    say(f"{tag}: normwise {norm:.3e} (bar {b.norm:.0e}), worst row {row:.3e} (bar {b.row:.0e}), "
-        f"worst element at {elem:.3f} of its bound")
+    if not quiet:
+        say(f"{tag}: normwise {norm:.3e} (bar {b.norm:.0e}), worst row {row:.3e} (bar {b.row:.0e}), "
+            f"worst element at {elem:.3f} of its bound")
     assert norm <= b.norm, f"{tag}: normwise rel err {norm:.3e} > {b.norm}"
     assert row <= b.row, f"{tag}: worst row rel err {row:.3e} > {b.row}"
     assert elem <= 1.0, f"{tag}: an element exceeds |o-r| <= {b.rel:.2e}|r| + {b.abs:.0e} rms (x{elem:.2f})"
