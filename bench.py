@@ -4,8 +4,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_64k_bf16]
 
 One step = one bimamba_scan_fwd call over the whole workload (summary, carry
-and output kernels), inputs already resident in HBM.  W untimed steps, then K
-timed steps bracketed by device synchronisations; one JSON line is printed.
+and output kernels), inputs already resident in HBM.  W untimed steps (continued
+until a quarter second of them has run, so that the shader clock has settled),
+then K timed steps bracketed by device synchronisations; one JSON line is
+printed.  The K steps timed after an idle second and W steps only are reported
+beside them (ms_per_step_after_idle).
 
 Besides the headline tokens/s the line carries:
   roofline      the output kernel (the dominant one) against the HBM roofline:
@@ -59,6 +62,28 @@ SSDCONV_PROFILE = os.path.join(ROOT, "profiles", "k_ssd1_conv_long_64k_bf16_traf
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# The shader clock drops whenever the GPU idles and climbs back over the first 10-15 calls of the
+# workload once work resumes (measured on MI355X at L = 65536: 1.86-2.15 ms per call right after half
+# a second of idle, 1.61-1.66 ms once settled).  Each timed region below therefore follows W untimed
+# steps continued until at least SETTLE_S seconds of them have run; the headline also reports the K
+# steps timed after an idle second and W steps only (ms_per_step_after_idle).
+SETTLE_S = 0.25
+
+
+def warm(fn, steps, torch, seconds=SETTLE_S):
+    """Run fn at least `steps` times and until `seconds` of them have run (synchronising every 8 calls so
+    that the host does not run ahead of the GPU); returns the number of calls."""
+    n = 0
+    t0 = time.perf_counter()
+    while n < steps or time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
 
 
 def algorithmic_bytes(batch, L, D, N, es):
@@ -316,7 +341,7 @@ def bench_block(args, w, torch, bm, I, dev):
             for b, o in zip(blk, outs):
                 bm.bimamba_scan_block(b["x"], b["dt"], A, b["B"], b["C"], Dv, b["z"], bias, h_in=h, h_out=h,
                                       out=o, workspace=ws, stream=gstream)
-    torch.cuda.synchronize()
+    warm(graph.replay, 3, torch)
     t_graph = []
     for r in range(max(3, args.steps)):
         h.zero_()
@@ -354,7 +379,7 @@ def bench_block(args, w, torch, bm, I, dev):
             with torch.cuda.graph(g2, stream=gs):
                 for _ in range(200):
                     one(gs)
-        torch.cuda.synchronize()
+        warm(g2.replay, 3, torch)
         ts = []
         for _ in range(3):
             o.zero_()
@@ -410,6 +435,10 @@ def bench_batched(args, torch, bm, I, dev, stream, calls=128):
     need = bm.bimamba_scan_fwd_workspace_bytes(w.batch, w.seqlen, w.d_inner, w.d_state)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     out = torch.empty(shp, dtype=torch.bfloat16, device=dev)
+    xz = I.device_normals({"x": shp, "z": shp}, seed=999, io_dtype=w.io_dtype, device=dev)
+    warm(lambda: bm.bimamba_scan_fwd(xz["x"], fixed["dt"], A, fixed["B"], fixed["C"], Dv, xz["z"], bias, out=out,
+                                     workspace=ws, stream=stream), 2, torch)
+    del xz
     ms = []
     for s in range(calls + 2):
         xz = I.device_normals({"x": shp, "z": shp}, seed=1000 + s, io_dtype=w.io_dtype, device=dev)
@@ -457,9 +486,7 @@ def bench_ssd(args, torch, bm, I, dev, stream):
     def step():
         bm.bimamba_ssd_fwd(*args_t, out=out, workspace=ws, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm(step, args.warmup, torch)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -467,7 +494,7 @@ def bench_ssd(args, torch, bm, I, dev, stream):
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     names = ("k_ssd_stage", "k_ssd_rsweep", "k_ssd_carry", "k_ssd_fsweep")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    warm(step, args.warmup, torch)
     for s_ in range(args.steps):
         e = evs[s_]
         e[0].record(stream)
@@ -535,7 +562,7 @@ def ssd_block_latency(torch, bm, I, dev, w, A, Dv, bias):
             with torch.cuda.graph(g, stream=gs):
                 for _ in range(100):
                     one(gs)
-        torch.cuda.synchronize()
+        warm(g.replay, 3, torch)
         ts = []
         for _ in range(3):
             o.zero_()
@@ -585,9 +612,7 @@ def bench_ssd_conv(args, torch, bm, I, dev, stream):
                                    out_f=out_f, out_r=out_r, workspace=ws, stream=stream)
 
     def timed(fn):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
+        warm(fn, 2, torch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
@@ -633,9 +658,7 @@ def bench_conv(args, torch, bm, I, dev, stream):
     def step():
         bm.bimamba_conv1d_bidir(u, w_f, b_f, w_r, b_r, out_f=out_f, out_r=out_r, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm(step, args.warmup, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
@@ -711,24 +734,33 @@ def main():
     def step(a_mat=A):
         bm.bimamba_scan_fwd(x, dt, a_mat, B, C, Dv, z, bias, out=out, workspace=ws, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
-
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+
+    def timed_steps():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, ev0.elapsed_time(ev1) / args.steps
+
+    # the same K steps after an idle second and only W warmup steps (the clock still climbing)
+    for _ in range(max(args.warmup, 1)):
         step()
-    ev1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    ms_step_ev = ev0.elapsed_time(ev1) / args.steps
-    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step wall, {ms_step_ev:.4f} ms/step events")
+    time.sleep(1.0)
+    for _ in range(args.warmup):
+        step()
+    ms_step_idle, _ = timed_steps()
+    log(f"after an idle second and {args.warmup} warmup steps: {ms_step_idle:.4f} ms/step")
+
+    nwarm = warm(step, args.warmup, torch)
+    ms_step, ms_step_ev = timed_steps()
+    log(f"warmup {nwarm} steps; timed {args.steps} steps: {ms_step:.4f} ms/step wall, {ms_step_ev:.4f} ms/step "
+        f"events")
     # each call timed on its own (HIP events around it): the median and the minimum beside the mean
     evp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for e0, e1 in evp:
@@ -740,9 +772,7 @@ def main():
     log(f"per call: median {np.median(per_call):.4f} ms, min {min(per_call):.4f} ms")
 
     # the general-A path on the same inputs (reported beside the headline)
-    for _ in range(2):
-        step(A_gen)
-    torch.cuda.synchronize()
+    warm(lambda: step(A_gen), 2, torch)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(A_gen)
@@ -764,9 +794,7 @@ def main():
     def step_untied():
         bm.bimamba_scan_fwd_untied(fwd_set, rev_set, out_f=out, out_r=out_r, workspace=ws, stream=stream)
 
-    for _ in range(2):
-        step_untied()
-    torch.cuda.synchronize()
+    warm(step_untied, 2, torch)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step_untied()
@@ -777,7 +805,7 @@ def main():
     # per-kernel attribution on the same stream: staged entry point, events between stages
     names = ("k_summary", "k_carry", "k_output")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    warm(step, args.warmup, torch)
     for s in range(args.steps):
         e = evs[s]
         e[0].record(stream)
@@ -835,6 +863,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": nwarm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -853,6 +882,7 @@ def main():
                       "note": "A[d,n] = -(n+1)*(1+0.2*U(-1,1)): no per-channel geometric structure, one exp per "
                               "(token, channel, state) in each pass"},
         "ms_per_step_events": round(ms_step_ev, 4),
+        "ms_per_step_after_idle": round(ms_step_idle, 4),
         "ms_per_call_median": round(float(np.median(per_call)), 4),
         "ms_per_call_min": round(float(min(per_call)), 4),
         "untied": {"ms_per_step": round(ms_step_untied, 4),
