@@ -1,5 +1,6 @@
 """Parity at sizes where every activation tensor exceeds 4 GiB (byte offsets past 32 bits: tile bases,
-boundary states, outputs) and, for the convolution, at the largest channel count the library accepts.
+boundary states, outputs), and at the largest sizes the library accepts: the convolution's channel count,
+the scan's d_inner (chunked call and block step) and the Mamba-2 head count.
 
 The activations are drawn on the device (`inputs.device_normals`: the recipe's distributions, torch's
 seeded generator, rounded once to the I/O dtype), since drawing 10^10 values on the host would take
@@ -101,3 +102,87 @@ def test_ssd_tensors_over_4gib():
     say("ssd over 4 GiB: oracle on 2 heads")
     want = oracle.ssd_scan_fwd(hx, hdt, A[heads], hB, hC, Dv[heads], hz, bias[heads])
     check(got, want, "ssd", "ssd over 4 GiB")
+
+
+# The largest d_inner the scan accepts for an I/O dtype and state size: a tile of 16 token rows, and the
+# d_state rows of fp32 states at a tile boundary, each just under 2^31 bytes (the range of one buffer
+# resource).  fp32 with 16 states: 16 * d * 4 <= 2^31 - 1 and 16 * d * 4 + 256 <= 2^31 - 1; bf16 with 8
+# states: 16 * d * 2 and 8 * d * 4 (+ 256).  d_inner is the largest multiple of 64 under both.
+_MAX_CASES = [("f32", 16, 33554368), ("bf16", 8, 67108800)]
+
+
+@pytest.mark.parametrize("io, N, D", _MAX_CASES, ids=[f"{c[0]}-N{c[1]}" for c in _MAX_CASES])
+def test_scan_max_channels(io, N, D):
+    """At the largest accepted d_inner, L = 20 (one chunk: a full tile and a ragged one): the chunked call,
+    then the block step over the same 20 tokens from a random cache, on 14 channels including the last
+    wavefront's, against the oracle (out, and the new cache)."""
+    import oracle
+    from bidirectional_mamba_selective_amd import bimamba_scan_block, bimamba_scan_fwd
+
+    torch = torch_mod()
+    es = 4 if io == "f32" else 2
+    assert 16 * D * es <= 2**31 - 1 and N * D * 4 + 256 <= 2**31 - 1 and D % 64 == 0
+    assert 16 * (D + 64) * es > 2**31 - 1 or N * (D + 64) * 4 + 256 > 2**31 - 1  # the next size is refused
+    L = 20
+    say(f"scan at the largest d_inner: {io} N {N} D {D} L {L}: drawing inputs on the device")
+    act = I.device_normals({"x": (1, L, D), "dt": (1, L, D), "z": (1, L, D), "B": (1, L, N), "C": (1, L, N),
+                            "h": (1, D, N)}, seed=24, io_dtype=io, scales={"dt": 0.5})
+    h_in = act.pop("h").float()
+    A, Dv, bias = I.make_params(D, N)
+    Ad, Dd, bd = f32_dev(A), f32_dev(Dv), f32_dev(bias)
+    chan = np.array([0, 1, 63, 64, 65, 1 << 20, D // 2, D // 2 + 1, 12345678, D - 65, D - 64, D - 63, D - 2, D - 1])
+    ci = torch.from_numpy(chan).cuda()
+    hx, hdt, hz = (_host(act[k][:, :, ci]) for k in ("x", "dt", "z"))
+    hB, hC = _host(act["B"]), _host(act["C"])
+    hh = h_in[:, ci, :].double().cpu().numpy()
+
+    say(f"scan at the largest d_inner ({io}): chunked call")
+    out = bimamba_scan_fwd(act["x"], act["dt"], Ad, act["B"], act["C"], Dd, act["z"], bd)
+    torch.cuda.synchronize()
+    got = to_host64(out[:, :, ci])
+    del out
+    torch.cuda.empty_cache()
+    bar = "f32" if io == "f32" else "bf16"
+    check(got, oracle.scan_fwd(hx, hdt, A[chan], hB, hC, Dv[chan], hz, bias[chan]), bar,
+          f"scan at d_inner {D} ({io}, N {N})")
+
+    say(f"scan at the largest d_inner ({io}): block step")
+    h_out = torch.empty_like(h_in)
+    out = bimamba_scan_block(act["x"], act["dt"], Ad, act["B"], act["C"], Dd, act["z"], bd, h_in=h_in, h_out=h_out)
+    torch.cuda.synchronize()
+    got = to_host64(out[:, :, ci])
+    got_h = h_out[:, ci, :].double().cpu().numpy()
+    del out, h_out, h_in, act
+    torch.cuda.empty_cache()
+    want, want_h = oracle.scan_block(hx, hdt, A[chan], hB, hC, Dv[chan], hz, bias[chan], h_in=hh)
+    check(got, want, bar, f"block step at d_inner {D} ({io}, N {N})")
+    check(got_h, want_h, "state", f"block cache at d_inner {D} ({io}, N {N})")
+
+
+def test_ssd_max_heads():
+    """Mamba-2 at the largest head count accepted (2^18 heads of 32 channels), L = 70 (a run and a ragged
+    one): a run's output rows span 1 GiB of one buffer resource, the chunk states 8 GiB; 9 heads including
+    the last ones against the oracle."""
+    import oracle
+    from bidirectional_mamba_selective_amd import bimamba_ssd_fwd
+
+    torch = torch_mod()
+    H, Pd, N, L = 1 << 18, 32, 128, 70
+    say(f"ssd at the largest head count: {H} heads, L {L}: drawing inputs on the device")
+    act = I.device_normals({"x": (1, L, H * Pd), "dt": (1, L, H), "z": (1, L, H * Pd), "B": (1, L, N),
+                            "C": (1, L, N)}, seed=25, io_dtype="bf16", scales={"dt": 0.5})
+    A, Dv, bias = I.make_ssd_params(H)
+    out = bimamba_ssd_fwd(act["x"], act["dt"], f32_dev(A), act["B"], act["C"], f32_dev(Dv), act["z"], f32_dev(bias))
+    torch.cuda.synchronize()
+    heads = np.array([0, 1, 7, 8, H // 2 - 1, H // 2, H - 8, H - 2, H - 1])
+    cols = np.concatenate([np.arange(h * Pd, (h + 1) * Pd) for h in heads])
+    ci, hi = torch.from_numpy(cols).cuda(), torch.from_numpy(heads).cuda()
+    got = to_host64(out[:, :, ci])
+    hx, hz = _host(act["x"][:, :, ci]), _host(act["z"][:, :, ci])
+    hdt = _host(act["dt"][:, :, hi])
+    hB, hC = _host(act["B"]), _host(act["C"])
+    del out, act
+    torch.cuda.empty_cache()
+    say("ssd at the largest head count: oracle on 9 heads")
+    want = oracle.ssd_scan_fwd(hx, hdt, A[heads], hB, hC, Dv[heads], hz, bias[heads])
+    check(got, want, "ssd", f"ssd at {H} heads")
