@@ -224,6 +224,50 @@ def test_batched_workload_calls():
         check(out, want, w.io_dtype, f"batched call {s}")
 
 
+# The oracle's inputs for test_batched_call_full_width, set before the worker processes are forked (they
+# inherit them copy-on-write and touch no GPU) and cleared afterwards.
+_SHARD = {}
+
+
+def _oracle_shard(chan):
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    s = _SHARD
+    with threadpool_limits(1):
+        return chan, oracle.scan_fwd(s["x"][:, :, chan], s["dt"][:, :, chan], s["A"][chan], s["B"], s["C"],
+                                     s["D"][chan], s["z"][:, :, chan], s["dt_bias"][chan])
+
+
+def test_batched_call_full_width():
+    """Denoising call 0 of the batched workload (batch 8, L 8192, d_inner 2048, bf16; x, z seeded 1000) over
+    its whole output, 134 million elements, against the oracle run on the host in channel shards (exact: a
+    channel's output depends only on that channel and the shared B, C) by up to 8 worker processes."""
+    import multiprocessing as mp
+    import os
+
+    from tests.gpu_util import run_fwd
+
+    w = I.WORKLOADS["batched_8k_bf16"]
+    A, Dv, bias = I.make_params(w.d_inner, w.d_state)
+    inp = I.make_activations(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype, seed=1, xz_seed=1000)
+    inp.update(A=A, D=Dv, dt_bias=bias)
+    say("batched call 0, full width: running on the GPU")
+    got = to_host64(run_fwd(upload(inp, w.io_dtype)))
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    say(f"batched call 0, full width: oracle on {w.d_inner} channels in {workers} processes")
+    _SHARD.clear()
+    _SHARD.update(inp)
+    want = np.empty_like(got)
+    try:
+        with mp.get_context("fork").Pool(workers) as pool:
+            for chan, part in pool.imap_unordered(_oracle_shard, np.array_split(np.arange(w.d_inner), 4 * workers)):
+                want[:, :, chan] = part
+    finally:
+        _SHARD.clear()
+    check(got, want, w.io_dtype, "batched call 0 (all 8 x 8192 x 2048 outputs)")
+
+
 def test_batched_workload_all_calls_channel_subset():
     """All 128 denoising calls of the batched workload (batch 8, L 8192, d_inner 2048, bf16), each with fresh
     x and z drawn on the device (torch's generator seeded 1000 + call; dt, B, C drawn once), one workspace
