@@ -134,6 +134,38 @@ def check(got, want, kind, tag="", quiet=False):
     return res
 
 
+# The inputs of oracle_sharded's worker processes: set before the workers are forked (they inherit them
+# copy-on-write, run numpy only and touch no GPU) and cleared afterwards.
+_SHARD = {}
+
+
+def _shard_call(chan):
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(1):
+        return chan, _SHARD["fn"](_SHARD["inp"], chan)
+
+
+def oracle_sharded(fn, inp, nchan, out_shape, workers=8):
+    """fn(inp, chan) -> the oracle's output on channels `chan` (the last axis), run over all nchan channels in
+    shards by up to `workers` forked host processes.  Exact: a channel's output depends only on that channel
+    and the shared B, C (the oracle pin on channel independence)."""
+    import multiprocessing as mp
+    import os
+
+    nw = max(1, min(workers, len(os.sched_getaffinity(0))))
+    out = np.empty(out_shape)
+    _SHARD.clear()
+    _SHARD.update(fn=fn, inp=inp)
+    try:
+        with mp.get_context("fork").Pool(nw) as pool:
+            for chan, part in pool.imap_unordered(_shard_call, np.array_split(np.arange(nchan), 4 * nw)):
+                out[..., chan] = part
+    finally:
+        _SHARD.clear()
+    return out
+
+
 def upload(inp, io_dtype):
     """Device tensors for one input dict of fp32 arrays (exact in io_dtype)."""
     dev = {}

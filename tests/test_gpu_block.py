@@ -206,6 +206,50 @@ def test_block_sweep_workload():
             _check_quiet(got_h[i], want_h[i])
 
 
+def _oracle_sweep(inp, chan, G):
+    """The oracle's block sweep on channels chan: blocks of G tokens chained through the forward cache.
+    Returns [batch, L + N, len(chan)]: the outputs, then the final cache with its state axis first."""
+    hh = None
+    L = inp["x"].shape[1]
+    out = np.empty(inp["x"].shape[:2] + (len(chan),))
+    for b0 in range(0, L, G):
+        sl = {k: inp[k][:, b0:b0 + G] for k in ("x", "dt", "z", "B", "C")}
+        o, hh = oracle.scan_block(sl["x"][:, :, chan], sl["dt"][:, :, chan], inp["A"][chan], sl["B"], sl["C"],
+                                  inp["D"][chan], sl["z"][:, :, chan], inp["dt_bias"][chan], hh)
+        out[:, b0:b0 + G] = o
+    return np.concatenate([out, hh.transpose(0, 2, 1)], axis=1)
+
+
+def test_block_sweep_full_width():
+    """The block workload's 1024-block sweep (L 32768, d_inner 4096, blocks of 32, the cache committed in place)
+    over its whole output, every token of every channel, against the oracle's sweep run on the host in
+    channel shards; and the final cache over every channel and state."""
+    import torch
+
+    from bidirectional_mamba_selective_amd import bimamba_scan_block
+    from tests.gpu_util import oracle_sharded
+
+    w = I.WORKLOADS["block_32k_bf16"]
+    G = w.block_len
+    inp = _case(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype)
+    dev = upload(inp, w.io_dtype)
+    h = torch.zeros(w.batch, w.d_inner, w.d_state, device="cuda")
+    outs = torch.empty_like(dev["x"])
+    say("block sweep full width: 1024 GPU calls")
+    for b0 in range(0, w.seqlen, G):
+        sl = _slice(dev, b0, b0 + G)
+        outs[:, b0:b0 + G] = bimamba_scan_block(sl["x"], sl["dt"], dev["A"], sl["B"], sl["C"], dev["D"], sl["z"],
+                                                dev["dt_bias"], h_in=h, h_out=h)
+    torch.cuda.synchronize()
+    got = to_host64(outs)
+    got_h = to_host64(h)
+    say(f"block sweep full width: oracle on {w.d_inner} channels in host processes")
+    both = oracle_sharded(lambda d, c: _oracle_sweep(d, c, G), inp, w.d_inner,
+                          (w.batch, w.seqlen + w.d_state, w.d_inner))
+    check(got, both[:, :w.seqlen], w.io_dtype, f"block sweep (all {w.seqlen} x {w.d_inner} outputs)")
+    check(got_h, both[:, w.seqlen:].transpose(0, 2, 1), "state", "block sweep final cache (all channels and states)")
+
+
 def test_batched_workload_calls():
     """batch 8, L 8192, d_inner 2048, d_state 16, bf16: denoising calls 0, 63 and 127, each with fresh
     seeded x and z (seed 1000 + call) and fixed dt, B, C, A, D, dt_bias; channel-subset oracle."""
@@ -224,29 +268,11 @@ def test_batched_workload_calls():
         check(out, want, w.io_dtype, f"batched call {s}")
 
 
-# The oracle's inputs for test_batched_call_full_width, set before the worker processes are forked (they
-# inherit them copy-on-write and touch no GPU) and cleared afterwards.
-_SHARD = {}
-
-
-def _oracle_shard(chan):
-    import oracle
-    from threadpoolctl import threadpool_limits
-
-    s = _SHARD
-    with threadpool_limits(1):
-        return chan, oracle.scan_fwd(s["x"][:, :, chan], s["dt"][:, :, chan], s["A"][chan], s["B"], s["C"],
-                                     s["D"][chan], s["z"][:, :, chan], s["dt_bias"][chan])
-
-
 def test_batched_call_full_width():
     """Denoising call 0 of the batched workload (batch 8, L 8192, d_inner 2048, bf16; x, z seeded 1000) over
     its whole output, 134 million elements, against the oracle run on the host in channel shards (exact: a
     channel's output depends only on that channel and the shared B, C) by up to 8 worker processes."""
-    import multiprocessing as mp
-    import os
-
-    from tests.gpu_util import run_fwd
+    from tests.gpu_util import oracle_sharded, run_fwd
 
     w = I.WORKLOADS["batched_8k_bf16"]
     A, Dv, bias = I.make_params(w.d_inner, w.d_state)
@@ -254,17 +280,8 @@ def test_batched_call_full_width():
     inp.update(A=A, D=Dv, dt_bias=bias)
     say("batched call 0, full width: running on the GPU")
     got = to_host64(run_fwd(upload(inp, w.io_dtype)))
-    workers = max(1, min(8, len(os.sched_getaffinity(0))))
-    say(f"batched call 0, full width: oracle on {w.d_inner} channels in {workers} processes")
-    _SHARD.clear()
-    _SHARD.update(inp)
-    want = np.empty_like(got)
-    try:
-        with mp.get_context("fork").Pool(workers) as pool:
-            for chan, part in pool.imap_unordered(_oracle_shard, np.array_split(np.arange(w.d_inner), 4 * workers)):
-                want[:, :, chan] = part
-    finally:
-        _SHARD.clear()
+    say(f"batched call 0, full width: oracle on {w.d_inner} channels in host processes")
+    want = oracle_sharded(lambda d, c: oracle_fwd(d, chan=c), inp, w.d_inner, got.shape)
     check(got, want, w.io_dtype, "batched call 0 (all 8 x 8192 x 2048 outputs)")
 
 

@@ -162,6 +162,21 @@ def test_long_64k_workload():
     check_variants(inp, w.io_dtype, variants=VARIANTS[:2], chan=chan, tag="long_64k")
 
 
+@pytest.mark.parametrize("name", ["layer_2k_bf16", "long_64k_bf16"])
+def test_workload_full_width(name):
+    """The layer-2k and long workloads (the long one is the benchmarked launch) over their whole outputs,
+    every token of every channel, against the oracle run on the host in channel shards."""
+    from tests.gpu_util import oracle_sharded
+
+    w = I.WORKLOADS[name]
+    say(f"{name} full width: generating inputs")
+    inp = case(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype)
+    got = to_host64(run_fwd(upload(inp, w.io_dtype)))
+    say(f"{name} full width: oracle on {w.d_inner} channels in host processes")
+    want = oracle_sharded(lambda d, c: oracle_fwd(d, chan=c), inp, w.d_inner, got.shape)
+    check(got, want, w.io_dtype, f"{name} (all {w.seqlen} x {w.d_inner} outputs)")
+
+
 def test_long_64k_general_A():
     """The L = 65536 launch with A off the geometric structure (general exponential path)."""
     w = I.WORKLOADS["long_64k_bf16"]
