@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from bidirectional_mamba_selective_amd import inputs as I
-from tests.gpu_util import check, f32_dev, say, to_host64, torch_mod
+from tests.gpu_util import check, f32_dev, say, ssd_magnitudes, to_host64, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -101,7 +101,8 @@ def test_ssd_tensors_over_4gib():
     torch.cuda.empty_cache()
     say("ssd over 4 GiB: oracle on 2 heads")
     want = oracle.ssd_scan_fwd(hx, hdt, A[heads], hB, hC, Dv[heads], hz, bias[heads])
-    check(got, want, "ssd", "ssd over 4 GiB")
+    mag = ssd_magnitudes(hx, hdt, A[heads], hB, hC, Dv[heads], hz, bias[heads])
+    check(got, want, "ssd", "ssd over 4 GiB", mag=mag)
 
 
 # The largest d_inner the scan accepts for an I/O dtype and state size: a tile of 16 token rows, and the
@@ -185,4 +186,5 @@ def test_ssd_max_heads():
     torch.cuda.empty_cache()
     say("ssd at the largest head count: oracle on 9 heads")
     want = oracle.ssd_scan_fwd(hx, hdt, A[heads], hB, hC, Dv[heads], hz, bias[heads])
-    check(got, want, "ssd", f"ssd at {H} heads")
+    mag = ssd_magnitudes(hx, hdt, A[heads], hB, hC, Dv[heads], hz, bias[heads])
+    check(got, want, "ssd", f"ssd at {H} heads", mag=mag)

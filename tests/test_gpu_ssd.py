@@ -8,13 +8,13 @@ import numpy as np
 import pytest
 
 from bidirectional_mamba_selective_amd import inputs
-from tests.gpu_util import check, f32_dev, say, to_dev, to_host64, torch_mod
+from tests.gpu_util import check, f32_dev, say, ssd_magnitudes, to_dev, to_host64, torch_mod
 
 pytestmark = pytest.mark.gpu
 
-# Bars (tests/gpu_util.py BARS): "ssd" for the bf16 output (normwise and per token 2e-2, every element within
-# the rounding of its bf16 value plus a share of the output's rms that covers the bf16 operands of the matrix-core
-# products); "ssd_state" for the fp32 cache, whose increments are matrix-core products too.  A block of up to 64
+# Bars (tests/gpu_util.py BARS): "ssd" for the bf16 output (normwise 2e-2, every element within the rounding of
+# its bf16 value plus three bf16 roundings of the sum of the magnitudes of its terms, which the matrix-core
+# products' bf16 operands cost); "ssd_state" for the fp32 cache, whose increments are matrix-core products too.  A block of up to 64
 # tokens runs as one kernel whose products take each fp32 operand as a pair of bf16 values (the rounded value
 # and its residual), so its output is held to the "bf16" bars (its own rounding) and its cache to the
 # "ssd_split_state" bars.
@@ -58,13 +58,23 @@ def _oracle(inp, heads=None, gate=True, fwd=True, rev=True, use_D=True, use_bias
                                inp["dt_bias"][hs] if use_bias else None, gate=gate, fwd=fwd, rev=rev), cols
 
 
+def _mag(inp, heads=None, gate=True, fwd=True, rev=True, use_D=True, use_bias=True):
+    """The magnitudes of each output element's terms (ssd_magnitudes) on the heads _oracle compares."""
+    nh = inp["A"].shape[0]
+    hs = list(range(nh)) if heads is None else list(heads)
+    cols = np.concatenate([np.arange(h * 32, (h + 1) * 32) for h in hs])
+    return ssd_magnitudes(inp["x"][:, :, cols], inp["dt"][:, :, hs], inp["A"][hs], inp["B"], inp["C"],
+                          inp["D"][hs] if use_D else None, inp["z"][:, :, cols] if gate else None,
+                          inp["dt_bias"][hs] if use_bias else None, gate=gate, fwd=fwd, rev=rev)
+
+
 @pytest.mark.parametrize("batch,L,nh", [(1, 64, 2), (1, 1, 3), (2, 200, 3), (1, 513, 4), (1, 1100, 2), (2, 4160, 2)])
 def test_ssd_small_full_compare(batch, L, nh):
     say(f"ssd parity batch={batch} L={L} heads={nh}")
     inp = _inputs(batch, L, nh)
     got = _run(_upload(inp))
     want, _ = _oracle(inp)
-    check(got, want, "ssd", f"ssd batch={batch} L={L} heads={nh}")
+    check(got, want, "ssd", f"ssd batch={batch} L={L} heads={nh}", mag=_mag(inp))
 
 
 @pytest.mark.parametrize("flags,kw", [
@@ -78,7 +88,7 @@ def test_ssd_flags(flags, kw):
     inp = _inputs(1, 777, 3, seed=5)
     got = _run(_upload(inp), flags=flags, use_z=kw.get("gate", True))
     want, _ = _oracle(inp, **kw)
-    check(got, want, "ssd", f"ssd flags={flags}")
+    check(got, want, "ssd", f"ssd flags={flags}", mag=_mag(inp, **kw))
 
 
 def test_ssd_optional_params():
@@ -86,7 +96,7 @@ def test_ssd_optional_params():
     inp = _inputs(1, 300, 2, seed=6)
     got = _run(_upload(inp), use_D=False, use_bias=False)
     want, _ = _oracle(inp, use_D=False, use_bias=False)
-    check(got, want, "ssd", "ssd D=None dt_bias=None")
+    check(got, want, "ssd", "ssd D=None dt_bias=None", mag=_mag(inp, use_D=False, use_bias=False))
 
 
 def test_ssd_delta_to_zero_limit():
@@ -109,7 +119,27 @@ def test_ssd_all_heads_sampled(L):
     assert np.all(np.isfinite(got))
     for heads in (([0], [57], [119]) if L < 50000 else ([0], [119])):
         want, cols = _oracle(inp, heads=heads)
-        check(got[:, :, cols], want, "ssd", f"ssd L={L} head {heads[0]}")
+        check(got[:, :, cols], want, "ssd", f"ssd L={L} head {heads[0]}", mag=_mag(inp, heads=heads))
+
+
+def test_ssd_full_width():
+    """All 120 heads at L = 65536 over the whole output (251 million values) against the oracle run on the
+    host in shards of heads, by worker processes (heads are independent given the shared B, C)."""
+    from tests.gpu_util import oracle_sharded
+
+    L, H, Pd = 65536, 120, 32
+    say(f"ssd full width: {H} heads L={L}")
+    inp = _inputs(1, L, H, seed=2)
+    got = _run(_upload(inp))
+
+    def heads_last(d, hs):
+        # the oracle's output and the magnitudes of its terms, heads on the last axis
+        pair = np.stack([_oracle(d, heads=hs)[0], _mag(d, heads=hs)])
+        return pair.reshape(2, 1, L, len(hs), Pd).transpose(0, 1, 2, 4, 3)
+
+    say("ssd full width: oracle on 120 heads in host processes")
+    pair = oracle_sharded(heads_last, inp, H, (2, 1, L, Pd, H)).transpose(0, 1, 2, 4, 3).reshape(2, 1, L, H * Pd)
+    check(got, pair[0], "ssd", f"ssd (all {L} x {H * Pd} outputs)", mag=pair[1])
 
 
 def test_ssd_deterministic_and_staged():
@@ -156,9 +186,12 @@ def test_ssd_block_step(G, flags):
     want, want_h = oracle.ssd_scan_block(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
                                          inp["z"] if gate else None, inp["dt_bias"], h0, gate=gate,
                                          fwd=True, rev=not (flags & 2))
+    m_out, m_h = ssd_magnitudes(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                inp["z"] if gate else None, inp["dt_bias"], h0, gate=gate, fwd=True,
+                                rev=not (flags & 2))
     out_bar, cache_bar = _block_bars(G)
-    check(to_host64(out), want, out_bar, f"ssd block G={G} flags={flags} out")
-    check(to_host64(h_out), want_h, cache_bar, f"ssd block G={G} flags={flags} cache")
+    check(to_host64(out), want, out_bar, f"ssd block G={G} flags={flags} out", mag=m_out)
+    check(to_host64(h_out), want_h, cache_bar, f"ssd block G={G} flags={flags} cache", mag=m_h)
 
 
 @pytest.mark.parametrize("G", [64, 96])
@@ -179,6 +212,9 @@ def test_ssd_block_chain_and_reruns(G):
     h_host = None
     full_f = oracle.ssd_scan_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], None, None, inp["dt_bias"],
                                  gate=False, fwd=True, rev=False)
+    mag_f = ssd_magnitudes(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], None, None, inp["dt_bias"],
+                           gate=False, fwd=True, rev=False)
+    mh_host = np.zeros((nb, nh, 32, 128))
     for k in range(nblk):
         sl = slice(k * G, (k + 1) * G)
         bl = {key: dev[key][:, sl].contiguous() for key in ("x", "dt", "z", "B", "C")}
@@ -196,11 +232,14 @@ def test_ssd_block_chain_and_reruns(G):
         torch.cuda.synchronize()
         want, want_h = oracle.ssd_scan_block(hb["x"], hb["dt"], inp["A"], hb["B"], hb["C"], inp["D"], hb["z"],
                                              inp["dt_bias"], h_host)
+        m_out, m_h = ssd_magnitudes(hb["x"], hb["dt"], inp["A"], hb["B"], hb["C"], inp["D"], hb["z"],
+                                    inp["dt_bias"], mh_host)
         out_bar, cache_bar = _block_bars(G)
-        check(to_host64(out), want, out_bar, f"ssd block chain G={G} block {k} out")
-        check(to_host64(h), want_h, cache_bar, f"ssd block chain G={G} block {k} cache")
-        check(to_host64(out_f), full_f[:, sl], out_bar, f"ssd block chain G={G} block {k} forward vs full scan")
-        h_host = want_h
+        check(to_host64(out), want, out_bar, f"ssd block chain G={G} block {k} out", mag=m_out)
+        check(to_host64(h), want_h, cache_bar, f"ssd block chain G={G} block {k} cache", mag=m_h)
+        check(to_host64(out_f), full_f[:, sl], out_bar, f"ssd block chain G={G} block {k} forward vs full scan",
+              mag=mag_f[:, sl])
+        h_host, mh_host = want_h, m_h
 
 
 def test_ssd_full_shape_ssm_only():
@@ -225,7 +264,9 @@ def test_ssd_full_shape_ssm_only():
         hx, hdt = to_host64(act["x"][:, :, ci]), to_host64(act["dt"][:, :, h:h + 1])
         want = oracle.ssd_scan_fwd(hx, hdt, A[h:h + 1], to_host64(act["B"]), to_host64(act["C"]), None, None,
                                    bias[h:h + 1], gate=False)
-        check(got, want, "ssd", f"ssd full shape ssm-only head {h}")
+        mag = ssd_magnitudes(hx, hdt, A[h:h + 1], to_host64(act["B"]), to_host64(act["C"]), None, None,
+                             bias[h:h + 1], gate=False)
+        check(got, want, "ssd", f"ssd full shape ssm-only head {h}", mag=mag)
 
 
 def test_ssd_block_long_chain():

@@ -6,13 +6,14 @@ Section 4.1 Table 8: untied, width 4; Appendix C Table 12: Conv1d over the xBC s
 reference is oracle.conv_causal (forward layer) or oracle.conv_anticausal (reverse layer), rounded to bf16 as
 the entry point states (the convolution's output takes the I/O precision, as when it is stored between two
 passes), split into x, B, C and fed to oracle.ssd_scan_fwd with one direction kept.  Bars: the "ssd" bars of
-tests/gpu_util.py (bf16 output, bf16 matrix-core operands).
+tests/gpu_util.py (bf16 output, bf16 matrix-core operands: each element within its rounding plus three bf16
+roundings of the magnitudes of its terms), and "ssd_pair" where two results of the HIP path are compared.
 """
 import numpy as np
 import pytest
 
 from bidirectional_mamba_selective_amd import inputs
-from tests.gpu_util import check, f32_dev, say, to_dev, to_host64, torch_mod
+from tests.gpu_util import check, f32_dev, say, ssd_magnitudes, to_dev, to_host64, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +41,8 @@ def _upload(inp, conv=True):
 
 def reference(inp, direction, conv=True, gate=True, use_D=True, use_bias=True, heads=None):
     """The oracle's convolution (of the direction), rounded to bf16, then its one-direction scan; heads
-    selects a subset of heads (the stream's B and C channels are shared by all heads)."""
+    selects a subset of heads (the stream's B and C channels are shared by all heads).  Returns (out, cols,
+    the magnitudes of each output element's terms)."""
     import oracle
 
     nh = inp["A"].shape[0]
@@ -53,9 +55,10 @@ def reference(inp, direction, conv=True, gate=True, use_D=True, use_bias=True, h
     hs = list(range(nh)) if heads is None else list(heads)
     cols = np.concatenate([np.arange(h * P, (h + 1) * P) for h in hs])
     x, B, C = u[:, :, cols], u[:, :, hp:hp + N], u[:, :, hp + N:hp + 2 * N]
-    return oracle.ssd_scan_fwd(x, inp["dt"][:, :, hs], inp["A"][hs], B, C, inp["D"][hs] if use_D else None,
-                               inp["z"][:, :, cols] if gate else None, inp["dt_bias"][hs] if use_bias else None,
-                               gate=gate, fwd=direction == "f", rev=direction == "r"), cols
+    args = (x, inp["dt"][:, :, hs], inp["A"][hs], B, C, inp["D"][hs] if use_D else None,
+            inp["z"][:, :, cols] if gate else None, inp["dt_bias"][hs] if use_bias else None)
+    kw = dict(gate=gate, fwd=direction == "f", rev=direction == "r")
+    return oracle.ssd_scan_fwd(*args, **kw), cols, ssd_magnitudes(*args, **kw)
 
 
 def run(fwd, rev, flags=0):
@@ -73,8 +76,10 @@ def test_layers_with_conv(batch, L, nh):
     f = inputs.make_ssd_layer_inputs(batch, L, nh, seed=L + 1, param_seed=0)
     r = inputs.make_ssd_layer_inputs(batch, L, nh, seed=L + 2, param_seed=3)
     of, orr = run(_upload(f), _upload(r))
-    check(to_host64(of), reference(f, "f")[0], "ssd", f"conv layers {batch}x{L}x{nh} forward")
-    check(to_host64(orr), reference(r, "r")[0], "ssd", f"conv layers {batch}x{L}x{nh} reverse")
+    want, _, mag = reference(f, "f")
+    check(to_host64(of), want, "ssd", f"conv layers {batch}x{L}x{nh} forward", mag=mag)
+    want, _, mag = reference(r, "r")
+    check(to_host64(orr), want, "ssd", f"conv layers {batch}x{L}x{nh} reverse", mag=mag)
 
 
 @pytest.mark.parametrize("mode", ["no_conv", "no_gate", "no_D_no_bias", "forward_only", "reverse_only"])
@@ -94,18 +99,20 @@ def test_layer_variants(mode):
     of, orr = run(None if mode == "reverse_only" else df, None if mode == "forward_only" else dr,
                   flags=0 if gate else 1)
     if mode != "reverse_only":
-        check(to_host64(of), reference(f, "f", conv, gate, use, use)[0], "ssd", f"variant {mode} forward")
+        want, _, mag = reference(f, "f", conv, gate, use, use)
+        check(to_host64(of), want, "ssd", f"variant {mode} forward", mag=mag)
     else:
         assert of is None
     if mode != "forward_only":
-        check(to_host64(orr), reference(r, "r", conv, gate, use, use)[0], "ssd", f"variant {mode} reverse")
+        want, _, mag = reference(r, "r", conv, gate, use, use)
+        check(to_host64(orr), want, "ssd", f"variant {mode} reverse", mag=mag)
     else:
         assert orr is None
 
 
 def test_one_direction_walks_match_the_bidirectional_kernels():
     """Without the convolution, each layer equals bimamba_ssd_fwd with FWD_ONLY / REV_ONLY on the same x, B, C
-    (the same mathematics through different kernels and decompositions), to the "ssd" bars."""
+    (the same mathematics through different kernels and decompositions), to the "ssd_pair" bars."""
     from bidirectional_mamba_selective_amd import bimamba_ssd_fwd
 
     torch = torch_mod()
@@ -118,8 +125,10 @@ def test_one_direction_walks_match_the_bidirectional_kernels():
     wf = bimamba_ssd_fwd(x, d["dt"], d["A"], B, C, d["D"], d["z"], d["dt_bias"], flags=2)
     wr = bimamba_ssd_fwd(x, d["dt"], d["A"], B, C, d["D"], d["z"], d["dt_bias"], flags=4)
     torch.cuda.synchronize()
-    check(to_host64(of), to_host64(wf), "ssd", "forward layer vs bidirectional kernels (FWD_ONLY)")
-    check(to_host64(orr), to_host64(wr), "ssd", "reverse layer vs bidirectional kernels (REV_ONLY)")
+    check(to_host64(of), to_host64(wf), "ssd_pair", "forward layer vs bidirectional kernels (FWD_ONLY)",
+          mag=reference(f, "f", conv=False)[2])
+    check(to_host64(orr), to_host64(wr), "ssd_pair", "reverse layer vs bidirectional kernels (REV_ONLY)",
+          mag=reference(f, "r", conv=False)[2])
 
 
 def test_fused_equals_convolution_then_scan_on_the_gpu():
@@ -134,8 +143,8 @@ def test_fused_equals_convolution_then_scan_on_the_gpu():
     uf, _ = bimamba_conv1d_bidir(df["xbc"], df["cw"], df["cb"], None, None)
     _, ur = bimamba_conv1d_bidir(dr["xbc"], None, None, dr["cw"], dr["cb"])
     pf, pr = run(dict(df, xbc=uf, cw=None, cb=None), dict(dr, xbc=ur, cw=None, cb=None))
-    check(to_host64(of), to_host64(pf), "ssd", "fused vs two-pass, forward layer")
-    check(to_host64(orr), to_host64(pr), "ssd", "fused vs two-pass, reverse layer")
+    check(to_host64(of), to_host64(pf), "ssd_pair", "fused vs two-pass, forward layer", mag=reference(f, "f")[2])
+    check(to_host64(orr), to_host64(pr), "ssd_pair", "fused vs two-pass, reverse layer", mag=reference(r, "r")[2])
 
 
 def test_full_shape_sampled_heads():
@@ -162,6 +171,6 @@ def test_full_shape_sampled_heads():
             inp = dict(xbc=to_host64(d["xbc"][:, :, ci]), dt=to_host64(d["dt"][:, :, h:h + 1]),
                        z=to_host64(d["z"][:, :, h * P:(h + 1) * P]), A=host["A"][h:h + 1], D=host["D"][h:h + 1],
                        dt_bias=host["dt_bias"][h:h + 1], cw=host["cw"][chan], cb=host["cb"][chan])
-            want, _ = reference(inp, direction)
+            want, _, mag = reference(inp, direction)
             cols = torch.from_numpy(np.arange(h * P, (h + 1) * P)).cuda()
-            check(to_host64(out[:, :, cols]), want, "ssd", f"full shape {direction} head {h}")
+            check(to_host64(out[:, :, cols]), want, "ssd", f"full shape {direction} head {h}", mag=mag)
