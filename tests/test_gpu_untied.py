@@ -83,6 +83,28 @@ def test_untied_equal_sets_sum_to_tied():
     check(got_f + got_r, tied, Bar(1e-5, 1e-5, 1e-5, 1e-6), "untied equal sets vs tied")
 
 
+def test_untied_long_full_width():
+    """The benchmarked untied shape (L 65536, d_inner 4096, bf16; the forward set with geometric A, the
+    reverse set with general A) over both whole outputs, against the oracle run on the host in channel shards."""
+    from tests.gpu_util import oracle_sharded
+
+    L, D, N = 65536, 4096, 16
+    say("untied long full width: generating inputs")
+    f = _set(1, L, D, N, "bf16", seed=13, a_jitter=0.0, param_seed=0)
+    r = _set(1, L, D, N, "bf16", seed=14, a_jitter=0.2, param_seed=5)
+    got_f, got_r = _run(f, r, "bf16")
+
+    def both(sets, chan):
+        sub = [{k: (c[k][:, :, chan] if k in ("x", "dt", "z") else (c[k][chan] if k in ("A", "D", "dt_bias")
+                                                                     else c[k])) for k in c} for c in sets]
+        return np.stack(oracle.scan_fwd_untied(sub[0], sub[1]))
+
+    say("untied long full width: oracle on 4096 channels in host processes")
+    want = oracle_sharded(both, (f, r), D, (2, 1, L, D))
+    check(got_f, want[0], "bf16", "untied long out_f (all 65536 x 4096 outputs)")
+    check(got_r, want[1], "bf16", "untied long out_r (all 65536 x 4096 outputs)")
+
+
 def test_untied_layer_2k_subset():
     """The layer shape (batch 1, L 2048, d_inner 4096, d_state 16, bf16), both directions checked on a
     channel subset (each output channel depends only on its own channel and the shared B, C)."""
