@@ -162,15 +162,16 @@ def test_long_64k_workload():
     check_variants(inp, w.io_dtype, variants=VARIANTS[:2], chan=chan, tag="long_64k")
 
 
-@pytest.mark.parametrize("name", ["layer_2k_bf16", "long_64k_bf16"])
-def test_workload_full_width(name):
-    """The layer-2k and long workloads (the long one is the benchmarked launch) over their whole outputs,
-    every token of every channel, against the oracle run on the host in channel shards."""
+@pytest.mark.parametrize("name, a_jitter", [("layer_2k_bf16", 0.0), ("long_64k_bf16", 0.0), ("long_64k_bf16", 0.2)])
+def test_workload_full_width(name, a_jitter):
+    """The layer-2k and long workloads (the long one is the benchmarked launch; also with A off its geometric
+    form, the general path trained weights take) over their whole outputs, every token of every channel,
+    against the oracle run on the host in channel shards."""
     from tests.gpu_util import oracle_sharded
 
     w = I.WORKLOADS[name]
-    say(f"{name} full width: generating inputs")
-    inp = case(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype)
+    say(f"{name} full width (A jitter {a_jitter}): generating inputs")
+    inp = case(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype, a_jitter=a_jitter)
     got = to_host64(run_fwd(upload(inp, w.io_dtype)))
     say(f"{name} full width: oracle on {w.d_inner} channels in host processes")
     want = oracle_sharded(lambda d, c: oracle_fwd(d, chan=c), inp, w.d_inner, got.shape)
