@@ -6,8 +6,10 @@ row of compared channels, and an elementwise bound from the arithmetic (bf16:
 the round-to-nearest-even error of the output plus 2e-4 of its rms; fp32:
 1e-4 relative plus 1e-5 of the rms).  Where stated, the SSM-only output
 (D = NULL, gate off) is compared, which a broken carry cannot hide behind.
-Full-size workloads are checked on a channel subset: output channel d depends
-only on channel d and the shared B, C, so the oracle on a subset is exact for it.
+Full-size workloads are checked on channel subsets in every variant, and over
+their whole outputs with the oracle run in channel shards by host processes:
+output channel d depends only on channel d and the shared B, C, so the oracle
+on a subset is exact for it.
 """
 import numpy as np
 import pytest

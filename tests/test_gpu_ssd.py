@@ -2,7 +2,9 @@
 
 Small cases compare every output; the long cases run all 120 heads on the GPU
 and compare sampled heads in full against the oracle run on those heads alone
-(heads are independent, a fact the oracle's head-independence pin fixes).
+(heads are independent, a fact the oracle's head-independence pin fixes), and
+one run at L = 65536 compares every output, the oracle run in shards of heads
+by host processes.
 """
 import numpy as np
 import pytest
