@@ -4,7 +4,7 @@ Bars (tests/gpu_util.py BARS): normwise relative error <= 2e-2 with bf16 I/O
 and <= 1e-4 with fp32 I/O on the whole output, the same bar on every token's
 row of compared channels, and an elementwise bound from the arithmetic (bf16:
 the round-to-nearest-even error of the output plus 2e-4 of its rms; fp32:
-1e-4 relative plus 1e-5 of the rms).  Where stated, the SSM-only output
+1e-4 relative plus 3e-5 of the rms).  Where stated, the SSM-only output
 (D = NULL, gate off) is compared, which a broken carry cannot hide behind.
 Full-size workloads are checked on channel subsets in every variant, and over
 their whole outputs with the oracle run in channel shards by host processes:
