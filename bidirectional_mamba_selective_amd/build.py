@@ -19,6 +19,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
@@ -36,10 +37,15 @@ HIPFLAGS = [
     "-std=c++17",
     f"--offload-arch={ARCH}",
     "-fPIC",
-    "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+
+# Per-source device code generation.  The scan kernels issue faster when the machine scheduler orders their
+# instructions for instruction-level parallelism (measured on MI355X at L = 65536, two runs each: the tied
+# call 1.632 -> 1.609 ms, untied directions 2.685 -> 2.592 ms, identical output bits); the Mamba-2 kernels
+# keep the default order (with it their fused one-direction layers took 2.43 instead of 2.37 ms).
+SOURCE_FLAGS = {"scan_kernels.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def sources():
@@ -53,9 +59,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libbimamba.so")
 
 
-def _compile(srcs, lib, verbose, extra_flags=()):
-    tmp = lib + ".tmp"
-    cmd = [hipcc(), *HIPFLAGS, *extra_flags, "-I", os.path.join(os.path.dirname(PKG), "include"), *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -65,6 +69,24 @@ def _compile(srcs, lib, verbose, extra_flags=()):
         raise RuntimeError("hipcc failed:\n" + "\n".join(noise))
     if verbose and noise:
         print("\n".join(noise))
+
+
+def _compile(srcs, lib, verbose, extra_flags=()):
+    """Each source to an object with its own flags (SOURCE_FLAGS), then one shared library."""
+    tmp = lib + ".tmp"
+    inc = os.path.join(os.path.dirname(PKG), "include")
+    os.makedirs(os.path.join(PKG, "_build"), exist_ok=True)
+    objdir = tempfile.mkdtemp(prefix="objs_", dir=os.path.join(PKG, "_build"))
+    try:
+        objs = []
+        for src in srcs:
+            obj = os.path.join(objdir, os.path.basename(src) + ".o")
+            _run([hipcc(), *HIPFLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), *extra_flags, "-I", inc, "-c", src,
+                  "-o", obj], verbose)
+            objs.append(obj)
+        _run([hipcc(), "-fPIC", "-shared", *extra_flags, *objs, "-o", tmp], verbose)
+    finally:
+        shutil.rmtree(os.path.join(PKG, "_build"), ignore_errors=True)
     os.replace(tmp, lib)
     return lib
 
