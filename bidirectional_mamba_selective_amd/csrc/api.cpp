@@ -45,6 +45,21 @@ int check_shape(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
   return BIMAMBA_OK;
 }
 
+// Whether r overlaps any input of a scan call (x, dt, z [batch, seqlen, d_inner]; B, C [batch, seqlen, d_state];
+// A [d_inner, d_state]; D, dt_bias [d_inner]); z, D and dt_bias may be NULL.
+bool hits_scan_inputs(Range r, const void* x, const void* dt, const float* A, const void* B, const void* C,
+                      const float* D, const void* z, const float* dt_bias, int64_t batch, int64_t seqlen,
+                      int64_t d_inner, int64_t d_state, int io_dtype) {
+  const size_t es = io_dtype == BIMAMBA_BF16 ? 2 : 4;
+  const size_t act = static_cast<size_t>(batch) * seqlen * d_inner * es;
+  const size_t bc = static_cast<size_t>(batch) * seqlen * d_state * es;
+  return overlap(r, range_of(x, act)) || overlap(r, range_of(dt, act)) || overlap(r, range_of(B, bc)) ||
+         overlap(r, range_of(C, bc)) || (z && overlap(r, range_of(z, act))) ||
+         overlap(r, range_of(A, static_cast<size_t>(d_inner) * d_state * 4)) ||
+         (D && overlap(r, range_of(D, static_cast<size_t>(d_inner) * 4))) ||
+         (dt_bias && overlap(r, range_of(dt_bias, static_cast<size_t>(d_inner) * 4)));
+}
+
 // Pointer checks shared by both entry points; sizes in elements.
 int check_tensors(const void* x, const void* dt, const float* A, const void* B, const void* C, const float* D,
                   const void* z, const float* dt_bias, void* out, int64_t batch, int64_t seqlen, int64_t d_inner,
@@ -57,14 +72,8 @@ int check_tensors(const void* x, const void* dt, const float* A, const void* B, 
   if (!aligned(x, 16) || !aligned(dt, 16) || !aligned(out, 16) || (z && !aligned(z, 16))) return BIMAMBA_ERR_INVALID_ARGUMENT;
   if (!aligned(B, es) || !aligned(C, es)) return BIMAMBA_ERR_INVALID_ARGUMENT;
   if (!aligned(A, 16) || (D && !aligned(D, 16)) || (dt_bias && !aligned(dt_bias, 16))) return BIMAMBA_ERR_INVALID_ARGUMENT;
-  const size_t act = static_cast<size_t>(batch) * seqlen * d_inner * es;
-  const size_t bc = static_cast<size_t>(batch) * seqlen * d_state * es;
-  const Range o = range_of(out, act);
-  if (overlap(o, range_of(x, act)) || overlap(o, range_of(dt, act)) || overlap(o, range_of(B, bc)) ||
-      overlap(o, range_of(C, bc)) || (z && overlap(o, range_of(z, act))) ||
-      overlap(o, range_of(A, static_cast<size_t>(d_inner) * d_state * 4)) ||
-      (D && overlap(o, range_of(D, static_cast<size_t>(d_inner) * 4))) ||
-      (dt_bias && overlap(o, range_of(dt_bias, static_cast<size_t>(d_inner) * 4))))
+  const Range o = range_of(out, static_cast<size_t>(batch) * seqlen * d_inner * es);
+  if (hits_scan_inputs(o, x, dt, A, B, C, D, z, dt_bias, batch, seqlen, d_inner, d_state, io_dtype))
     return BIMAMBA_ERR_INVALID_ARGUMENT;
   return BIMAMBA_OK;
 }
@@ -115,6 +124,10 @@ static int scan_fwd_impl(int stage, const void* x, const void* dt, const float* 
   const size_t es = io_dtype == BIMAMBA_BF16 ? 2 : 4;
   s = check_workspace(p, workspace, workspace_bytes, out, static_cast<size_t>(batch) * seqlen * d_inner * es);
   if (s != BIMAMBA_OK) return s;
+  // the kernels write the workspace while others still read the inputs
+  if (hits_scan_inputs(range_of(workspace, p.total), x, dt, A, B, C, D, z, dt_bias, batch, seqlen, d_inner, d_state,
+                       io_dtype))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
   bimamba::ScanArgs a{x, dt, A, B, C, D, z, dt_bias, out, nullptr, nullptr, io_dtype, flags};
   return map_hip(bimamba::launch_chunked(a, p, workspace, stream, stage));
 }
@@ -191,7 +204,11 @@ int bimamba_scan_fwd_untied(const void* x_f, const void* dt_f, const float* A_f,
   const Plan p = bimamba::make_plan(batch, seqlen, d_inner, d_state);
   s = check_workspace(p, workspace, workspace_bytes, out_f, act);
   if (s != BIMAMBA_OK) return s;
-  if (overlap(range_of(workspace, p.total), range_of(out_r, act))) return BIMAMBA_ERR_INVALID_ARGUMENT;
+  const Range wr = range_of(workspace, p.total);
+  if (overlap(wr, range_of(out_r, act)) ||
+      hits_scan_inputs(wr, x_f, dt_f, A_f, B_f, C_f, D_f, z_f, dt_bias_f, batch, seqlen, d_inner, d_state, io_dtype) ||
+      hits_scan_inputs(wr, x_r, dt_r, A_r, B_r, C_r, D_r, z_r, dt_bias_r, batch, seqlen, d_inner, d_state, io_dtype))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
   // two one-direction passes in stream order, sharing the workspace
   const bimamba::ScanArgs af{x_f, dt_f, A_f, B_f, C_f, D_f, z_f, dt_bias_f, out_f, nullptr, nullptr, io_dtype,
                              flags | BIMAMBA_FLAG_FWD_ONLY};
@@ -245,8 +262,9 @@ int bimamba_scan_block(const void* x, const void* dt, const float* A, const void
   s = check_workspace(p, workspace, workspace_bytes, out, out_bytes);
   if (s != BIMAMBA_OK) return s;
   // the staging and summary kernels write the workspace before the carry kernel reads h_in
-  if ((h_out && overlap(range_of(h_out, st_bytes), range_of(workspace, p.total))) ||
-      (h_in && overlap(range_of(h_in, st_bytes), range_of(workspace, p.total))))
+  const Range wr = range_of(workspace, p.total);
+  if ((h_out && overlap(range_of(h_out, st_bytes), wr)) || (h_in && overlap(range_of(h_in, st_bytes), wr)) ||
+      hits_scan_inputs(wr, x, dt, A, B, C, D, z, dt_bias, batch, block_len, d_inner, d_state, io_dtype))
     return BIMAMBA_ERR_INVALID_ARGUMENT;
   return map_hip(bimamba::launch_chunked(a, p, workspace, stream));
 }
@@ -321,6 +339,11 @@ static int ssd_impl(int stage, const void* x, const void* dt, const float* A, co
   if (!workspace || !aligned(workspace, 256)) return BIMAMBA_ERR_INVALID_ARGUMENT;
   const Range wr = range_of(workspace, p.total);
   if (overlap(wr, o) || (h_in && overlap(wr, range_of(h_in, stb))) || (h_out && overlap(wr, range_of(h_out, stb))))
+    return BIMAMBA_ERR_INVALID_ARGUMENT;
+  // the tiling kernel and the sweeps write the workspace while others still read the inputs
+  if (overlap(wr, range_of(x, act)) || overlap(wr, range_of(dt, dtb)) || overlap(wr, range_of(B, bc)) ||
+      overlap(wr, range_of(C, bc)) || (z && overlap(wr, range_of(z, act))) || overlap(wr, range_of(A, par)) ||
+      (D && overlap(wr, range_of(D, par))) || (dt_bias && overlap(wr, range_of(dt_bias, par))))
     return BIMAMBA_ERR_INVALID_ARGUMENT;
   return map_hip(bimamba::ssd::launch_ssd(a, p, workspace, stream, stage));
 }

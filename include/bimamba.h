@@ -31,8 +31,9 @@
  *     dt_bias, block states and every internal state are fp32; out is rounded
  *     to nearest even when io_dtype is BF16.
  *   - D == NULL means D = 0; dt_bias == NULL means dt_bias = 0; z may be NULL
- *     only together with BIMAMBA_FLAG_NO_GATE.  Inputs are read-only and out
- *     must not overlap any input or the workspace.
+ *     only together with BIMAMBA_FLAG_NO_GATE.  Inputs are read-only; out and
+ *     the workspace must not overlap any input or each other (such a call is
+ *     rejected with BIMAMBA_ERR_INVALID_ARGUMENT).
  *   - Supported shapes: 1 <= batch <= 65535, seqlen/block_len >= 1, d_inner a
  *     positive multiple of 64, 1 <= d_state <= 16, and the kernels' 32-bit
  *     buffer offsets: 16 * d_inner * element size and d_state * d_inner * 4 + 256
@@ -145,7 +146,8 @@ int bimamba_scan_fwd_noalloc(const void* x, const void* dt, const float* A, cons
  * bimamba_scan_fwd_workspace_bytes, used by the two passes in turn) are as for
  * bimamba_scan_fwd; flags may only be BIMAMBA_FLAG_NO_GATE (then z_f and z_r
  * may be NULL).  Neither output may overlap any tensor of either set, the other
- * output or the workspace; a rejected call returns a status and enqueues nothing. */
+ * output or the workspace, and the workspace may not overlap any tensor of
+ * either set; a rejected call returns a status and enqueues nothing. */
 int bimamba_scan_fwd_untied(const void* x_f, const void* dt_f, const float* A_f, const void* B_f, const void* C_f,
                             const float* D_f, const void* z_f, const float* dt_bias_f, void* out_f,
                             const void* x_r, const void* dt_r, const float* A_r, const void* B_r, const void* C_r,
@@ -171,7 +173,7 @@ size_t bimamba_scan_block_workspace_bytes(int64_t batch, int64_t block_len, int6
  *          out.  The flags select the directions summed into out; h_out is the
  *          forward state in every case.
  * workspace may be NULL when bimamba_scan_block_workspace_bytes returns 0;
- * otherwise neither h_in nor h_out may overlap it. */
+ * otherwise neither h_in, h_out nor any input may overlap it. */
 int bimamba_scan_block(const void* x, const void* dt, const float* A, const void* B, const void* C,
                        const float* D, const void* z, const float* dt_bias,
                        const float* h_in, float* h_out, void* out,

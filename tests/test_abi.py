@@ -395,6 +395,20 @@ def test_scan_block_rejects_cache_overlapping_workspace():
     # as far as launching, which the fake pointers must not reach, so only the rejections are exercised here
 
 
+@pytest.mark.parametrize("target", ["x", "dt", "A", "B", "C", "D", "z", "dt_bias"])
+def test_workspace_over_an_input_is_rejected(target):
+    """The kernels write the workspace while others still read the inputs, so a workspace that overlaps
+    any input is rejected before any HIP call (scan, untied directions, a block past the single-kernel
+    limit, the Mamba-2 heads)."""
+    idx = dict(x=0, dt=1, A=2, B=3, C=4, D=5, z=6, dt_bias=7)[target]
+    assert call_fwd(ws=fake(idx), wsb=1 << 40) == INV
+    assert call_block(L=200, ws=fake(idx), wsb=1 << 40) == INV
+    assert call_ssd(ws=fake(idx), wsb=1 << 40) == INV
+    # untied directions: the forward set sits at fake(0..7), the reverse set at fake(12..19)
+    assert call_untied(ws=fake(idx), wsb=1 << 40) == INV
+    assert call_untied(ws=fake(idx + 12), wsb=1 << 40) == INV
+
+
 def test_ssd_rejects_head_counts_past_the_output_buffer_range():
     lib = _lib.load()
     f = lib.bimamba_ssd_fwd_workspace_bytes
