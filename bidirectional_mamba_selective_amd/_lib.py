@@ -140,13 +140,20 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _nbytes(t):
+def _bytes_of(t):
     """Bytes of a caller-provided workspace tensor (any dtype; it must be contiguous); 0 for None."""
     if t is None:
         return 0
     if not t.is_contiguous():
         raise ValueError("workspace must be contiguous")
     return t.numel() * t.element_size()
+
+
+def _nbytes(t, device):
+    """_bytes_of a workspace that must sit on the call's device (a host tensor's address would reach the kernels)."""
+    if t is not None and (not t.is_cuda or t.device != device):
+        raise ValueError(f"workspace must be on {device}")
+    return _bytes_of(t)
 
 
 def _io_dtype(x):
@@ -220,8 +227,8 @@ def bimamba_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, fla
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = lib.bimamba_scan_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
-                              _ptr(out), nb, L, nd, ns, _io_dtype(x), flags, _ptr(workspace), _nbytes(workspace),
-                              _stream(stream, x.device))
+                              _ptr(out), nb, L, nd, ns, _io_dtype(x), flags, _ptr(workspace),
+                              _nbytes(workspace, x.device), _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_scan_fwd")
     return out
@@ -260,7 +267,7 @@ def bimamba_scan_fwd_untied(fwd, rev, out_f=None, out_r=None, flags: int = 0, wo
     ptrs = [_ptr(f[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")] + [_ptr(out_f)]
     ptrs += [_ptr(r[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")] + [_ptr(out_r)]
     st = lib.bimamba_scan_fwd_untied(*ptrs, nb, L, nd, ns, _io_dtype(f["x"]), flags, _ptr(workspace),
-                                     _nbytes(workspace), _stream(stream, f["x"].device))
+                                     _nbytes(workspace, f["x"].device), _stream(stream, f["x"].device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_scan_fwd_untied")
     return out_f, out_r
@@ -276,7 +283,7 @@ def bimamba_scan_fwd_stage(stage: int, x, dt, A, B, C, D=None, z=None, dt_bias=N
         raise ValueError("the staged entry point needs a caller-kept workspace")
     st = load().bimamba_scan_fwd_stage(int(stage), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                        _ptr(dt_bias), _ptr(out), nb, L, nd, ns, _io_dtype(x), flags, _ptr(workspace),
-                                       _nbytes(workspace), _stream(stream, x.device))
+                                       _nbytes(workspace, x.device), _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, f"bimamba_scan_fwd_stage({stage})")
     return out
@@ -295,7 +302,7 @@ def bimamba_scan_block(x, dt, A, B, C, D=None, z=None, dt_bias=None, h_in=None, 
         need = int(lib.bimamba_scan_block_workspace_bytes(nb, L, nd, ns))
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    wbytes = _nbytes(workspace)
+    wbytes = _nbytes(workspace, x.device)
     st = lib.bimamba_scan_block(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
                                 _ptr(h_in), _ptr(h_out), _ptr(out), nb, L, nd, ns, _io_dtype(x), flags,
                                 _ptr(workspace), wbytes, _stream(stream, x.device))
@@ -346,8 +353,8 @@ def bimamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, out=None, flag
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = lib.bimamba_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
-                             _ptr(out), nb, L, nh, hp, ns, _io_dtype(x), flags, _ptr(workspace), _nbytes(workspace),
-                             _stream(stream, x.device))
+                             _ptr(out), nb, L, nh, hp, ns, _io_dtype(x), flags, _ptr(workspace),
+                             _nbytes(workspace, x.device), _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_ssd_fwd")
     return out
@@ -362,7 +369,7 @@ def bimamba_ssd_fwd_stage(stage: int, x, dt, A, B, C, D=None, z=None, dt_bias=No
         raise ValueError("the staged entry point needs a caller-kept workspace")
     st = load().bimamba_ssd_fwd_stage(int(stage), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                       _ptr(dt_bias), _ptr(out), nb, L, nh, hp, ns, _io_dtype(x), flags,
-                                      _ptr(workspace), _nbytes(workspace), _stream(stream, x.device))
+                                      _ptr(workspace), _nbytes(workspace, x.device), _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, f"bimamba_ssd_fwd_stage({stage})")
     return out
@@ -387,7 +394,7 @@ def bimamba_ssd_block(x, dt, A, B, C, D=None, z=None, dt_bias=None, h_in=None, h
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = lib.bimamba_ssd_block(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
                                _ptr(h_in), _ptr(h_out), _ptr(out), nb, L, nh, hp, ns, _io_dtype(x), flags,
-                               _ptr(workspace), _nbytes(workspace), _stream(stream, x.device))
+                               _ptr(workspace), _nbytes(workspace, x.device), _stream(stream, x.device))
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_ssd_block")
     return out
@@ -447,8 +454,9 @@ def bimamba_ssd_conv_untied(fwd=None, rev=None, out_f=None, out_r=None, flags: i
     for t in sets:
         ptrs += [None] * 9 if t is None else [_ptr(t[k]) for k in _LAYER_KEYS + ("out",)]
     first = next(t for t in sets if t)
+    dev = first["xbc"].device
     st = lib.bimamba_ssd_conv_untied(*ptrs, nb, L, nh, hp // nh, d_state, 4, _io_dtype(first["xbc"]), flags,
-                                     _ptr(workspace), _nbytes(workspace), _stream(stream, first["xbc"].device))
+                                     _ptr(workspace), _nbytes(workspace, dev), _stream(stream, dev))
     if st != BIMAMBA_OK:
         raise BimambaError(st, "bimamba_ssd_conv_untied")
     return tuple(None if t is None else t["out"] for t in sets)

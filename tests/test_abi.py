@@ -316,11 +316,15 @@ def test_conv_cache_arguments():
 def test_binding_counts_workspace_bytes():
     import torch
 
-    assert _lib._nbytes(None) == 0
-    assert _lib._nbytes(torch.empty(10, dtype=torch.uint8)) == 10
-    assert _lib._nbytes(torch.empty(10, dtype=torch.float32)) == 40  # any dtype: bytes, not elements
+    assert _lib._bytes_of(None) == 0
+    assert _lib._bytes_of(torch.empty(10, dtype=torch.uint8)) == 10
+    assert _lib._bytes_of(torch.empty(10, dtype=torch.float32)) == 40  # any dtype: bytes, not elements
     with pytest.raises(ValueError):
-        _lib._nbytes(torch.empty(4, 4, dtype=torch.uint8).t())
+        _lib._bytes_of(torch.empty(4, 4, dtype=torch.uint8).t())
+    # a host tensor as the workspace of a device call is refused before its address reaches the library
+    assert _lib._nbytes(None, torch.device("cuda:0")) == 0
+    with pytest.raises(ValueError):
+        _lib._nbytes(torch.empty(16, dtype=torch.uint8), torch.device("cuda:0"))
 
 
 def call_ssd_block(**kw):
