@@ -228,17 +228,17 @@ def bench_micro(torch, dev, stream):
     del src
     clk = torch.zeros(8192, dtype=torch.int64, device=dev)
     # the shader clock under a full FMA load at 4 wavefronts per SIMD (the scans' occupancy)
-    lib.micro_fma(ctypes.c_void_p(sink.data_ptr()), 4096, 4, ctypes.c_void_p(clk.data_ptr()), sp)
+    lib.micro_fma(ctypes.c_void_p(sink.data_ptr()), 1024, 4, ctypes.c_void_p(clk.data_ptr()), sp)
     torch.cuda.synchronize()
     c = clk.cpu().numpy().reshape(-1, 2)
     ghz = float(np.median(c[:, 0] / np.maximum(c[:, 1], 1))) * 0.1
     res["clock_ghz_under_fma_load"] = round(ghz, 3)
     fma, ex = {}, {}
     for w in (1, 2, 4, 8):
-        iters = 4096
+        iters = 1024
         t = timed(lambda: lib.micro_fma(ctypes.c_void_p(sink.data_ptr()), iters, w, ctypes.c_void_p(clk.data_ptr()),
                                         sp))
-        rate = N_SIMD * w * 64 * 8 * iters / t  # lane-FMAs per second
+        rate = N_SIMD * w * 64 * 64 * iters / t  # lane-FMAs per second (64 per thread and iteration)
         fma[str(w)] = round(rate / (256 * ghz * 1e9), 1)  # per clock and CU at the measured clock
         t = timed(lambda: lib.micro_exp(ctypes.c_void_p(sink.data_ptr()), 1024, w, sp))
         ex[str(w)] = round(N_SIMD * w * 64 * 8 * 1024 / t / (256 * ghz * 1e9), 1)

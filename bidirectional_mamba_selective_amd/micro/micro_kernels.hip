@@ -28,25 +28,28 @@ __global__ __launch_bounds__(256) void k_copy(const f32x4* __restrict__ src, f32
     __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
-// 8 independent FMA chains per lane, `iters` steps each: 8 * iters lane-FMAs per thread.  Every operand is a
-// VGPR (a and b are made lane-varying), the form of the scans' state arithmetic: a VALU instruction that reads
-// an SGPR issues more slowly when several follow each other, though not when mixed with VGPR-only ones.
+// 32 independent FMA chains per lane, two steps of each per loop iteration (64 FMAs between loop branches, so
+// that the branch costs no issue slots at low occupancy), `iters` iterations: 64 * iters lane-FMAs per thread.
+// Every operand is a VGPR (a and b are made lane-varying), the form of the scans' state arithmetic.
 // Wavefront 0 of each workgroup records the shader clock (s_memtime) and the 100 MHz reference
 // (s_memrealtime) around its loop in clk[2 * block], [2 * block + 1] for the first 4096 workgroups.
 __global__ __launch_bounds__(64) void k_fma(float* out, int iters, float a0, float b0, unsigned long long* clk) {
   const float a = a0 * (1.0f + 1e-30f * static_cast<float>(threadIdx.x));
   const float b = b0 * (1.0f + 1e-30f * static_cast<float>(threadIdx.x));
   const unsigned long long c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
-  float v[8];
+  float v[32];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) v[k] = static_cast<float>(threadIdx.x + k);
+  for (int k = 0; k < 32; ++k) v[k] = static_cast<float>(threadIdx.x + k);
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = fmaf(v[k], a, b);
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) v[k] = fmaf(v[k], a, b);
+    }
   }
   float s = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) s += v[k];
+  for (int k = 0; k < 32; ++k) s += v[k];
   if (s == -1.2345e37f) out[threadIdx.x] = s;
   const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
   if (threadIdx.x == 0 && blockIdx.x < 4096) {
