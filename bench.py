@@ -185,7 +185,7 @@ def host_workers():
 def bench_micro(torch, dev, stream):
     """Microbenchmarks on this machine, each timed with HIP events on `stream` (median of 5): HBM read-only and
     copy streams over 4 GiB and 2 GiB, the issue rate of independent fp32 FMAs and of v_exp_f32 at 1 to 8
-    wavefronts per SIMD, FMAs with an SGPR operand, and an empty kernel's launch floor replayed from a graph (one 64-lane workgroup,
+    wavefronts per SIMD, FMAs with SGPR and DPP-broadcast operands, and an empty kernel's launch floor replayed from a graph (one 64-lane workgroup,
     and the block step's grid of 256 workgroups of 512 threads)."""
     import ctypes
 
@@ -197,7 +197,7 @@ def bench_micro(torch, dev, stream):
     lib.micro_copy.argtypes = [vp, vp, sz, vp]
     lib.micro_fma.argtypes = [vp, ci, ci, vp, vp]
     lib.micro_exp.argtypes = [vp, ci, ci, vp]
-    lib.micro_fma_sgpr.argtypes = [vp, ci, ci, ci, vp]
+    lib.micro_fma_operand.argtypes = [vp, ci, ci, ci, vp]
     lib.micro_empty.argtypes = [ci, ci, vp]
     sp = ctypes.c_void_p(stream.cuda_stream)
 
@@ -246,14 +246,19 @@ def bench_micro(torch, dev, stream):
     res["exp_lanes_per_clk_per_cu"] = ex
     # clocks per wave64 FMA instruction and SIMD at 4 wavefronts per SIMD (the scan kernels' occupancy)
     res["fma_clk_per_instruction_4waves"] = round(64 * 4 / fma["4"], 3)
-    # the same at 8 wavefronts per SIMD, and with a wave-uniform (SGPR) multiplier in every FMA or in every
-    # other one: clocks per wavefront instruction and SIMD
+    # the same at 8 wavefronts per SIMD
     res["fma_clk_per_instruction_8waves"] = round(64 * 4 / fma["8"], 3)
+    # clocks per wavefront FMA instruction and SIMD by the kind of the multiplier operand, 32 chains in one
+    # harness: lane-varying VGPR, wave-uniform SGPR in every FMA or in every other one, a VGPR read through the
+    # DPP row broadcast (row_newbcast), at 4 and 8 wavefronts per SIMD
     sg = {}
-    for mode, name in ((0, "every_fma"), (1, "every_other_fma")):
-        t = timed(lambda: lib.micro_fma_sgpr(ctypes.c_void_p(sink.data_ptr()), 4096, 8, mode, sp))
-        sg[name] = round(t * ghz * 1e9 / (8 * 8 * 4096), 3)
-    res["fma_sgpr_operand_clk_per_instruction_8waves"] = sg
+    for w in (4, 8):
+        row = {}
+        for mode, name in ((0, "vgpr"), (1, "sgpr_every_fma"), (2, "sgpr_every_other_fma"), (3, "dpp_row_bcast")):
+            t = timed(lambda: lib.micro_fma_operand(ctypes.c_void_p(sink.data_ptr()), 2048, w, mode, sp))
+            row[name] = round(t * ghz * 1e9 / (w * 64 * 2048), 3)
+        sg[str(w)] = row
+    res["fma_operand_clk_per_instruction"] = sg
 
     floor = {}
     for groups, threads in ((1, 64), (256, 512)):
@@ -274,7 +279,7 @@ def bench_micro(torch, dev, stream):
         floor[f"{groups}x{threads}"] = round(float(np.median(ts[1:])) * 1e6 / 200, 2)
     res["empty_kernel_graph_us"] = floor
     log(f"micro: read {res['hbm_read_gbs']} GB/s, copy {res['hbm_copy_gbs']} GB/s, fma lanes/clk/CU {fma}, "
-        f"exp {ex}, SGPR-operand fma clk/instr {sg}, empty-kernel graph floor {floor} us")
+        f"exp {ex}, fma clk/instr by operand {sg}, empty-kernel graph floor {floor} us")
     return res
 
 

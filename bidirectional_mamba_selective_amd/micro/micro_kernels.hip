@@ -1,5 +1,6 @@
 // Microbenchmarks behind the rooflines the benchmark reports (gfx950): the HBM read and copy streams, the
-// issue rate of independent fp32 FMAs and of v_exp_f32, the shader clock under that load, and an empty
+// issue rate of independent fp32 FMAs (with VGPR, SGPR and DPP-broadcast operands) and of v_exp_f32, the
+// shader clock under that load, and an empty
 // kernel for the launch floor.  Built
 // into libbimamba_micro.so, a library of its own: the scan library does not contain or call any of it.
 // Every entry point enqueues one kernel on `stream` and returns the HIP status; the caller times it.
@@ -58,29 +59,52 @@ __global__ __launch_bounds__(64) void k_fma(float* out, int iters, float a0, flo
   }
 }
 
-// The same chains with a wave-uniform multiplier, which the compiler keeps in an SGPR and feeds to
-// v_fma_f32 as a scalar operand: mode 0 gives every chain the SGPR operand, mode 1 only the even chains (the
-// odd ones keep a lane-varying VGPR multiplier), so SGPR-operand instructions alternate with VGPR-only ones.
-__global__ __launch_bounds__(64) void k_fma_sgpr(float* out, int iters, float a0, float b0, int mode) {
+// The same 32 chains and loop with the multiplier taken in four ways: mode 0 a lane-varying VGPR (as k_fma);
+// mode 1 a wave-uniform value, which the compiler keeps in an SGPR and feeds to the FMA as a scalar operand;
+// mode 2 that SGPR operand in every other FMA only (the odd chains keep the VGPR); mode 3 a VGPR read through
+// the DPP row broadcast (v_fmac_f32_dpp with row_newbcast: every lane of a 16-lane row takes the row's lane k),
+// the other way to give every lane one shared value without a copy per lane.  The broadcast source is written
+// once before the loop, behind the wait states a DPP read of a VALU result needs.
+template <int K>
+__device__ __forceinline__ void fmac_row_bcast(float& acc, float m, float b) {
+  asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+               : "+v"(acc)
+               : "v"(m), "v"(b), "i"(K));
+}
+
+template <int MODE>
+__global__ __launch_bounds__(64) void k_fma_operand(float* out, int iters, float a0, float b0) {
   const float av = a0 * (1.0f + 1e-30f * static_cast<float>(threadIdx.x));
   const float b = b0 * (1.0f + 1e-30f * static_cast<float>(threadIdx.x));
-  float v[8];
+  float v[32];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) v[k] = static_cast<float>(threadIdx.x + k);
-  if (mode == 0) {
-    for (int i = 0; i < iters; ++i) {
+  for (int k = 0; k < 32; ++k) v[k] = static_cast<float>(threadIdx.x + k) * 1e-3f;
+  if (MODE == 3) asm volatile("s_nop 4" ::: "memory");
+  for (int i = 0; i < iters; ++i) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = fmaf(v[k], a0, b);
-    }
-  } else {
-    for (int i = 0; i < iters; ++i) {
+    for (int r = 0; r < 2; ++r) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = fmaf(v[k], (k & 1) ? av : a0, b);
+      for (int k = 0; k < 32; ++k) {
+        if (MODE == 0) {
+          v[k] = fmaf(v[k], av, b);
+        } else if (MODE == 1) {
+          v[k] = fmaf(v[k], a0, b);
+        } else if (MODE == 2) {
+          v[k] = fmaf(v[k], (k & 1) ? av : a0, b);
+        } else {
+          switch (k & 3) {  // the multiplier (v += m * b) from lanes 0, 5, 10, 15 of each row
+            case 0: fmac_row_bcast<0>(v[k], av, b); break;
+            case 1: fmac_row_bcast<5>(v[k], av, b); break;
+            case 2: fmac_row_bcast<10>(v[k], av, b); break;
+            default: fmac_row_bcast<15>(v[k], av, b); break;
+          }
+        }
+      }
     }
   }
   float s = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) s += v[k];
+  for (int k = 0; k < 32; ++k) s += v[k];
   if (s == -1.2345e37f) out[threadIdx.x] = s;
 }
 
@@ -124,9 +148,18 @@ int micro_fma(float* out, int iters, int waves_per_simd, unsigned long long* clk
   return static_cast<int>(hipGetLastError());
 }
 
-// mode 0: every FMA reads an SGPR multiplier; mode 1: every other one (see k_fma_sgpr)
-int micro_fma_sgpr(float* out, int iters, int waves_per_simd, int mode, hipStream_t stream) {
-  hipLaunchKernelGGL(k_fma_sgpr, dim3(1024 * waves_per_simd), dim3(64), 0, stream, out, iters, 0.999f, 0.001f, mode);
+// 64 * iters FMAs per thread, one 64-lane wavefront per workgroup, waves_per_simd wavefronts per SIMD; mode:
+// 0 VGPR multiplier, 1 SGPR multiplier in every FMA, 2 in every other FMA, 3 DPP row broadcast (see
+// k_fma_operand)
+int micro_fma_operand(float* out, int iters, int waves_per_simd, int mode, hipStream_t stream) {
+  const dim3 grid(1024 * waves_per_simd), block(64);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(k_fma_operand<0>, grid, block, 0, stream, out, iters, 0.999f, 0.001f); break;
+    case 1: hipLaunchKernelGGL(k_fma_operand<1>, grid, block, 0, stream, out, iters, 0.999f, 0.001f); break;
+    case 2: hipLaunchKernelGGL(k_fma_operand<2>, grid, block, 0, stream, out, iters, 0.999f, 0.001f); break;
+    case 3: hipLaunchKernelGGL(k_fma_operand<3>, grid, block, 0, stream, out, iters, 0.999f, 0.001f); break;
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
   return static_cast<int>(hipGetLastError());
 }
 
