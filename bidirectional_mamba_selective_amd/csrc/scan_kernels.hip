@@ -247,6 +247,37 @@ __device__ __forceinline__ void summary_tile_states(int N, int lane, const float
 }
 
 // ---------------------------------------------------------------------------
+// One-direction summary with geometric A: the chunk's end state from zero is a
+// sum over its tokens, each input decayed over the tokens between it and the
+// chunk edge: S[n] = sum_k rho_k^(n+1) u_k B_k[n], with rho_k = e^(A[d,0] s_k)
+// and s_k the sum of delta over those tokens (after k to the chunk end for the
+// forward summary, from the chunk start to before k for the reverse one).  So
+// rho_k <= 1 and no factor can overflow.  Per state: p_k = u_k rho_k^(n+1) by
+// one multiply, then one FMA into S: two operations per (token, channel,
+// state) where the recurrence takes three (the power, u B and the chain).
+// sAcc[n][lane] accumulates S over the chunk's tiles.
+// ---------------------------------------------------------------------------
+template <int SUB>
+__device__ __forceinline__ void summary_tile_closed(int N, int lane, const float (&rho)[SUB], const float (&u)[SUB],
+                                                    float (*sB)[SUB], float (*sAcc)[64]) {
+  float p[SUB];
+#pragma unroll
+  for (int k = 0; k < SUB; ++k) p[k] = u[k];
+#pragma unroll 1
+  for (int n = 0; n < N; ++n) {
+    float s0 = sAcc[n][lane], s1 = 0.0f;  // two partial sums: half the dependent chain
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) p[k] *= rho[k];
+#pragma unroll
+    for (int k = 0; k < SUB; k += 2) {
+      s0 = fmaf(p[k], sB[n][k], s0);
+      s1 = fmaf(p[k + 1], sB[n][k + 1], s1);
+    }
+    sAcc[n][lane] = s0 + s1;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_summary: grid (d_inner / 64, nchunk, batch), block 64.  DS as above; P is
 // always written (both carries compose with it).  Each wavefront tests its
 // channels' A rows and runs the geometric or the general body (a
@@ -281,10 +312,15 @@ __device__ __forceinline__ void summary_body(const T* __restrict__ x, const T* _
   const float bias = dt_bias ? dt_bias[d] : 0.0f;
   const uint32_t voff = static_cast<uint32_t>(lane) * IO<T>::kBytes;
   const uint32_t row_bytes = static_cast<uint32_t>(D) * IO<T>::kBytes;
-  float sigma = 0.0f;  // sum of delta from the current tile's right edge to the chunk end
+  float sigma = 0.0f;  // sum of delta from the current tile's right edge to the chunk end (kLR: chunk start to its left edge)
 
+  // a one-direction summary with geometric A takes the closed form (summary_tile_closed); the reverse one
+  // walks the chunk left to right, so that sigma is the sum of delta before the tile
+  constexpr bool kClosed = GEO && DS != 3;
+  constexpr bool kLR = kClosed && DS == 2;
   const int nsub_c = (te - t0 + SUB - 1) / SUB;
-  for (int j = nsub_c - 1; j >= 0; --j) {
+  for (int jj = 0; jj < nsub_c; ++jj) {
+    const int j = kLR ? jj : nsub_c - 1 - jj;
     const int ts = t0 + j * SUB;
     const int nvalid = min(SUB, te - ts);
     const size_t tile = (row + ts) * D + static_cast<size_t>(blockIdx.x) * 64;
@@ -328,7 +364,26 @@ __device__ __forceinline__ void summary_body(const T* __restrict__ x, const T* _
       u[k] = dl[k] * xr[k];
       tile_sum += dl[k];
     }
-    if (GEO) {
+    if (kClosed) {
+      // rho_k = e^(A[d,0] s_k): s_k sums delta from token k (exclusive) to the chunk end, or from the chunk
+      // start to token k (exclusive); sigma holds the part outside this tile
+      float rho[SUB];
+      float run = sigma;
+      if (DS == 1) {
+#pragma unroll
+        for (int k = SUB - 1; k >= 0; --k) {
+          rho[k] = fast_exp2(a20 * run);
+          run += dl[k];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < SUB; ++k) {
+          rho[k] = fast_exp2(a20 * run);
+          run += dl[k];
+        }
+      }
+      summary_tile_closed<SUB>(N, lane, rho, u, sB, (DS == 1) ? sS : sR);
+    } else if (GEO) {
       float w[SUB];
 #pragma unroll
       for (int k = 0; k < SUB; ++k) w[k] = fast_exp2(dl[k] * a20);
