@@ -195,6 +195,52 @@ __global__ __launch_bounds__(256) void k_stage_bc(const T* __restrict__ Bm, cons
 __device__ __forceinline__ bool wave_geometric(bool lane_geo) { return __all(lane_geo ? 1 : 0) != 0; }
 
 // ---------------------------------------------------------------------------
+// Explicit waits.  The tile buffers are filled by direct-to-LDS buffer loads,
+// whose completion the compiler does not track: the kernel waits for them
+// itself.  The memory clobber keeps the compiler from moving LDS accesses
+// across a wait.
+// ---------------------------------------------------------------------------
+// s_waitcnt vmcnt(0) through the builtin, so that the compiler's own wait insertion knows that every
+// vector memory operation issued so far is complete (with an opaque asm wait it kept adding waits of
+// its own for loads already waited for: 1-2 % of the output pass); the empty asm keeps memory accesses
+// from moving across it.
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt at their maxima (not waited for)
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_lds_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Direct-to-LDS load of a [kSub x 64] tile of a token-major [*, D] tensor
+// (base = the tile's first row at this wavefront's first channel) into dst,
+// laid out [row][lane].  One instruction moves 16 bytes per lane, i.e. 1 KiB:
+// 8 rows of bf16 or 4 rows of fp32.  Rows past nvalid repeat the last valid
+// row (they are never used), so every read is in bounds.
+template <typename T>
+__device__ __forceinline__ void lds_load_tile(const T* base, int nvalid, uint32_t row_bytes, T (*dst)[64],
+                                              int lane) {
+  constexpr int kLanesPerRow = 64 * static_cast<int>(sizeof(T)) / 16;
+  constexpr int kRowsPerInst = 64 / kLanesPerRow;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, static_cast<size_t>(nvalid) * row_bytes);
+  const int rl = lane / kLanesPerRow;
+  const uint32_t cb = static_cast<uint32_t>(lane % kLanesPerRow) * 16u;
+#pragma unroll
+  for (int i = 0; i < static_cast<int>(kSub) / kRowsPerInst; ++i) {
+    const int row = min(i * kRowsPerInst + rl, nvalid - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)&dst[i * kRowsPerInst][0],
+                                             16, static_cast<uint32_t>(row) * row_bytes + cb, 0, 0, kStreamCpol);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float lds_val(const T (*src)[64], int k, int lane);
+template <>
+__device__ __forceinline__ float lds_val<float>(const float (*src)[64], int k, int lane) { return src[k][lane]; }
+template <>
+__device__ __forceinline__ float lds_val<bf16_t>(const bf16_t (*src)[64], int k, int lane) {
+  return to_f32(src[k][lane]);
+}
+
+// ---------------------------------------------------------------------------
 // k_summary state loop: all states of one tile, right to left across tiles.
 // f is the tile-local forward state from zero; S accumulates it decayed to the
 // chunk end; r is the running reverse state.
@@ -290,7 +336,7 @@ __device__ __forceinline__ void summary_body(const T* __restrict__ x, const T* _
                                              int nchunk, int nsub, int ntile, float* __restrict__ Sf,
                                              float* __restrict__ Sr, float* __restrict__ P, float* __restrict__ R,
                                              float* __restrict__ SIG, float (*sR)[64], float (*sS)[64],
-                                             float (*sB)[kSub]) {
+                                             float (*sB)[kSub], T (*sX)[64], T (*sDT)[64]) {
   constexpr int SUB = static_cast<int>(kSub);
   // the boundary states feed only an output pass that runs both chains left to right; a
   // reverse-only pass walks right to left and carries its state across tiles instead
@@ -318,16 +364,45 @@ __device__ __forceinline__ void summary_body(const T* __restrict__ x, const T* _
   // walks the chunk left to right, so that sigma is the sum of delta before the tile
   constexpr bool kClosed = GEO && DS != 3;
   constexpr bool kLR = kClosed && DS == 2;
+  // A one-direction summary brings each tile's x and dt into LDS with direct-to-LDS loads one tile ahead of
+  // its walk (its state loop is short, so a tile's loads would otherwise be waited for in full); the pass
+  // with both directions loads them straight into registers.
+  constexpr bool kPre = DS != 3;
   const int nsub_c = (te - t0 + SUB - 1) / SUB;
+  const size_t col0 = static_cast<size_t>(blockIdx.x) * 64;
+  if (kPre) {
+    const int jf = kLR ? 0 : nsub_c - 1;  // the walk's first tile
+    const int tsf = t0 + jf * SUB;
+    const int nvf = min(SUB, te - tsf);
+    lds_load_tile<T>(x + (row + tsf) * D + col0, nvf, row_bytes, sX, lane);
+    lds_load_tile<T>(dt + (row + tsf) * D + col0, nvf, row_bytes, sDT, lane);
+  }
   for (int jj = 0; jj < nsub_c; ++jj) {
     const int j = kLR ? jj : nsub_c - 1 - jj;
     const int ts = t0 + j * SUB;
     const int nvalid = min(SUB, te - ts);
-    const size_t tile = (row + ts) * D + static_cast<size_t>(blockIdx.x) * 64;
+    const size_t tile = (row + ts) * D + col0;
     const size_t tile_bytes = static_cast<size_t>(nvalid) * row_bytes;
     float xr[SUB], dr[SUB];
-    load_col_raw<T, SUB>(make_rsrc(x + tile, tile_bytes), voff, row_bytes, nvalid, xr);
-    load_col_raw<T, SUB>(make_rsrc(dt + tile, tile_bytes), voff, row_bytes, nvalid, dr);
+    if (kPre) {
+      // this tile's x and dt are in LDS once every vector load issued so far is done
+      wait_vmem_all();
+#pragma unroll
+      for (int k = 0; k < SUB; ++k) {
+        xr[k] = lds_val<T>(sX, k, lane);
+        dr[k] = lds_val<T>(sDT, k, lane);
+      }
+      wait_lds_all();  // the reads are done before the buffers are refilled
+      if (jj + 1 < nsub_c) {
+        const int ts1 = t0 + (kLR ? j + 1 : j - 1) * SUB;
+        const int nv1 = min(SUB, te - ts1);
+        lds_load_tile<T>(x + (row + ts1) * D + col0, nv1, row_bytes, sX, lane);
+        lds_load_tile<T>(dt + (row + ts1) * D + col0, nv1, row_bytes, sDT, lane);
+      }
+    } else {
+      load_col_raw<T, SUB>(make_rsrc(x + tile, tile_bytes), voff, row_bytes, nvalid, xr);
+      load_col_raw<T, SUB>(make_rsrc(dt + tile, tile_bytes), voff, row_bytes, nvalid, dr);
+    }
     const float* bt = bct + (static_cast<size_t>(b) * ntile + static_cast<size_t>(c) * nsub + j) * N * 2 * SUB;
     if (GEO) {
       // copy the tile's B rows (fp32, from the staged table) into LDS: lane = (state, quarter row).
@@ -346,7 +421,6 @@ __device__ __forceinline__ void summary_body(const T* __restrict__ x, const T* _
     if (kStoreR) {
       const bool have = j < nsub_c - 1;
       const size_t jp = cbase * nsub + (have ? j : 0);  // the slot of the boundary left of tile j + 1
-      const size_t col0 = static_cast<size_t>(blockIdx.x) * 64;
       const __amdgpu_buffer_rsrc_t rr =
           make_rsrc(R + jp * N * D + col0, have ? (static_cast<size_t>(N) * D - col0) * 4 : 0);
 #pragma unroll
@@ -412,6 +486,8 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
   __shared__ float sR[(DS & 2) ? NM : 1][64];
   __shared__ float sS[(DS & 1) ? NM : 1][64];
   __shared__ __align__(16) float sB[NM][kSub];  // the tile's B, one row per state (geometric body)
+  __shared__ __align__(16) T sX[(DS != 3) ? kSub : 1][64];  // a one-direction pass's next x and dt tiles
+  __shared__ __align__(16) T sDT[(DS != 3) ? kSub : 1][64];
   const int d = blockIdx.x * 64 + threadIdx.x;
   const float* __restrict__ Arow = A + static_cast<size_t>(d) * N;
   const float a0 = Arow[0];
@@ -419,10 +495,10 @@ __global__ __launch_bounds__(64) void k_summary(const T* __restrict__ x, const T
   for (int n = 0; n < N; ++n) geo_lane = geo_lane && (Arow[n] == static_cast<float>(n + 1) * a0);
   if (wave_geometric(geo_lane)) {
     summary_body<T, NM, true, DS>(x, dt, Arow, bct, dt_bias, L, D, N, chunk, nchunk, nsub, ntile, Sf, Sr, P, R, SIG,
-                                  sR, sS, sB);
+                                  sR, sS, sB, sX, sDT);
   } else {
     summary_body<T, NM, false, DS>(x, dt, Arow, bct, dt_bias, L, D, N, chunk, nchunk, nsub, ntile, Sf, Sr, P, R,
-                                   SIG, sR, sS, sB);
+                                   SIG, sR, sS, sB, sX, sDT);
   }
 }
 
@@ -472,52 +548,6 @@ __global__ __launch_bounds__(256) void k_carry(const float* __restrict__ Sf, con
       }
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Explicit waits.  The tile buffers are filled by direct-to-LDS buffer loads,
-// whose completion the compiler does not track: the kernel waits for them
-// itself.  The memory clobber keeps the compiler from moving LDS accesses
-// across a wait.
-// ---------------------------------------------------------------------------
-// s_waitcnt vmcnt(0) through the builtin, so that the compiler's own wait insertion knows that every
-// vector memory operation issued so far is complete (with an opaque asm wait it kept adding waits of
-// its own for loads already waited for: 1-2 % of the output pass); the empty asm keeps memory accesses
-// from moving across it.
-__device__ __forceinline__ void wait_vmem_all() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt at their maxima (not waited for)
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void wait_lds_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Direct-to-LDS load of a [kSub x 64] tile of a token-major [*, D] tensor
-// (base = the tile's first row at this wavefront's first channel) into dst,
-// laid out [row][lane].  One instruction moves 16 bytes per lane, i.e. 1 KiB:
-// 8 rows of bf16 or 4 rows of fp32.  Rows past nvalid repeat the last valid
-// row (they are never used), so every read is in bounds.
-template <typename T>
-__device__ __forceinline__ void lds_load_tile(const T* base, int nvalid, uint32_t row_bytes, T (*dst)[64],
-                                              int lane) {
-  constexpr int kLanesPerRow = 64 * static_cast<int>(sizeof(T)) / 16;
-  constexpr int kRowsPerInst = 64 / kLanesPerRow;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, static_cast<size_t>(nvalid) * row_bytes);
-  const int rl = lane / kLanesPerRow;
-  const uint32_t cb = static_cast<uint32_t>(lane % kLanesPerRow) * 16u;
-#pragma unroll
-  for (int i = 0; i < static_cast<int>(kSub) / kRowsPerInst; ++i) {
-    const int row = min(i * kRowsPerInst + rl, nvalid - 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)&dst[i * kRowsPerInst][0],
-                                             16, static_cast<uint32_t>(row) * row_bytes + cb, 0, 0, kStreamCpol);
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ float lds_val(const T (*src)[64], int k, int lane);
-template <>
-__device__ __forceinline__ float lds_val<float>(const float (*src)[64], int k, int lane) { return src[k][lane]; }
-template <>
-__device__ __forceinline__ float lds_val<bf16_t>(const bf16_t (*src)[64], int k, int lane) {
-  return to_f32(src[k][lane]);
 }
 
 // ---------------------------------------------------------------------------
