@@ -63,6 +63,19 @@ def check_variants(inp, io, variants=VARIANTS, chan=None, tag=""):
         check(got, want, io, f"{tag} {name}")
 
 
+def test_one_direction_many_tiles_per_chunk():
+    """The one-direction passes with geometric A at chunks of 16 tiles (batch 1, L 16384, d_inner 4096: 64
+    chunks of 256 tokens), fp32 I/O: their chunk summaries take the closed form, the reverse one walking each
+    chunk left to right with the sum of delta before each tile carried across its 16 tiles, and both bring
+    each next tile into LDS while the current one computes.  SSM only and full, on a channel subset."""
+    inp = case(1, 16384, 4096, 16, "f32", seed=17)
+    chan = np.r_[0:8, 2040:2048, 4088:4096]
+    check_variants(inp, "f32", variants=[("fwd_only_ssm", FWD_ONLY | NO_GATE, dict(use_D=False)),
+                                         ("rev_only_ssm", REV_ONLY | NO_GATE, dict(use_D=False)),
+                                         ("fwd_only", FWD_ONLY, dict()), ("rev_only", REV_ONLY, dict())],
+                   chan=chan, tag="one_direction_16_tiles")
+
+
 def test_tiny_fp32_workload():
     """batch 1, L 256, d_inner 64, d_state 16, fp32 I/O."""
     w = I.WORKLOADS["tiny_fp32"]
