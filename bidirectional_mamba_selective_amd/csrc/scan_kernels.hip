@@ -585,6 +585,57 @@ __device__ __forceinline__ void output_tile_states(int N, int D, int lane, const
     cr_next = IO<float>::load(cr_rsrc, voff4, 0);
   }
   if (!GEO) a2_next = IO<float>::load(a2_rsrc, voff4, 0);
+  if constexpr (DIRS == 1) {
+    // Forward readout only: every u B product is formed before the chain, so B's uses all precede C's, and
+    // each half of the state's table row is loaded half a state ahead into registers whose values are dead:
+    // C of state n after the first use of B, B of state n + 1 after the first use of C.  Scalar loads
+    // complete out of order (a wait for one waits for all issued before it), so this order keeps each wait
+    // from covering a load issued just before it.  The scheduling barriers hold the loads in place.
+    float bv[SUB], cv[SUB];
+    float hf_next = sHf[0][lane];
+    {
+      const sfloat* b0 = scalar_ptr(bt);
+#pragma unroll
+      for (int k = 0; k < SUB; ++k) bv[k] = b0[k];
+    }
+#pragma unroll 1
+    for (int n = 0; n < N; ++n) {
+      const sfloat* cn = scalar_ptr(bt + static_cast<size_t>(n) * 2 * SUB + SUB);
+      const sfloat* bn1 = scalar_ptr(bt + static_cast<size_t>(min(n + 1, N - 1)) * 2 * SUB);
+      float a2 = 0.0f;
+      if (!GEO) {
+        a2 = a2_next;
+        a2_next = IO<float>::load(a2_rsrc, voff4, static_cast<uint32_t>(min(n + 1, N - 1)) * nstride4);
+      }
+      float hf = hf_next;
+      float bb[SUB];
+      a[0] = GEO ? a[0] * w[0] : fast_exp2(w[0] * a2);
+      bb[0] = u[0] * bv[0];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < SUB; ++k) cv[k] = cn[k];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 1; k < SUB; ++k) {
+        a[k] = GEO ? a[k] * w[k] : fast_exp2(w[k] * a2);
+        bb[k] = u[k] * bv[k];
+      }
+      hf = fmaf(a[0], hf, bb[0]);
+      y[0] = fmaf(cv[0], hf, y[0]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < SUB; ++k) bv[k] = bn1[k];
+      hf_next = sHf[min(n + 1, N - 1)][lane];  // sHf[n + 1] is not written in this step
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 1; k < SUB; ++k) {
+        hf = fmaf(a[k], hf, bb[k]);
+        y[k] = fmaf(cv[k], hf, y[k]);
+      }
+      sHf[n][lane] = hf;
+    }
+    return;
+  }
 #pragma unroll 1
   for (int n = 0; n < N; ++n) {
     const sfloat* bn = scalar_ptr(bt + static_cast<size_t>(n) * 2 * SUB);
@@ -646,25 +697,51 @@ __device__ __forceinline__ void output_tile_states_rwalk(int N, int D, int lane,
 #pragma unroll
   for (int k = 0; k < SUB; ++k) a[k] = 1.0f;
   float a2_next = GEO ? 0.0f : IO<float>::load(a2_rsrc, voff4, 0);
+  // B's uses all precede C's in a state step: each half of the state's table row is loaded half a state
+  // ahead into registers whose values are dead, as in the forward-only readout of output_tile_states
+  float bv[SUB], cv[SUB];
+  float hr_next = sH[0][lane];
+  {
+    const sfloat* b0 = scalar_ptr(bt);
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) bv[k] = b0[k];
+  }
 #pragma unroll 1
   for (int n = 0; n < N; ++n) {
-    const sfloat* bn = scalar_ptr(bt + static_cast<size_t>(n) * 2 * SUB);
+    const sfloat* cn = scalar_ptr(bt + static_cast<size_t>(n) * 2 * SUB + SUB);
+    const sfloat* bn1 = scalar_ptr(bt + static_cast<size_t>(min(n + 1, N - 1)) * 2 * SUB);
     float a2 = 0.0f;
     if (!GEO) {
       a2 = a2_next;
       a2_next = IO<float>::load(a2_rsrc, voff4, static_cast<uint32_t>(min(n + 1, N - 1)) * nstride4);
     }
-    float hr = sH[n][lane];
+    float hr = hr_next;
     float bb[SUB];
+    a[0] = GEO ? a[0] * w[0] : fast_exp2(w[0] * a2);
+    bb[0] = u[0] * bv[0];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < SUB; ++k) {
+    for (int k = 0; k < SUB; ++k) cv[k] = cn[k];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 1; k < SUB; ++k) {
       a[k] = GEO ? a[k] * w[k] : fast_exp2(w[k] * a2);
-      bb[k] = u[k] * bn[k];
+      bb[k] = u[k] * bv[k];
     }
-#pragma unroll
-    for (int k = SUB - 1; k >= 0; --k) {
+    {
+      constexpr int k = SUB - 1;
       hr = fmaf(a[k], hr, bb[k]);
-      y[k] = fmaf(bn[SUB + k], hr, y[k]);
+      y[k] = fmaf(cv[k], hr, y[k]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < SUB; ++k) bv[k] = bn1[k];
+    hr_next = sH[min(n + 1, N - 1)][lane];  // sH[n + 1] is not written in this step
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = SUB - 2; k >= 0; --k) {
+      hr = fmaf(a[k], hr, bb[k]);
+      y[k] = fmaf(cv[k], hr, y[k]);
     }
     sH[n][lane] = hr;
   }
